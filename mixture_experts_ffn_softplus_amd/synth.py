@@ -1,0 +1,166 @@
+"""Seeded synthetic inputs of the mixture-of-experts FFN block.
+
+This module only draws and stores input tensors; it holds none of the block's
+arithmetic, and both the GPU path's tests and the oracle consume what it
+produces.  Every tensor comes from its own torch generator, seeded from
+(workload seed, tensor tag, expert index), so any one expert's weights can be
+regenerated alone -- the oracle's token sample needs only the experts those
+tokens use, and a 34 GB weight set never has to exist on the host.
+
+Recipe (all logical layouts row-major):
+
+* x [T, d] ~ N(0, 1), stored fp32 or bf16 (round to nearest even).
+* W_r [d, E] ~ N(0, 1/d) (standard deviation 1/sqrt(fan_in), fan_in = d).
+* W_gate, W_up [E, d, f] ~ N(0, 1/d); W_down [E, f, d] ~ N(0, 1/f); the shared
+  experts likewise with f_s, stacked [S, ...].
+* FP8 weights: each 128 x 128 block of the fp32 draw gets scale amax/448 (1 if
+  the block is zero) and codes = the draw over the scale, cast to E4M3FN by
+  torch.  The quantised weights are the inputs; how they were made is not part
+  of the block.
+* Selection-only bias b_e ~ U(-r, r) (fp32) when the workload asks for one.
+* Load skew: logit bias z_e = ln p_e - mean(ln p), p_e proportional to
+  (e + 1)^-s, expert 0 hottest (fp32).
+
+Generators on a CUDA device and on the CPU produce different streams for the
+same seed; a test always hands the very same tensors to both sides.
+"""
+import math
+
+import torch
+
+from .configs import BF16, F32, FP8_E4M3, MoEConfig
+
+TAG_X, TAG_ROUTER, TAG_SELECT_BIAS = 1, 2, 3
+TAG_GATE, TAG_UP, TAG_DOWN = 4, 5, 6
+TAG_SGATE, TAG_SUP, TAG_SDOWN = 7, 8, 9
+
+_MASK64 = (1 << 64) - 1
+
+
+def _mix(*vals) -> int:
+    """A 63-bit seed from a tuple of small integers (splitmix64 finaliser chain)."""
+    h = 0x9E3779B97F4A7C15
+    for v in vals:
+        h = (h ^ (int(v) & _MASK64)) & _MASK64
+        h = (h * 0xBF58476D1CE4E5B9) & _MASK64
+        h ^= h >> 31
+        h = (h * 0x94D049BB133111EB) & _MASK64
+        h ^= h >> 29
+    return h & ((1 << 63) - 1)
+
+
+def _gen(device, *vals) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(_mix(*vals))
+    return g
+
+
+def _normal(shape, std, device, *seed_vals) -> torch.Tensor:
+    g = _gen(device, *seed_vals)
+    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    return t
+
+
+def _store(t: torch.Tensor, dtype: int) -> torch.Tensor:
+    if dtype == F32:
+        return t.contiguous()
+    if dtype == BF16:
+        return t.to(torch.bfloat16).contiguous()
+    raise ValueError("use _store_fp8 for FP8 weights")
+
+
+def _store_fp8(t: torch.Tensor, block: int):
+    """fp32 [..., R, C] -> (E4M3FN codes [..., R, C], fp32 scales [..., R/block, C/block])."""
+    *lead, R, C = t.shape
+    assert R % block == 0 and C % block == 0
+    b = t.reshape(*lead, R // block, block, C // block, block)
+    amax = b.abs().amax(dim=(-3, -1))                       # [..., R/b, C/b]
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax)).to(torch.float32)
+    q = (b / scale[..., :, None, :, None]).to(torch.float8_e4m3fn)
+    return q.reshape(*lead, R, C).contiguous(), scale.contiguous()
+
+
+def tokens(cfg: MoEConfig, device="cpu") -> torch.Tensor:
+    x = _normal((cfg.num_tokens, cfg.d_model), 1.0, device, cfg.seed, TAG_X)
+    return _store(x, F32 if cfg.act_dtype == F32 else BF16)
+
+
+def router(cfg: MoEConfig, device="cpu"):
+    """(W_r [d,E], logit bias z [E] or None, selection bias b [E] or None)."""
+    d, E = cfg.d_model, cfg.num_experts
+    wr = _store(_normal((d, E), 1.0 / math.sqrt(d), device, cfg.seed, TAG_ROUTER),
+                cfg.router_dtype)
+    z = None
+    if cfg.zipf_s > 0:
+        lnp = [-cfg.zipf_s * math.log(e + 1) for e in range(E)]
+        mean = sum(lnp) / E
+        z = torch.tensor([v - mean for v in lnp], dtype=torch.float64).to(torch.float32)
+        z = z.to(device)
+    b = None
+    if cfg.select_bias_range > 0:
+        g = _gen(device, cfg.seed, TAG_SELECT_BIAS)
+        r = cfg.select_bias_range
+        b = (torch.rand((E,), generator=g, device=device, dtype=torch.float32) * (2 * r) - r)
+    return wr, z, b
+
+
+def _expert(cfg: MoEConfig, shared: bool, e: int, device):
+    d = cfg.d_model
+    f = cfg.d_ff_shared if shared else cfg.d_ff
+    tg, tu, td = (TAG_SGATE, TAG_SUP, TAG_SDOWN) if shared else (TAG_GATE, TAG_UP, TAG_DOWN)
+    g = _normal((d, f), 1.0 / math.sqrt(d), device, cfg.seed, tg, e)
+    u = _normal((d, f), 1.0 / math.sqrt(d), device, cfg.seed, tu, e)
+    dn = _normal((f, d), 1.0 / math.sqrt(f), device, cfg.seed, td, e)
+    if cfg.expert_dtype == FP8_E4M3:
+        (gq, gs), (uq, us), (dq, ds) = (_store_fp8(t, cfg.quant_block) for t in (g, u, dn))
+        return {"gate": gq, "up": uq, "down": dq, "gate_scales": gs, "up_scales": us,
+                "down_scales": ds}
+    return {"gate": _store(g, cfg.expert_dtype), "up": _store(u, cfg.expert_dtype),
+            "down": _store(dn, cfg.expert_dtype)}
+
+
+def routed_expert(cfg: MoEConfig, e: int, device="cpu"):
+    """Weights of routed expert e: gate/up [d,f], down [f,d] (+ FP8 block scales)."""
+    return _expert(cfg, False, e, device)
+
+
+def shared_expert(cfg: MoEConfig, s: int, device="cpu"):
+    return _expert(cfg, True, s, device)
+
+
+def _stack(cfg, shared: bool, n: int, device):
+    parts = [_expert(cfg, shared, e, device) for e in range(n)]
+    if n == 0:
+        return None
+    return {key: torch.stack([p[key] for p in parts]) for key in parts[0]}
+
+
+def routed_experts(cfg: MoEConfig, device="cpu"):
+    """All routed experts stacked: gate/up [E,d,f], down [E,f,d] (+ scales)."""
+    out = {}
+    keys = None
+    for e in range(cfg.num_experts):
+        p = _expert(cfg, False, e, device)
+        if keys is None:
+            keys = list(p)
+            for key in keys:
+                out[key] = torch.empty((cfg.num_experts,) + tuple(p[key].shape),
+                                       dtype=p[key].dtype, device=device)
+        for key in keys:
+            out[key][e].copy_(p[key])
+        del p
+    return out
+
+
+def shared_experts(cfg: MoEConfig, device="cpu"):
+    """All shared experts stacked: gate/up [S,d,f_s], down [S,f_s,d] (+ scales), or None."""
+    return _stack(cfg, True, cfg.num_shared, device)
+
+
+def inputs(cfg: MoEConfig, device="cpu"):
+    """Every input of the block, logical layouts."""
+    wr, z, b = router(cfg, device)
+    return {"x": tokens(cfg, device), "w_router": wr, "logit_bias": z, "select_bias": b,
+            "routed": routed_experts(cfg, device), "shared": shared_experts(cfg, device)}
