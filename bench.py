@@ -1,0 +1,260 @@
+"""Throughput of the MI355X mixture-of-experts FFN block on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload softmax_bf16]
+
+A step is one moe_forward (router -> top-k -> permutation -> routed SwiGLU experts -> shared
+experts and weighted combine) over one batch of seeded synthetic tokens, with every input and
+the packed weights resident in HBM before the timed region starts.  Prints one JSON line.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec + % MFMA peak (T=4096) and % HBM BW (decode)"
+HBM_PEAK_GBS = 8000.0                 # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {0: 157.3, 1: 2500.0, 2: 5000.0}   # fp32, bf16, fp8 dense
+DTYPE_NAME = {0: "f32", 1: "bf16", 2: "fp8_e4m3"}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """A few HIP runtime calls for stage timing (the runtime torch already loaded)."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        evs = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            assert self.rt.hipEventCreate(ctypes.byref(h)) == 0
+            evs[i] = h
+        return evs
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.rt.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.rt.hipEventDestroy(e)
+
+
+def algorithmic(cfg, touched):
+    """Algorithmic bytes and flops of one step (what the block must read, write and compute)."""
+    d, f, fs, S, E, T, k = (cfg.d_model, cfg.d_ff, cfg.d_ff_shared, cfg.num_shared,
+                            cfg.num_experts, cfg.num_tokens, cfg.top_k)
+    wb = {0: 4, 1: 2, 2: 1}[cfg.expert_dtype]
+    rb = 4 if cfg.router_dtype == 0 else 2
+    xb = 4 if cfg.act_dtype == 0 else 2
+    step_bytes = (touched * 3 * d * f * wb + S * 3 * d * fs * wb + d * E * rb + 2 * T * d * xb)
+    step_flops = 2 * T * d * E + 6 * T * k * d * f + 6 * T * d * S * fs
+    gate_up_bytes = touched * 2 * d * f * wb + T * d * xb
+    gate_up_flops = 4 * T * k * d * f
+    return step_bytes, step_flops, gate_up_bytes, gate_up_flops
+
+
+def cpu_baseline(cfg, inp, n_tokens, seed=0):
+    """The oracle, as it stands, on a bounded token sample of the same workload."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from mixture_experts_ffn_softplus_amd import synth
+
+    def np_storage(t):
+        t = t.detach().contiguous().cpu()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        if t.dtype == torch.float8_e4m3fn:
+            return t.view(torch.uint8).numpy()
+        return t.numpy()
+
+    def exact64(t):
+        return t.detach().cpu().to(torch.float64).numpy()
+
+    def expert_set(n, parts):
+        col = lambda key: [None if p is None else p.get(key) for p in parts]  # noqa: E731
+        return oracle.ExpertSet(n, col("gate"), col("up"), col("down"),
+                                gate_scales=col("gate_scales"), up_scales=col("up_scales"),
+                                down_scales=col("down_scales"))
+
+    rng = np.random.default_rng(seed)
+    tok = np.sort(rng.choice(cfg.num_tokens, min(n_tokens, cfg.num_tokens), replace=False))
+    x = exact64(inp["x"][torch.as_tensor(tok, device=inp["x"].device)])
+    wr = np_storage(inp["w_router"])
+    z = None if inp["logit_bias"] is None else inp["logit_bias"].cpu().numpy()
+    sb = None if inp["select_bias"] is None else inp["select_bias"].cpu().numpy()
+    quant = cfg.expert_dtype == 2
+
+    def host(d):
+        return {k: (v.cpu().numpy() if k.endswith("scales") else np_storage(v))
+                for k, v in d.items()}
+
+    shared = None
+    if cfg.num_shared:
+        sh = [host(synth.shared_expert(cfg, s, inp["x"].device)) for s in range(cfg.num_shared)]
+        shared = expert_set(cfg.num_shared, sh)
+    t_cpu = 0.0
+    t0 = time.perf_counter()
+    l = oracle.router_logits(x, wr, z)
+    ids, w, _ = oracle.route(l, cfg.top_k, cfg.score, bool(cfg.renormalize), cfg.routed_scale, sb)
+    oracle.permute(ids, cfg.num_experts)
+    t_cpu += time.perf_counter() - t0
+    max_experts = 160
+    i = 0
+    while i < len(tok):
+        used, j = set(), i
+        while j < len(tok) and len(used | set(ids[j].tolist())) <= max_experts:
+            used |= set(ids[j].tolist())
+            j += 1
+        j = max(j, i + 1)
+        used = sorted(used | set(ids[i].tolist()))
+        parts = {e: host(synth.routed_expert(cfg, e, inp["x"].device)) for e in used}
+        slots = [parts.get(e) for e in range(cfg.num_experts)]
+        routed = expert_set(cfg.num_experts, slots)
+        t0 = time.perf_counter()
+        oracle.moe_tokens(x[i:j], ids[i:j], w[i:j], routed, shared, cfg.d_model, cfg.d_ff,
+                          cfg.d_ff_shared, quant=quant)
+        t_cpu += time.perf_counter() - t0
+        log(f"cpu_baseline: {j}/{len(tok)} tokens, {t_cpu:.1f} s of oracle time")
+        del parts, routed, slots
+        i = j
+    return {"value": len(tok) / t_cpu, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": (f"{len(tok)} seeded tokens of {cfg.name}: fp64 router logits, top-k, "
+                       f"permutation and routed+shared SwiGLU experts for those tokens; "
+                       f"{t_cpu:.1f} s of CPU time"),
+            "seconds": t_cpu}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="softmax_bf16")
+    ap.add_argument("--cpu-tokens", type=int, default=96)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs the block on one GPU; --gpus {args.gpus} is not "
+              f"supported (expert-parallel sharding is described in DESIGN.md, not built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from mixture_experts_ffn_softplus_amd import PRESETS, api, synth
+
+    cfg = PRESETS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"workload {cfg.describe()}")
+    inp = synth.inputs(cfg, dev)
+    pw = api.pack(cfg, inp["w_router"], inp["routed"], inp["shared"], inp["logit_bias"],
+                  inp["select_bias"])
+    torch.cuda.synchronize()
+    inp["routed"] = None   # the packed copy is what the kernels read
+    torch.cuda.empty_cache()
+    w = pw.struct()
+    ws = api.workspace(cfg, dev)
+    T, d = cfg.num_tokens, cfg.d_model
+    out = torch.empty(T, d, dtype=api.out_dtype(cfg), device=dev)
+    x = inp["x"]
+    log(f"packed weights {pw.nbytes() / 1e9:.2f} GB, workspace {ws.numel() / 1e9:.2f} GB")
+
+    # routing statistics of this input (untimed)
+    off = torch.empty(cfg.num_experts + 1, dtype=torch.int32, device=dev)
+    api.moe_forward(cfg, x, w, out, ws, {"expert_offsets": off})
+    torch.cuda.synchronize()
+    counts = (off[1:] - off[:-1]).cpu()
+    touched = int((counts > 0).sum())
+
+    for _ in range(args.warmup):
+        api.moe_forward(cfg, x, w, out, ws)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        api.moe_forward(cfg, x, w, out, ws)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    log(f"timed {args.steps} steps: {ms:.4f} ms/step")
+
+    # per-stage times: the same steps again, with the library recording HIP events on the
+    # stream at each stage boundary
+    hip = HipEvents()
+    n_ev = api.NUM_STAGE_EVENTS
+    ev = [hip.create(n_ev) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        api.moe_forward(cfg, x, w, out, ws, {"stage_events": ctypes.addressof(ev[i])})
+    torch.cuda.synchronize()
+    stage_ms = {}
+    for s, name in enumerate(api.STAGES):
+        stage_ms[name] = sum(hip.elapsed_ms(ev[i][s], ev[i][s + 1])
+                             for i in range(args.steps)) / args.steps
+    for e in ev:
+        hip.destroy(e)
+    log("stage ms: " + ", ".join(f"{k}={v:.4f}" for k, v in stage_ms.items()))
+
+    step_bytes, step_flops, gu_bytes, gu_flops = algorithmic(cfg, touched)
+    gu_ms = stage_ms["gate_up"]
+    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "grouped_gemm_kernel (routed gate/up + SiLU*up)",
+                "kernel_ms": round(gu_ms, 5), "bytes_per_launch": gu_bytes}
+    mfma_peak = MFMA_PEAK_TFLOPS[cfg.expert_dtype]
+    step = {"bytes": step_bytes, "flops": step_flops,
+            "GB_s": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "TFLOP_s": round(step_flops / (ms * 1e-3) / 1e12, 2),
+            "mfma_frac": round(step_flops / (ms * 1e-3) / 1e12 / mfma_peak, 4),
+            "touched_experts": touched, "max_rows_per_expert": int(counts.max())}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        inp["routed"] = None
+        cpu = cpu_baseline(cfg, inp, args.cpu_tokens)
+
+    result = {
+        "metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": DTYPE_NAME[cfg.expert_dtype], "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": T, "d_model": d,
+                   "experts": cfg.num_experts, "top_k": cfg.top_k, "d_ff": cfg.d_ff,
+                   "shared": cfg.num_shared, "d_ff_shared": cfg.d_ff_shared,
+                   "router": ["softmax", "sigmoid", "sqrt_softplus"][cfg.score],
+                   "parallelism": "single_gpu"},
+        "roofline": roofline, "step_roofline": step, "stage_ms": {k: round(v, 5) for k, v in
+                                                                   stage_ms.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,407 @@
+// gemm.hip -- grouped expert GEMMs on gfx950 MFMA with fused epilogues.
+//
+// Computes, for every tile of rows of every group (expert), OUT = A_rows x B_group^T with B
+// stored [N, K] K-contiguous (the packed weight layout), followed by one of:
+//   kEpiSwiglu  -- h = SiLU(gate) * up: B interleaves gate and up columns in blocks of 16
+//                  packed rows, so each wave's accumulators hold matching gate/up columns and
+//                  h is formed in registers ("SwiGLU experts", routed-experts row of
+//                  "Qwen3.5-397B-A17B vs Gemma 4 31B"); FP8 re-quantises h per 128 values;
+//   kEpiStore   -- the down projection, rows stored as they are (y_perm);
+//   kEpiCombine -- the shared experts' down projection plus the un-permute and weighted sum
+//                  of the routed rows: out[t] = acc[t] + sum_j w[t,j] y[inv_perm[t*k+j]]
+//                  (shared-expert row of the same page: the shared output is added to the
+//                  routed sum).
+//
+// Structure.  256 threads (4 waves) per workgroup, a BM x BN output tile, K consumed 128 bytes
+// per step (64 bf16, 32 fp32 or 128 E4M3 values -- exactly one FP8 scale block).  Each step's
+// A rows (gathered through a_map: no permuted copy of x is ever written) and B rows are
+// fetched with 16-byte loads into registers while the MFMAs of the previous step run, then
+// written to a double-buffered LDS tile whose 16-byte chunks are XOR-swizzled by row so that
+// the fragment reads of 16 consecutive rows hit distinct banks.  Workgroups map to tiles
+// through an XCD-aware remap so that neighbouring tiles (the N-tiles of one expert, which share
+// its A rows) run in the same XCD's L2.  Grids are sized for the worst case and read the
+// device tile count, so no per-expert count travels to the host.
+#include <math.h>
+
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+template <int DT>
+struct DT_ {};
+template <>
+struct DT_<MOE_F32> { static constexpr int esize = 4; };
+template <>
+struct DT_<MOE_BF16> { static constexpr int esize = 2; };
+template <>
+struct DT_<MOE_FP8_E4M3> { static constexpr int esize = 1; };
+
+__device__ __forceinline__ int swz(int row, int ch) { return row * kBlockK + ((ch ^ (row & 7)) << 4); }
+
+template <int DT, int BM, int BN, int EPI>
+struct GemmShape {
+  static constexpr int WM = BM >= 32 ? 2 : 1;
+  static constexpr int WN = 4 / WM;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int FM = TM / 16, FN = TN / 16;
+  static constexpr bool kFp8 = DT == MOE_FP8_E4M3;
+  static constexpr int A_CHUNKS = BM * 8, B_CHUNKS = BN * 8;  // 16-byte chunks per step
+  static constexpr int A_PER = (A_CHUNKS + 255) / 256, B_PER = (B_CHUNKS + 255) / 256;
+  static constexpr int STAGE = (BM + BN) * kBlockK;
+  static constexpr int SCALE_STAGE = kFp8 ? (BM + BN / 16) * 4 : 0;
+  static constexpr int MAIN = 2 * STAGE + 2 * SCALE_STAGE;
+  static constexpr int EPI_BYTES =
+      EPI == kEpiSwiglu ? BM * (BN / 2 + 4) * 4 : BM * (BN + 4) * 4;
+  static constexpr int SMEM = MAIN > EPI_BYTES ? MAIN : EPI_BYTES;
+  static_assert(FM >= 1 && FN >= 1, "tile too small for 4 waves");
+  static_assert(EPI != kEpiSwiglu || FN % 2 == 0, "gate/up pairs must stay within one wave");
+  static_assert(!(kFp8 && EPI == kEpiSwiglu) || BN == 256, "FP8 h groups need 128 h columns");
+};
+
+template <int DT, int BM, int BN, int EPI>
+__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
+  using S = GemmShape<DT, BM, BN, EPI>;
+  constexpr int esize = DT_<DT>::esize;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[S::SMEM];
+
+  // ---------------------------------------------------------------- which tile
+  const int NT = a.N / BN;
+  const int ntiles = a.tiles ? a.tiles_count[0] : (a.M + BM - 1) / BM;
+  const int nblocks = ntiles * NT;
+  if (static_cast<int>(blockIdx.x) >= nblocks) return;
+  const int L = xcd_remap(blockIdx.x, nblocks);
+  const int tile = L / NT, nt = L - tile * NT;
+  int group = 0, m0, rows;
+  if (a.tiles) {
+    int4 ti = a.tiles[tile];
+    group = ti.x;
+    m0 = ti.y;
+    rows = ti.z;
+  } else {
+    m0 = tile * BM;
+    rows = min(BM, a.M - m0);
+  }
+  const int n0 = nt * BN;
+
+  const int tid = threadIdx.x, l = lane_id(), wv = tid / kWave;
+  const int wm = wv / S::WN, wn = wv % S::WN;
+  const int lr = l & 15, kq = l >> 4;
+  const int KB = a.K * esize / kBlockK;  // pipeline steps
+  const int64_t ldb = static_cast<int64_t>(a.K) * esize;
+
+  f32x4 acc[S::FM][S::FN];
+#pragma unroll
+  for (int i = 0; i < S::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < S::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (KB > 0) {
+    // ------------------------------------------------------------ per-thread load addresses
+    const uint8_t* a_ptr[S::A_PER];
+    const uint8_t* b_ptr[S::B_PER];
+    const float* as_ptr = nullptr;
+    const float* bs_ptr = nullptr;
+#pragma unroll
+    for (int i = 0; i < S::A_PER; ++i) {
+      int c = tid + 256 * i;
+      int r = min(c >> 3, rows - 1);  // rows past the group's end re-read a valid row
+      int arow = a.a_map ? a.a_map[m0 + r] : m0 + r;
+      a_ptr[i] = static_cast<const uint8_t*>(a.A) + static_cast<int64_t>(arow) * a.lda + (c & 7) * 16;
+    }
+    const uint8_t* bg = static_cast<const uint8_t*>(a.B) + group * a.b_group_stride;
+#pragma unroll
+    for (int i = 0; i < S::B_PER; ++i) {
+      int c = tid + 256 * i;
+      b_ptr[i] = bg + static_cast<int64_t>(n0 + (c >> 3)) * ldb + (c & 7) * 16;
+    }
+    if constexpr (S::kFp8) {
+      if (tid < BM) {
+        int r = min(tid, rows - 1);
+        int arow = a.a_map ? a.a_map[m0 + r] : m0 + r;
+        as_ptr = a.a_scales + static_cast<int64_t>(arow) * KB;
+      } else if (tid < BM + BN / 16) {
+        bs_ptr = a.b_scales + group * a.bs_group_stride +
+                 static_cast<int64_t>(n0 / 16 + (tid - BM)) * KB;
+      }
+    }
+
+    i32x4 ra[S::A_PER], rb[S::B_PER];
+    float rsc = 0.0f;
+    auto load = [&](int step) {
+#pragma unroll
+      for (int i = 0; i < S::A_PER; ++i)
+        if (S::A_CHUNKS % 256 == 0 || tid + 256 * i < S::A_CHUNKS)
+          ra[i] = *reinterpret_cast<const i32x4*>(a_ptr[i] + step * kBlockK);
+#pragma unroll
+      for (int i = 0; i < S::B_PER; ++i)
+        if (S::B_CHUNKS % 256 == 0 || tid + 256 * i < S::B_CHUNKS)
+          rb[i] = *reinterpret_cast<const i32x4*>(b_ptr[i] + step * kBlockK);
+      if constexpr (S::kFp8) {
+        if (as_ptr) rsc = as_ptr[step];
+        else if (bs_ptr) rsc = bs_ptr[step];
+      }
+    };
+    auto store = [&](int buf) {
+      uint8_t* sa = smem + buf * S::STAGE;
+      uint8_t* sb = sa + BM * kBlockK;
+#pragma unroll
+      for (int i = 0; i < S::A_PER; ++i) {
+        int c = tid + 256 * i;
+        if (S::A_CHUNKS % 256 == 0 || c < S::A_CHUNKS)
+          *reinterpret_cast<i32x4*>(sa + swz(c >> 3, c & 7)) = ra[i];
+      }
+#pragma unroll
+      for (int i = 0; i < S::B_PER; ++i) {
+        int c = tid + 256 * i;
+        if (S::B_CHUNKS % 256 == 0 || c < S::B_CHUNKS)
+          *reinterpret_cast<i32x4*>(sb + swz(c >> 3, c & 7)) = rb[i];
+      }
+      if constexpr (S::kFp8) {
+        float* ss = reinterpret_cast<float*>(smem + 2 * S::STAGE + buf * S::SCALE_STAGE);
+        if (tid < BM + BN / 16) ss[tid] = rsc;
+      }
+    };
+
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int step = 0; step < KB; ++step) {
+      const int buf = step & 1;
+      if (step + 1 < KB) load(step + 1);
+      const uint8_t* sa = smem + buf * S::STAGE;
+      const uint8_t* sb = sa + BM * kBlockK;
+      if constexpr (DT == MOE_BF16) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int ch = 4 * s + kq;
+          bf16x8 af[S::FM], bf[S::FN];
+#pragma unroll
+          for (int i = 0; i < S::FM; ++i)
+            af[i] = *reinterpret_cast<const bf16x8*>(sa + swz(wm * S::TM + i * 16 + lr, ch));
+#pragma unroll
+          for (int j = 0; j < S::FN; ++j)
+            bf[j] = *reinterpret_cast<const bf16x8*>(sb + swz(wn * S::TN + j * 16 + lr, ch));
+#pragma unroll
+          for (int i = 0; i < S::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < S::FN; ++j) acc[i][j] = mfma_bf16(af[i], bf[j], acc[i][j]);
+        }
+      } else if constexpr (DT == MOE_F32) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int ch = kq + 4 * s;
+          f32x4 af[S::FM], bf[S::FN];
+#pragma unroll
+          for (int i = 0; i < S::FM; ++i)
+            af[i] = *reinterpret_cast<const f32x4*>(sa + swz(wm * S::TM + i * 16 + lr, ch));
+#pragma unroll
+          for (int j = 0; j < S::FN; ++j)
+            bf[j] = *reinterpret_cast<const f32x4*>(sb + swz(wn * S::TN + j * 16 + lr, ch));
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int i = 0; i < S::FM; ++i)
+#pragma unroll
+              for (int j = 0; j < S::FN; ++j) acc[i][j] = mfma_f32(af[i][e], bf[j][e], acc[i][j]);
+        }
+      } else {
+        const float* ss = reinterpret_cast<const float*>(smem + 2 * S::STAGE + buf * S::SCALE_STAGE);
+        i32x8 af[S::FM];
+        float sav[S::FM][4];
+#pragma unroll
+        for (int i = 0; i < S::FM; ++i) {
+          const int r = wm * S::TM + i * 16 + lr;
+          i32x4 lo = *reinterpret_cast<const i32x4*>(sa + swz(r, 2 * kq));
+          i32x4 hi = *reinterpret_cast<const i32x4*>(sa + swz(r, 2 * kq + 1));
+          af[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sav[i][e] = ss[wm * S::TM + i * 16 + 4 * kq + e];
+        }
+#pragma unroll
+        for (int j = 0; j < S::FN; ++j) {
+          const int r = wn * S::TN + j * 16 + lr;
+          i32x4 lo = *reinterpret_cast<const i32x4*>(sb + swz(r, 2 * kq));
+          i32x4 hi = *reinterpret_cast<const i32x4*>(sb + swz(r, 2 * kq + 1));
+          i32x8 bfr = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const float sbv = ss[BM + (wn * S::TN + j * 16) / 16];
+#pragma unroll
+          for (int i = 0; i < S::FM; ++i) {
+            f32x4 p = mfma_fp8(af[i], bfr, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(p[e], sav[i][e] * sbv, acc[i][j][e]);
+          }
+        }
+      }
+      if (step + 1 < KB) store(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // ---------------------------------------------------------------- epilogues
+  if constexpr (EPI == kEpiSwiglu) {
+    constexpr int HC = BN / 2, HS = HC + 4;
+    float* sH = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int i = 0; i < S::FM; ++i)
+#pragma unroll
+      for (int p = 0; p < S::FN / 2; ++p) {
+        const int hc = (wn * (S::FN / 2) + p) * 16 + lr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = wm * S::TM + i * 16 + 4 * kq + e;
+          sH[r * HS + hc] = silu(acc[i][2 * p][e]) * acc[i][2 * p + 1][e];
+        }
+      }
+    __syncthreads();
+    uint8_t* out = static_cast<uint8_t*>(a.out);
+    if constexpr (DT == MOE_FP8_E4M3) {
+      // one 128-value group per row: scale = max|h| / 448, codes = E4M3(h / scale)
+      const int groups = (a.N / 2) / 128;
+      for (int r = wv; r < rows; r += 4) {
+        float v0 = sH[r * HS + 2 * l], v1 = sH[r * HS + 2 * l + 1];
+        float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+        float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+        uint32_t c = f32_to_e4m3(v0 / s) | (f32_to_e4m3(v1 / s) << 8);
+        *reinterpret_cast<uint16_t*>(out + static_cast<int64_t>(m0 + r) * a.ldo + nt * HC + 2 * l) =
+            static_cast<uint16_t>(c);
+        if (l == 0) a.out_scales[static_cast<int64_t>(m0 + r) * groups + nt] = s;
+      }
+    } else {
+      constexpr int CPR = HC / 8;  // 8-value chunks per row
+      for (int c = tid; c < BM * CPR; c += 256) {
+        const int r = c / CPR, cc = (c - r * CPR) * 8;
+        if (r >= rows) continue;
+        const float* v = sH + r * HS + cc;
+        uint8_t* dst = out + static_cast<int64_t>(m0 + r) * a.ldo + static_cast<int64_t>(nt * HC + cc) * esize;
+        if constexpr (DT == MOE_F32) {
+          *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+          *reinterpret_cast<f32x4*>(dst + 16) = f32x4{v[4], v[5], v[6], v[7]};
+        } else {
+          i32x4 pk;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            pk[q] = static_cast<int>(f32_to_bf16(v[2 * q]) | (static_cast<uint32_t>(f32_to_bf16(v[2 * q + 1])) << 16));
+          *reinterpret_cast<i32x4*>(dst) = pk;
+        }
+      }
+    }
+  } else {
+    constexpr int OS = BN + 4;
+    float* sO = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int i = 0; i < S::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < S::FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sO[(wm * S::TM + i * 16 + 4 * kq + e) * OS + wn * S::TN + j * 16 + lr] = acc[i][j][e];
+    __syncthreads();
+    constexpr bool out_f32 = DT == MOE_F32;
+    constexpr int osz = out_f32 ? 4 : 2;
+    constexpr int CPR = BN / 8;
+    uint8_t* out = static_cast<uint8_t*>(a.out);
+    for (int c = tid; c < BM * CPR; c += 256) {
+      const int r = c / CPR, cc = (c - r * CPR) * 8;
+      if (r >= rows) continue;
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = sO[r * OS + cc + q];
+      if constexpr (EPI == kEpiCombine) {
+        const int t = m0 + r;
+        const uint8_t* y = static_cast<const uint8_t*>(a.y);
+        for (int j = 0; j < a.top_k; ++j) {
+          const int64_t idx = static_cast<int64_t>(t) * a.top_k + j;
+          const float w = a.topk_w[idx];
+          const uint8_t* yr = y + static_cast<int64_t>(a.inv_perm[idx]) * a.ldy +
+                              static_cast<int64_t>(n0 + cc) * osz;
+          if constexpr (out_f32) {
+            f32x4 y0 = *reinterpret_cast<const f32x4*>(yr);
+            f32x4 y1 = *reinterpret_cast<const f32x4*>(yr + 16);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              v[q] = fmaf(w, y0[q], v[q]);
+              v[4 + q] = fmaf(w, y1[q], v[4 + q]);
+            }
+          } else {
+            i32x4 yv = *reinterpret_cast<const i32x4*>(yr);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              uint32_t u = static_cast<uint32_t>(yv[q]);
+              v[2 * q] = fmaf(w, __uint_as_float(u << 16), v[2 * q]);
+              v[2 * q + 1] = fmaf(w, __uint_as_float(u & 0xFFFF0000u), v[2 * q + 1]);
+            }
+          }
+        }
+      }
+      uint8_t* dst = out + static_cast<int64_t>(m0 + r) * a.ldo + static_cast<int64_t>(n0 + cc) * osz;
+      if constexpr (out_f32) {
+        *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(dst + 16) = f32x4{v[4], v[5], v[6], v[7]};
+      } else {
+        i32x4 pk;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          pk[q] = static_cast<int>(f32_to_bf16(v[2 * q]) | (static_cast<uint32_t>(f32_to_bf16(v[2 * q + 1])) << 16));
+        *reinterpret_cast<i32x4*>(dst) = pk;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ host side
+
+int gemm_bm(int dtype, int epi, int avg_rows) {
+  if (dtype == MOE_F32) return 32;
+  if (dtype == MOE_FP8_E4M3) return 128;
+  if (avg_rows <= 16) return 16;
+  if (avg_rows <= 32) return 32;
+  if (avg_rows <= 48) return 64;
+  return 128;
+}
+
+int gemm_bn(int dtype, int epi) { return (dtype == MOE_FP8_E4M3 && epi == kEpiSwiglu) ? 256 : 128; }
+
+template <int DT, int BM, int BN, int EPI>
+static hipError_t launch_one(const GemmArgs& a, int max_tiles, hipStream_t s) {
+  int nb = max_tiles * (a.N / BN);
+  if (nb <= 0) return hipSuccess;
+  hipLaunchKernelGGL((grouped_gemm_kernel<DT, BM, BN, EPI>), dim3(nb), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DT, int EPI>
+static hipError_t launch_dt(int bm, const GemmArgs& a, int max_tiles, hipStream_t s) {
+  if constexpr (DT == MOE_F32) {
+    return launch_one<DT, 32, 128, EPI>(a, max_tiles, s);
+  } else if constexpr (DT == MOE_FP8_E4M3) {
+    return launch_one<DT, 128, (EPI == kEpiSwiglu ? 256 : 128), EPI>(a, max_tiles, s);
+  } else {
+    switch (bm) {
+      case 16: return launch_one<DT, 16, 128, EPI>(a, max_tiles, s);
+      case 32: return launch_one<DT, 32, 128, EPI>(a, max_tiles, s);
+      case 64: return launch_one<DT, 64, 128, EPI>(a, max_tiles, s);
+      default: return launch_one<DT, 128, 128, EPI>(a, max_tiles, s);
+    }
+  }
+}
+
+hipError_t launch_grouped_gemm(int dtype, int epi, int bm, bool /*out_f32*/, const GemmArgs& a,
+                               int max_tiles, hipStream_t s) {
+  switch (dtype) {
+    case MOE_F32:
+      if (epi == kEpiSwiglu) return launch_dt<MOE_F32, kEpiSwiglu>(bm, a, max_tiles, s);
+      if (epi == kEpiStore) return launch_dt<MOE_F32, kEpiStore>(bm, a, max_tiles, s);
+      return launch_dt<MOE_F32, kEpiCombine>(bm, a, max_tiles, s);
+    case MOE_BF16:
+      if (epi == kEpiSwiglu) return launch_dt<MOE_BF16, kEpiSwiglu>(bm, a, max_tiles, s);
+      if (epi == kEpiStore) return launch_dt<MOE_BF16, kEpiStore>(bm, a, max_tiles, s);
+      return launch_dt<MOE_BF16, kEpiCombine>(bm, a, max_tiles, s);
+    default:
+      if (epi == kEpiSwiglu) return launch_dt<MOE_FP8_E4M3, kEpiSwiglu>(bm, a, max_tiles, s);
+      if (epi == kEpiStore) return launch_dt<MOE_FP8_E4M3, kEpiStore>(bm, a, max_tiles, s);
+      return launch_dt<MOE_FP8_E4M3, kEpiCombine>(bm, a, max_tiles, s);
+  }
+}
+
+}  // namespace moe

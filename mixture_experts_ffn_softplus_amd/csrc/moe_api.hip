@@ -1,0 +1,489 @@
+// moe_api.hip -- the C ABI of include/moe.h: argument checks, workspace layout, packing and
+// the launch sequence of the block (route -> permute -> expert FFN -> combine) on one stream.
+#include <math.h>
+#include <string.h>
+
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool is_fp8(const moe_config_t* c) { return c->expert_dtype == MOE_FP8_E4M3; }
+
+// Bytes of one element of an expert operand (weights and h), of x / out, and of y_perm.
+int weight_bytes(const moe_config_t* c) {
+  return c->expert_dtype == MOE_F32 ? 4 : c->expert_dtype == MOE_BF16 ? 2 : 1;
+}
+int act_bytes(const moe_config_t* c) { return c->act_dtype == MOE_F32 ? 4 : 2; }
+int y_bytes(const moe_config_t* c) { return c->expert_dtype == MOE_F32 ? 4 : 2; }
+
+int e_pad(const moe_config_t* c) { return (c->num_experts + 15) / 16 * 16; }
+int64_t assignments(const moe_config_t* c) {
+  return static_cast<int64_t>(c->num_tokens) * c->top_k;
+}
+int64_t shared_width(const moe_config_t* c) {
+  return static_cast<int64_t>(c->num_shared) * c->d_ff_shared;
+}
+
+int router_kind(const moe_config_t* c) {
+  if (c->router_dtype == MOE_F32 && c->act_dtype == MOE_F32) return kRouterF32;
+  if (c->router_dtype == MOE_BF16) return kRouterBF16;
+  return kRouterBF16HiLo;
+}
+
+int routed_bm(const moe_config_t* c) {
+  int64_t avg = c->num_experts > 0 ? assignments(c) / c->num_experts : 0;
+  return gemm_bm(c->expert_dtype, kEpiSwiglu, static_cast<int>(avg < 1 << 20 ? avg : 1 << 20));
+}
+int shared_bm(const moe_config_t* c) {
+  if (c->expert_dtype != MOE_BF16) return gemm_bm(c->expert_dtype, kEpiSwiglu, 0);
+  int T = c->num_tokens;
+  return T <= 16 ? 16 : T <= 32 ? 32 : T <= 64 ? 64 : 128;
+}
+int64_t routed_max_tiles(const moe_config_t* c) {
+  int bm = routed_bm(c);
+  return (assignments(c) + bm - 1) / bm + c->num_experts;
+}
+
+moe_status_t check_config(const moe_config_t* c) {
+  if (!c) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->num_tokens < 0 || c->d_model <= 0 || c->num_experts <= 0 || c->top_k < 1 ||
+      c->top_k > c->num_experts || c->d_ff <= 0 || c->num_shared < 0 ||
+      (c->num_shared > 0 && c->d_ff_shared <= 0))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (c->score < MOE_SCORE_SOFTMAX || c->score > MOE_SCORE_SQRT_SOFTPLUS)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (!isfinite(c->routed_scale)) return MOE_ERR_INVALID_ARGUMENT;
+  const int dts[3] = {c->act_dtype, c->expert_dtype, c->router_dtype};
+  for (int v : dts)
+    if (v < MOE_F32 || v > MOE_FP8_E4M3) return MOE_ERR_INVALID_ARGUMENT;
+  const bool ok_types =
+      (c->act_dtype == MOE_F32 && c->expert_dtype == MOE_F32 && c->router_dtype == MOE_F32) ||
+      (c->act_dtype == MOE_BF16 && c->expert_dtype == MOE_BF16 && c->router_dtype == MOE_BF16) ||
+      (c->act_dtype == MOE_BF16 && c->expert_dtype == MOE_FP8_E4M3 &&
+       c->router_dtype != MOE_FP8_E4M3);
+  if (!ok_types) return MOE_ERR_UNSUPPORTED;
+  if (is_fp8(c) && c->quant_block != 128) return MOE_ERR_UNSUPPORTED;
+  if (c->d_model % 128 || c->d_ff % 128 || (c->num_shared > 0 && c->d_ff_shared % 128))
+    return MOE_ERR_UNSUPPORTED;
+  if (c->num_experts > 1024 || c->top_k > 64) return MOE_ERR_UNSUPPORTED;
+  if (assignments(c) > (1LL << 30) || shared_width(c) > (1 << 20)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+struct WsLayout {
+  size_t ids, w, offsets, perm, inv, hist, tiles, tiles_count, xq, xq_scales, h, h_scales, hs,
+      hs_scales, y, total;
+};
+
+WsLayout ws_layout(const moe_config_t* c) {
+  WsLayout L{};
+  const int64_t A = assignments(c), T = c->num_tokens, d = c->d_model, f = c->d_ff;
+  const int64_t fs = shared_width(c);
+  const int hb = weight_bytes(c);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  L.ids = take(A * 4);
+  L.w = take(A * 4);
+  L.offsets = take((c->num_experts + 1) * 4);
+  L.perm = take(A * 4);
+  L.inv = take(A * 4);
+  L.hist = take(static_cast<size_t>(permute_num_chunks(c->num_tokens, c->top_k)) *
+                c->num_experts * 4);
+  L.tiles = take(routed_max_tiles(c) * 16);
+  L.tiles_count = take(4);
+  L.xq = take(is_fp8(c) ? T * d : 0);
+  L.xq_scales = take(is_fp8(c) ? T * (d / 128) * 4 : 0);
+  L.h = take(A * f * hb);
+  L.h_scales = take(is_fp8(c) ? A * (f / 128) * 4 : 0);
+  L.hs = take(T * fs * hb);
+  L.hs_scales = take(is_fp8(c) ? T * (fs / 128) * 4 : 0);
+  L.y = take(A * d * y_bytes(c));
+  L.total = o;
+  return L;
+}
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off);
+}
+
+moe_status_t check_ws(const moe_config_t* c, const void* ws, size_t ws_bytes) {
+  if (!ws) return MOE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < ws_layout(c).total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return MOE_OK;
+}
+
+moe_status_t check_weights(const moe_config_t* c, const moe_weights_t* w, bool router,
+                           bool routed, bool shared) {
+  if (!w) return MOE_ERR_INVALID_ARGUMENT;
+  if (router && !w->w_router) return MOE_ERR_INVALID_ARGUMENT;
+  if (routed && (!w->w_gate_up || !w->w_down)) return MOE_ERR_INVALID_ARGUMENT;
+  if (routed && is_fp8(c) && (!w->w_gate_up_scales || !w->w_down_scales))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (shared && c->num_shared > 0) {
+    if (!w->ws_gate_up || !w->ws_down) return MOE_ERR_INVALID_ARGUMENT;
+    if (is_fp8(c) && (!w->ws_gate_up_scales || !w->ws_down_scales))
+      return MOE_ERR_INVALID_ARGUMENT;
+  }
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- launch sequences
+
+hipError_t do_route(const moe_config_t* c, const void* x, const moe_weights_t* w, float* logits,
+                    int32_t* ids, float* tw, void* xq, float* xq_scales, hipStream_t s) {
+  RouteArgs a{};
+  a.x = x;
+  a.w = w->w_router;
+  a.logit_bias = w->logit_bias;
+  a.select_bias = w->select_bias;
+  a.logits = logits;
+  a.ids = ids;
+  a.weights = tw;
+  a.T = c->num_tokens;
+  a.d = c->d_model;
+  a.E = c->num_experts;
+  a.E_pad = e_pad(c);
+  a.k = c->top_k;
+  a.score = c->score;
+  a.renorm = c->renormalize;
+  a.gamma = c->routed_scale;
+  hipError_t e = launch_router_topk(router_kind(c), a, s);
+  if (e != hipSuccess) return e;
+  if (is_fp8(c) && xq && xq_scales)
+    e = launch_quant_x_fp8(static_cast<const uint16_t*>(x), static_cast<uint8_t*>(xq), xq_scales,
+                           c->num_tokens, c->d_model, s);
+  return e;
+}
+
+// Records stage event i when the caller asked for stage timing.
+hipError_t mark(hipEvent_t* ev, int i, hipStream_t s) {
+  return ev ? hipEventRecord(ev[i], s) : hipSuccess;
+}
+
+hipError_t do_expert_ffn(const moe_config_t* c, const void* xa, const float* xs,
+                         const int32_t* offsets, const int32_t* perm, const moe_weights_t* w,
+                         void* y, void* ws, hipStream_t s, hipEvent_t* ev = nullptr) {
+  const WsLayout L = ws_layout(c);
+  const int64_t A = assignments(c), d = c->d_model, f = c->d_ff;
+  const int wb = weight_bytes(c);
+  const int bm = routed_bm(c);
+  int4* tiles = at<int4>(ws, L.tiles);
+  int32_t* tcount = at<int32_t>(ws, L.tiles_count);
+  hipError_t e = launch_tile_list(offsets, c->num_experts, bm, tiles, tcount, s);
+  if (e == hipSuccess) e = mark(ev, MOE_STAGE_TILED, s);
+  if (e != hipSuccess) return e;
+  const int max_tiles = static_cast<int>(routed_max_tiles(c));
+
+  GemmArgs g{};
+  g.A = xa;
+  g.lda = d * (is_fp8(c) ? 1 : act_bytes(c));
+  g.a_map = perm;
+  g.a_scales = xs;
+  g.B = w->w_gate_up;
+  g.b_group_stride = 2 * f * d * wb;
+  g.b_scales = w->w_gate_up_scales;
+  g.bs_group_stride = (2 * f / 16) * (d / 128);
+  g.K = static_cast<int>(d);
+  g.N = static_cast<int>(2 * f);
+  g.tiles = tiles;
+  g.tiles_count = tcount;
+  g.M = static_cast<int>(A);
+  g.out = at<uint8_t>(ws, L.h);
+  g.ldo = f * wb;
+  g.out_scales = is_fp8(c) ? at<float>(ws, L.h_scales) : nullptr;
+  e = launch_grouped_gemm(c->expert_dtype, kEpiSwiglu, bm, false, g, max_tiles, s);
+  if (e == hipSuccess) e = mark(ev, MOE_STAGE_GATE_UP, s);
+  if (e != hipSuccess) return e;
+
+  GemmArgs h{};
+  h.A = at<uint8_t>(ws, L.h);
+  h.lda = f * wb;
+  h.a_map = nullptr;
+  h.a_scales = is_fp8(c) ? at<float>(ws, L.h_scales) : nullptr;
+  h.B = w->w_down;
+  h.b_group_stride = d * f * wb;
+  h.b_scales = w->w_down_scales;
+  h.bs_group_stride = (d / 16) * (f / 128);
+  h.K = static_cast<int>(f);
+  h.N = static_cast<int>(d);
+  h.tiles = tiles;
+  h.tiles_count = tcount;
+  h.M = static_cast<int>(A);
+  h.out = y;
+  h.ldo = d * y_bytes(c);
+  e = launch_grouped_gemm(c->expert_dtype, kEpiStore, bm, false, h, max_tiles, s);
+  if (e == hipSuccess) e = mark(ev, MOE_STAGE_DOWN, s);
+  return e;
+}
+
+hipError_t do_combine(const moe_config_t* c, const void* xa, const float* xs, const void* y,
+                      const int32_t* inv, const float* tw, const moe_weights_t* w, void* out,
+                      void* ws, hipStream_t s, hipEvent_t* ev = nullptr) {
+  const WsLayout L = ws_layout(c);
+  const int64_t T = c->num_tokens, d = c->d_model, F = shared_width(c);
+  const int wb = weight_bytes(c);
+  const int bm = shared_bm(c);
+  const int max_tiles = static_cast<int>((T + bm - 1) / bm);
+  hipError_t e;
+  if (c->num_shared > 0) {
+    GemmArgs g{};
+    g.A = xa;
+    g.lda = d * (is_fp8(c) ? 1 : act_bytes(c));
+    g.a_scales = xs;
+    g.B = w->ws_gate_up;
+    g.b_scales = w->ws_gate_up_scales;
+    g.K = static_cast<int>(d);
+    g.N = static_cast<int>(2 * F);
+    g.M = static_cast<int>(T);
+    g.out = at<uint8_t>(ws, L.hs);
+    g.ldo = F * wb;
+    g.out_scales = is_fp8(c) ? at<float>(ws, L.hs_scales) : nullptr;
+    e = launch_grouped_gemm(c->expert_dtype, kEpiSwiglu, bm, false, g, max_tiles, s);
+    if (e != hipSuccess) return e;
+  }
+  e = mark(ev, MOE_STAGE_SHARED_GATE_UP, s);
+  if (e != hipSuccess) return e;
+  GemmArgs h{};
+  h.A = at<uint8_t>(ws, L.hs);
+  h.lda = F * wb;
+  h.a_scales = is_fp8(c) ? at<float>(ws, L.hs_scales) : nullptr;
+  h.B = w->ws_down;
+  h.b_scales = w->ws_down_scales;
+  h.K = static_cast<int>(F);
+  h.N = static_cast<int>(d);
+  h.M = static_cast<int>(T);
+  h.out = out;
+  h.ldo = d * act_bytes(c);
+  h.y = y;
+  h.ldy = d * y_bytes(c);
+  h.inv_perm = inv;
+  h.topk_w = tw;
+  h.top_k = c->top_k;
+  e = launch_grouped_gemm(c->expert_dtype, kEpiCombine, bm, false, h, max_tiles, s);
+  if (e == hipSuccess) e = mark(ev, MOE_STAGE_COMBINE, s);
+  return e;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t st) {
+  switch (st) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+size_t moe_workspace_size(const moe_config_t* cfg) {
+  if (check_config(cfg) != MOE_OK) return 0;
+  return ws_layout(cfg).total;
+}
+
+size_t moe_packed_size(const moe_config_t* c, int which) {
+  if (check_config(c) != MOE_OK) return 0;
+  const size_t d = c->d_model, f = c->d_ff, E = c->num_experts, F = shared_width(c);
+  const size_t wb = weight_bytes(c);
+  const bool q = is_fp8(c);
+  switch (which) {
+    case MOE_PACK_ROUTER: {
+      int k = router_kind(c);
+      size_t eb = k == kRouterF32 ? 4 : k == kRouterBF16 ? 2 : 4;  // hi/lo: two bf16 planes
+      return static_cast<size_t>(e_pad(c)) * d * eb;
+    }
+    case MOE_PACK_GATE_UP: return E * 2 * f * d * wb;
+    case MOE_PACK_GATE_UP_SCALES: return q ? E * (2 * f / 16) * (d / 128) * 4 : 0;
+    case MOE_PACK_DOWN: return E * d * f * wb;
+    case MOE_PACK_DOWN_SCALES: return q ? E * (d / 16) * (f / 128) * 4 : 0;
+    case MOE_PACK_SHARED_GATE_UP: return 2 * F * d * wb;
+    case MOE_PACK_SHARED_GATE_UP_SCALES: return q ? (2 * F / 16) * (d / 128) * 4 : 0;
+    case MOE_PACK_SHARED_DOWN: return d * F * wb;
+    case MOE_PACK_SHARED_DOWN_SCALES: return q ? (d / 16) * (F / 128) * 4 : 0;
+    default: return 0;
+  }
+}
+
+moe_status_t moe_pack_weights(const moe_config_t* c, const moe_logical_weights_t* lw,
+                              void* const* packed, hipStream_t s) {
+  moe_status_t st = check_config(c);
+  if (st != MOE_OK) return st;
+  if (!lw || !packed) return MOE_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < MOE_PACK_COUNT; ++i)
+    if (moe_packed_size(c, i) > 0 && !packed[i]) return MOE_ERR_INVALID_ARGUMENT;
+  if (!lw->w_router || !lw->w_gate || !lw->w_up || !lw->w_down) return MOE_ERR_INVALID_ARGUMENT;
+  const bool q = is_fp8(c);
+  if (q && (!lw->w_gate_scales || !lw->w_up_scales || !lw->w_down_scales))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (c->num_shared > 0) {
+    if (!lw->ws_gate || !lw->ws_up || !lw->ws_down) return MOE_ERR_INVALID_ARGUMENT;
+    if (q && (!lw->ws_gate_scales || !lw->ws_up_scales || !lw->ws_down_scales))
+      return MOE_ERR_INVALID_ARGUMENT;
+  }
+  const int d = c->d_model, f = c->d_ff, E = c->num_experts, wb = weight_bytes(c);
+  hipError_t e;
+  const int rk = router_kind(c);
+  e = launch_pack_router(lw->w_router, c->router_dtype == MOE_F32 ? 4 : 2,
+                         rk == kRouterBF16HiLo, packed[MOE_PACK_ROUTER], d, E, e_pad(c), s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = launch_pack_gate_up(lw->w_gate, lw->w_up, packed[MOE_PACK_GATE_UP], d, f, 1, E, wb, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = launch_pack_down(lw->w_down, packed[MOE_PACK_DOWN], d, f, 1, E, wb, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (q) {
+    e = launch_pack_scales_gate_up(lw->w_gate_scales, lw->w_up_scales,
+                                   static_cast<float*>(packed[MOE_PACK_GATE_UP_SCALES]), d, f, 1,
+                                   E, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    e = launch_pack_scales_down(lw->w_down_scales,
+                                static_cast<float*>(packed[MOE_PACK_DOWN_SCALES]), d, f, 1, E, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  if (c->num_shared > 0) {
+    const int S = c->num_shared, fs = c->d_ff_shared;
+    e = launch_pack_gate_up(lw->ws_gate, lw->ws_up, packed[MOE_PACK_SHARED_GATE_UP], d, fs, S, 1,
+                            wb, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    e = launch_pack_down(lw->ws_down, packed[MOE_PACK_SHARED_DOWN], d, fs, S, 1, wb, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    if (q) {
+      e = launch_pack_scales_gate_up(lw->ws_gate_scales, lw->ws_up_scales,
+                                     static_cast<float*>(packed[MOE_PACK_SHARED_GATE_UP_SCALES]),
+                                     d, fs, S, 1, s);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+      e = launch_pack_scales_down(lw->ws_down_scales,
+                                  static_cast<float*>(packed[MOE_PACK_SHARED_DOWN_SCALES]), d, fs,
+                                  S, 1, s);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+  }
+  return MOE_OK;
+}
+
+moe_status_t moe_route(const moe_config_t* c, const void* x, const moe_weights_t* w,
+                       float* logits, int32_t* ids, float* tw, void* xq, float* xq_scales,
+                       void* ws, size_t ws_bytes, hipStream_t s) {
+  (void)ws;
+  (void)ws_bytes;
+  moe_status_t st = check_config(c);
+  if (st != MOE_OK) return st;
+  if (!x || !ids || !tw) return MOE_ERR_INVALID_ARGUMENT;
+  if ((st = check_weights(c, w, true, false, false)) != MOE_OK) return st;
+  if (c->num_tokens == 0) return MOE_OK;
+  return hip_status(do_route(c, x, w, logits, ids, tw, xq, xq_scales, s));
+}
+
+moe_status_t moe_route_from_logits(const moe_config_t* c, const float* logits,
+                                   const float* select_bias, int32_t* ids, float* tw,
+                                   hipStream_t s) {
+  moe_status_t st = check_config(c);
+  if (st != MOE_OK) return st;
+  if (!logits || !ids || !tw) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->num_tokens == 0) return MOE_OK;
+  RouteArgs a{};
+  a.select_bias = select_bias;
+  a.logits = const_cast<float*>(logits);
+  a.ids = ids;
+  a.weights = tw;
+  a.T = c->num_tokens;
+  a.d = c->d_model;
+  a.E = c->num_experts;
+  a.E_pad = e_pad(c);
+  a.k = c->top_k;
+  a.score = c->score;
+  a.renorm = c->renormalize;
+  a.gamma = c->routed_scale;
+  return hip_status(launch_topk_from_logits(a, s));
+}
+
+moe_status_t moe_permute(const moe_config_t* c, const int32_t* ids, int32_t* offsets,
+                         int32_t* perm, int32_t* inv, void* ws, size_t ws_bytes, hipStream_t s) {
+  moe_status_t st = check_config(c);
+  if (st != MOE_OK) return st;
+  if (!ids || !offsets || !perm || !inv) return MOE_ERR_INVALID_ARGUMENT;
+  if ((st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
+  if (c->num_tokens == 0) return MOE_OK;
+  const WsLayout L = ws_layout(c);
+  return hip_status(launch_permute(ids, c->num_tokens, c->top_k, c->num_experts, offsets, perm,
+                                   inv, at<int32_t>(ws, L.hist), s));
+}
+
+moe_status_t moe_expert_ffn(const moe_config_t* c, const void* xa, const float* xs,
+                            const int32_t* offsets, const int32_t* perm, const moe_weights_t* w,
+                            void* y, void* ws, size_t ws_bytes, hipStream_t s) {
+  moe_status_t st = check_config(c);
+  if (st != MOE_OK) return st;
+  if (!xa || !offsets || !perm || !y || (is_fp8(c) && !xs)) return MOE_ERR_INVALID_ARGUMENT;
+  if ((st = check_weights(c, w, false, true, false)) != MOE_OK) return st;
+  if ((st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
+  if (c->num_tokens == 0) return MOE_OK;
+  return hip_status(do_expert_ffn(c, xa, xs, offsets, perm, w, y, ws, s));
+}
+
+moe_status_t moe_combine(const moe_config_t* c, const void* xa, const float* xs, const void* y,
+                         const int32_t* inv, const float* tw, const moe_weights_t* w, void* out,
+                         void* ws, size_t ws_bytes, hipStream_t s) {
+  moe_status_t st = check_config(c);
+  if (st != MOE_OK) return st;
+  if (!y || !inv || !tw || !out) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->num_shared > 0 && (!xa || (is_fp8(c) && !xs))) return MOE_ERR_INVALID_ARGUMENT;
+  if ((st = check_weights(c, w, false, false, true)) != MOE_OK) return st;
+  if ((st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
+  if (c->num_tokens == 0) return MOE_OK;
+  return hip_status(do_combine(c, xa, xs, y, inv, tw, w, out, ws, s));
+}
+
+moe_status_t moe_forward(const moe_config_t* c, const void* x, const moe_weights_t* w, void* out,
+                         const moe_debug_t* dbg, void* ws, size_t ws_bytes, hipStream_t s) {
+  moe_status_t st = check_config(c);
+  if (st != MOE_OK) return st;
+  if (!x || !out) return MOE_ERR_INVALID_ARGUMENT;
+  if ((st = check_weights(c, w, true, true, true)) != MOE_OK) return st;
+  if ((st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
+  if (c->num_tokens == 0) return MOE_OK;
+  const WsLayout L = ws_layout(c);
+  moe_debug_t d{};
+  if (dbg) d = *dbg;
+  int32_t* ids = d.topk_ids ? d.topk_ids : at<int32_t>(ws, L.ids);
+  float* tw = d.topk_w ? d.topk_w : at<float>(ws, L.w);
+  int32_t* offsets = d.expert_offsets ? d.expert_offsets : at<int32_t>(ws, L.offsets);
+  int32_t* perm = d.perm_token ? d.perm_token : at<int32_t>(ws, L.perm);
+  int32_t* inv = d.inv_perm ? d.inv_perm : at<int32_t>(ws, L.inv);
+  void* y = d.y_perm ? d.y_perm : at<void>(ws, L.y);
+  void* xq = is_fp8(c) ? at<void>(ws, L.xq) : nullptr;
+  float* xs = is_fp8(c) ? at<float>(ws, L.xq_scales) : nullptr;
+  const void* xa = is_fp8(c) ? static_cast<const void*>(xq) : x;
+  hipEvent_t* ev = d.stage_events;
+  hipError_t e = mark(ev, MOE_STAGE_BEGIN, s);
+  if (e == hipSuccess) e = do_route(c, x, w, d.logits, ids, tw, xq, xs, s);
+  if (e == hipSuccess) e = mark(ev, MOE_STAGE_ROUTED, s);
+  if (e == hipSuccess)
+    e = launch_permute(ids, c->num_tokens, c->top_k, c->num_experts, offsets, perm, inv,
+                       at<int32_t>(ws, L.hist), s);
+  if (e == hipSuccess) e = mark(ev, MOE_STAGE_PERMUTED, s);
+  if (e == hipSuccess) e = do_expert_ffn(c, xa, xs, offsets, perm, w, y, ws, s, ev);
+  if (e == hipSuccess) e = do_combine(c, xa, xs, y, inv, tw, w, out, ws, s, ev);
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// moe_common.h -- device building blocks shared by the gfx950 kernels of the MoE block.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;     // MI355X: 8 XCDs, workgroups dispatched round-robin over them
+constexpr int kBlockK = 128;   // bytes of K per pipeline step (= one FP8 scale block)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// ----------------------------------------------------------------------------- conversions
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even (the hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 h = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// E4M3FN code nearest to r: ties to even, saturating at +-448 (NaN inputs unsupported).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float r) {
+  uint32_t u = __float_as_uint(r);
+  uint32_t sign = (u >> 24) & 0x80u;
+  float a = fabsf(r);
+  if (a >= 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f) {                       // below 2^-6: multiples of 2^-9
+    uint32_t m = static_cast<uint32_t>(rintf(a * 512.0f));  // exact scaling, RNE
+    return sign | m;                          // m == 8 encodes 2^-6 correctly
+  }
+  uint32_t ua = __float_as_uint(a);
+  ua += 0x7FFFFu + ((ua >> 20) & 1u);         // round the 23-bit mantissa to 3 bits, ties even
+  uint32_t e = ((ua >> 23) & 0xFFu) - 127u + 7u;
+  uint32_t m = (ua >> 20) & 7u;
+  return sign | (e << 3) | m;
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float mag = e == 0 ? static_cast<float>(m) * 0.001953125f
+                     : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// ----------------------------------------------------------------------------- MFMA
+// 16x16 output blocks, fp32 accumulate.  Lane l holds output column (l % 16) and
+// rows 4*(l / 16) + i, i = 0..3.  Operands: lane l supplies row (A) / column (B)
+// (l % 16) and one K-slice chosen by (l / 16); A and B use the same K-slices.
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// E4M3 x E4M3, K = 128 per instruction (format selectors 0 = E4M3, unit scales).
+__device__ __forceinline__ f32x4 mfma_fp8(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// ----------------------------------------------------------------------------- wave utilities
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Logical block id with the blocks of one XCD made contiguous: hardware block b
+// runs on XCD b % 8, so consecutive logical ids (neighbouring tiles that share
+// operands) land in the same XCD's L2.  Bijective on [0, n).
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  int q = n / kNumXcd, r = n % kNumXcd;
+  int xcd = b % kNumXcd, local = b / kNumXcd;
+  return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+}  // namespace moe

@@ -1,0 +1,98 @@
+// moe_internal.h -- host-side launchers shared between the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---- router (route.hip)
+struct RouteArgs {
+  const void* x;             // [T, d] act dtype
+  const void* w;             // packed router [E_pad, d] (or [2, E_pad, d] hi/lo)
+  const float* logit_bias;   // [E] or null
+  const float* select_bias;  // [E] or null
+  float* logits;             // [T, E] or null
+  int32_t* ids;              // [T, k]
+  float* weights;            // [T, k]
+  int T, d, E, E_pad, k;
+  int score, renorm;
+  float gamma;
+};
+enum RouterKind { kRouterF32 = 0, kRouterBF16 = 1, kRouterBF16HiLo = 2 };
+hipError_t launch_router_topk(int kind, const RouteArgs& a, hipStream_t s);
+hipError_t launch_topk_from_logits(const RouteArgs& a, hipStream_t s);
+hipError_t launch_quant_x_fp8(const uint16_t* x, uint8_t* xq, float* scales, int T, int d,
+                              hipStream_t s);
+
+// ---- permutation (permute.hip)
+int permute_num_chunks(int T, int k);
+hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
+                          int32_t* perm_token, int32_t* inv_perm, int32_t* hist,
+                          hipStream_t s);
+hipError_t launch_tile_list(const int32_t* offsets, int E, int bm, int4* tiles,
+                            int32_t* tiles_count, hipStream_t s);
+
+// ---- grouped GEMMs (gemm.hip)
+enum Epilogue { kEpiSwiglu = 0, kEpiStore = 1, kEpiCombine = 2 };
+
+struct GemmArgs {
+  // A: activations, K-contiguous rows
+  const void* A;
+  int64_t lda;                // bytes per A row
+  const int32_t* a_map;       // row of the M space -> A row, or null (identity)
+  const float* a_scales;      // FP8: [A rows, K/128]
+  // B: packed weights of each group, [N, K] K-contiguous
+  const void* B;
+  int64_t b_group_stride;     // bytes per group
+  const float* b_scales;      // FP8: [N/128, K/128] per group
+  int64_t bs_group_stride;    // floats per group
+  int K, N;
+  // tiles of rows: a device list {group, first row, rows} (grouped), or one group of M rows
+  const int4* tiles;          // null: one group, rows [0, M)
+  const int32_t* tiles_count; // device count of `tiles`
+  int M;
+  // output
+  void* out;
+  int64_t ldo;                // bytes per output row
+  float* out_scales;          // FP8 h: [rows, out_cols/128]
+  // combine epilogue
+  const void* y;              // y_perm [T*k, N]
+  int64_t ldy;                // bytes per y row
+  const int32_t* inv_perm;
+  const float* topk_w;
+  int top_k;
+};
+
+// dtype: MOE_F32 / MOE_BF16 / MOE_FP8_E4M3 (operands); out_f32: output rows fp32.
+int gemm_bm(int dtype, int epi, int avg_rows);
+hipError_t launch_grouped_gemm(int dtype, int epi, int bm, bool out_f32, const GemmArgs& a,
+                               int max_tiles, hipStream_t s);
+
+// ---- packing (pack.hip)
+// Packed gate/up of one group: [2F, K] K-contiguous, rows in blocks of 16 alternating
+// gate / up: packed row p = 32c + j (j < 16) is gate column 16c + j, p = 32c + 16 + j is up
+// column 16c + j.  F = sub * C: `sub` source experts of C columns each are concatenated
+// (the shared experts).  Sources are logical [K, C] (row-major), `groups` of them in a row
+// per operand, each group taking `sub` consecutive sources.
+hipError_t launch_pack_gate_up(const void* gate, const void* up, void* dst, int K, int C,
+                               int sub, int groups, int esize, hipStream_t s);
+// Packed down of one group: [N, F] with F = sub * C; packed[n][s*C + c] = down_s[c][n],
+// sources logical [C, N].
+hipError_t launch_pack_down(const void* down, void* dst, int N, int C, int sub, int groups,
+                            int esize, hipStream_t s);
+// Router [d, E] -> [E_pad, d] (rows >= E zero).  hilo: fp32 source split into bf16 hi and
+// lo = bf16(w - hi) planes [2, E_pad, d]; otherwise the element type is kept.
+hipError_t launch_pack_router(const void* wr, int esize, int hilo, void* dst, int d, int E,
+                              int E_pad, hipStream_t s);
+// FP8 block scales, one per 16 packed rows and 128 K values:
+//   gate/up: dst[g][p16][kb] from gate/up scales [K/128, C/128] of the source expert;
+//   down:    dst[g][n16][kb] from down scales [C/128, N/128].
+hipError_t launch_pack_scales_gate_up(const float* gs, const float* us, float* dst, int K, int C,
+                                      int sub, int groups, hipStream_t s);
+hipError_t launch_pack_scales_down(const float* ds, float* dst, int N, int C, int sub,
+                                   int groups, hipStream_t s);
+
+}  // namespace moe

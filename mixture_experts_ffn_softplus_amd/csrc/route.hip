@@ -1,0 +1,271 @@
+// route.hip -- router GEMM fused with scoring and top-k, plus the FP8 activation quantiser.
+//
+// The router of the archdiff.com pages ("Qwen3.5-397B-A17B vs DeepSeek-V4-Pro", component
+// table, router row): a linear map of the token to one logit per expert; then either a
+// softmax over the experts with the top k kept and renormalised (Qwen3.5 cell), or
+// sqrt-softplus (or sigma, blueprint router box) scores with a per-expert bias added only for
+// choosing the top k, the chosen unbiased scores normalised and scaled by 2.5 (DeepSeek-V4-Pro
+// cell).  Ties at equal keys go to the lower expert index.
+//
+// One workgroup (4 waves) owns 16 tokens and all E_pad experts: the 16 x E_pad logit tile is
+// accumulated on MFMA (each wave a quarter of the 16-expert column blocks, operands streamed
+// straight from global memory: x rows are shared through L1, every router column is read by
+// exactly one wave), parked in LDS, then each wave selects the top k of four tokens with k
+// rounds of a 64-lane argmax.
+#include <math.h>
+
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kRouterRows = 16;       // tokens per workgroup
+constexpr int kMaxColBlocks = 16;     // 16-expert blocks per wave: E_pad <= 1024
+constexpr int kMaxPerLane = 16;       // experts per lane in top-k: E <= 1024
+
+// Score of the sigma family, evaluated in fp64 and rounded once to fp32, so the
+// selection key is one fixed fp32 number.
+__device__ __forceinline__ float sigma_family_score(int score, float l) {
+  double s;
+  if (score == MOE_SCORE_SIGMOID) {
+    s = 1.0 / (1.0 + exp(-static_cast<double>(l)));
+  } else {
+    double ld = static_cast<double>(l);
+    s = sqrt(fmax(ld, 0.0) + log1p(exp(-fabs(ld))));
+  }
+  return static_cast<float>(s);
+}
+
+// Top-k of one token over `row[0..E)` (LDS or global), executed by one full wave.
+__device__ void topk_row(const float* row, int t, const RouteArgs& a) {
+  const int l = lane_id();
+  float key[kMaxPerLane], val[kMaxPerLane];
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    int e = l + kWave * i;
+    key[i] = -INFINITY;
+    val[i] = 0.0f;
+    if (e < a.E) {
+      float lg = row[e];
+      if (a.score == MOE_SCORE_SOFTMAX) {
+        key[i] = lg;
+        val[i] = lg;
+      } else {
+        float s = sigma_family_score(a.score, lg);
+        float b = a.select_bias ? a.select_bias[e] : 0.0f;
+        val[i] = s;
+        key[i] = __fadd_rn(s, b);
+      }
+    }
+  }
+  uint32_t taken = 0;
+  int my_id = 0;
+  float my_val = 0.0f;
+  for (int j = 0; j < a.k; ++j) {
+    float bk = -INFINITY, bv = 0.0f;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) {
+      int e = l + kWave * i;
+      bool ok = e < a.E && !((taken >> i) & 1u);
+      if (ok && (key[i] > bk || (key[i] == bk && e < be))) {
+        bk = key[i];
+        be = e;
+        bv = val[i];
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      float ok_ = __shfl_xor(bk, o, kWave);
+      int oe = __shfl_xor(be, o, kWave);
+      float ov = __shfl_xor(bv, o, kWave);
+      if (ok_ > bk || (ok_ == bk && oe < be)) {
+        bk = ok_;
+        be = oe;
+        bv = ov;
+      }
+    }
+    if ((be & (kWave - 1)) == l) taken |= 1u << (be >> 6);
+    if (l == j) {
+      my_id = be;
+      my_val = bv;
+    }
+  }
+  float w;
+  if (a.score == MOE_SCORE_SOFTMAX) {
+    float m = __shfl(my_val, 0, kWave);  // slot 0 holds the largest logit
+    float denom;
+    if (a.renorm) {
+      denom = wave_sum(l < a.k ? expf(my_val - m) : 0.0f);
+    } else {
+      float part = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kMaxPerLane; ++i)
+        if (l + kWave * i < a.E) part += expf(val[i] - m);
+      denom = wave_sum(part);
+    }
+    w = a.gamma * expf(my_val - m) / denom;
+  } else {
+    float denom = a.renorm ? wave_sum(l < a.k ? my_val : 0.0f) : 1.0f;
+    w = a.gamma * my_val / denom;
+  }
+  if (l < a.k) {
+    a.ids[static_cast<size_t>(t) * a.k + l] = my_id;
+    a.weights[static_cast<size_t>(t) * a.k + l] = w;
+  }
+}
+
+template <int KIND>
+__global__ __launch_bounds__(256) void router_topk_kernel(RouteArgs a) {
+  extern __shared__ float sL[];
+  const int LS = a.E_pad + 4;
+  const int wv = threadIdx.x / kWave, l = lane_id();
+  const int t0 = blockIdx.x * kRouterRows;
+  const int nb = a.E_pad / 16;
+  const int row = min(t0 + (l & 15), a.T - 1);
+  const int kq = l >> 4;  // K-slice of this lane
+
+  f32x4 acc[kMaxColBlocks];
+#pragma unroll
+  for (int i = 0; i < kMaxColBlocks; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if constexpr (KIND == kRouterF32) {
+    const float* xr = static_cast<const float*>(a.x) + static_cast<size_t>(row) * a.d + 4 * kq;
+    const float* wb = static_cast<const float*>(a.w) + 4 * kq;
+    for (int k0 = 0; k0 < a.d; k0 += 16) {
+      f32x4 av = *reinterpret_cast<const f32x4*>(xr + k0);
+#pragma unroll
+      for (int i = 0; i < kMaxColBlocks; ++i) {
+        int b = wv + 4 * i;
+        if (b < nb) {
+          f32x4 bv = *reinterpret_cast<const f32x4*>(
+              wb + static_cast<size_t>(b * 16 + (l & 15)) * a.d + k0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i] = mfma_f32(av[j], bv[j], acc[i]);
+        }
+      }
+    }
+  } else {
+    const uint16_t* xr =
+        static_cast<const uint16_t*>(a.x) + static_cast<size_t>(row) * a.d + 8 * kq;
+    const uint16_t* wb = static_cast<const uint16_t*>(a.w) + 8 * kq;
+    const size_t lo_off = static_cast<size_t>(a.E_pad) * a.d;
+#pragma unroll 2
+    for (int k0 = 0; k0 < a.d; k0 += 32) {
+      bf16x8 av = *reinterpret_cast<const bf16x8*>(xr + k0);
+#pragma unroll
+      for (int i = 0; i < kMaxColBlocks; ++i) {
+        int b = wv + 4 * i;
+        if (b < nb) {
+          const uint16_t* p = wb + static_cast<size_t>(b * 16 + (l & 15)) * a.d + k0;
+          acc[i] = mfma_bf16(av, *reinterpret_cast<const bf16x8*>(p), acc[i]);
+          if constexpr (KIND == kRouterBF16HiLo)
+            acc[i] = mfma_bf16(av, *reinterpret_cast<const bf16x8*>(p + lo_off), acc[i]);
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < kMaxColBlocks; ++i) {
+    int b = wv + 4 * i;
+    if (b < nb) {
+      int col = b * 16 + (l & 15);
+      float z = (a.logit_bias && col < a.E) ? a.logit_bias[col] : 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sL[(4 * kq + j) * LS + col] = acc[i][j] + z;
+    }
+  }
+  __syncthreads();
+
+  const int rows = min(kRouterRows, a.T - t0);
+  if (a.logits) {
+    for (int idx = threadIdx.x; idx < rows * a.E; idx += blockDim.x) {
+      int r = idx / a.E, c = idx - r * a.E;
+      a.logits[static_cast<size_t>(t0 + r) * a.E + c] = sL[r * LS + c];
+    }
+  }
+  for (int r = wv; r < rows; r += 4) topk_row(sL + r * LS, t0 + r, a);
+}
+
+__global__ __launch_bounds__(256) void topk_from_logits_kernel(RouteArgs a) {
+  int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= a.T) return;  // whole waves leave together
+  topk_row(a.logits + static_cast<size_t>(t) * a.E, t, a);
+}
+
+// Block-scaled FP8 activations: one fp32 scale = max|x| / 448 (1 for an all-zero group)
+// per 128 consecutive values of a row, codes = E4M3(x / scale), both divisions correctly
+// rounded fp32.  16 lanes own one group, 8 values each.
+__global__ __launch_bounds__(256) void quant_x_fp8_kernel(const uint16_t* __restrict__ x,
+                                                          uint8_t* __restrict__ xq,
+                                                          float* __restrict__ scales, int T,
+                                                          int d) {
+  const int groups_per_row = d / 128;
+  const int64_t total = static_cast<int64_t>(T) * groups_per_row;
+  const int64_t gid = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / 16;
+  const int sub = threadIdx.x & 15;
+  const bool valid = gid < total;
+  const int64_t g = valid ? gid : 0;
+  const int64_t row = g / groups_per_row, grp = g - row * groups_per_row;
+  const size_t base = static_cast<size_t>(row) * d + grp * 128 + sub * 8;
+  i32x4 raw = *reinterpret_cast<const i32x4*>(x + base);
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(static_cast<uint32_t>(raw[i]) << 16);
+    v[2 * i + 1] = __uint_as_float(static_cast<uint32_t>(raw[i]) & 0xFFFF0000u);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(v[i] / s) << (8 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(v[4 + i] / s) << (8 * i);
+  if (valid) {
+    uint2 packed{lo, hi};
+    *reinterpret_cast<uint2*>(xq + base) = packed;
+    if (sub == 0) scales[g] = s;
+  }
+}
+
+hipError_t launch_router_topk(int kind, const RouteArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  dim3 grid((a.T + kRouterRows - 1) / kRouterRows);
+  size_t lds = sizeof(float) * kRouterRows * (a.E_pad + 4);
+  switch (kind) {
+    case kRouterF32:
+      hipLaunchKernelGGL(router_topk_kernel<kRouterF32>, grid, dim3(256), lds, s, a);
+      break;
+    case kRouterBF16:
+      hipLaunchKernelGGL(router_topk_kernel<kRouterBF16>, grid, dim3(256), lds, s, a);
+      break;
+    default:
+      hipLaunchKernelGGL(router_topk_kernel<kRouterBF16HiLo>, grid, dim3(256), lds, s, a);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_from_logits(const RouteArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_from_logits_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_x_fp8(const uint16_t* x, uint8_t* xq, float* scales, int T, int d,
+                              hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  int64_t groups = static_cast<int64_t>(T) * (d / 128);
+  int64_t blocks = (groups * 16 + 255) / 256;
+  hipLaunchKernelGGL(quant_x_fp8_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     x, xq, scales, T, d);
+  return hipGetLastError();
+}
+
+}  // namespace moe

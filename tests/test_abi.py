@@ -1,0 +1,155 @@
+"""The C ABI without a GPU: the library loads, exports every symbol include/moe.h declares, the
+ctypes structs match the header's layout, and bad arguments return their status codes from
+the host-side checks (nothing is launched on these paths)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from mixture_experts_ffn_softplus_amd import PRESETS, api
+from mixture_experts_ffn_softplus_amd.configs import BF16, F32, FP8_E4M3
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    syms = declared_symbols()
+    assert set(syms) == set(api.EXPORTED)
+    L = api.lib()
+    for s in syms:
+        assert hasattr(L, s), s
+    out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(syms) <= exported
+    # internal kernels and helpers stay hidden
+    assert not any(s.startswith("_ZN3moe") for s in exported)
+
+
+def test_struct_layouts_match_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "moe.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(moe_config_t), offsetof(moe_config_t, routed_scale),
+         offsetof(moe_config_t, quant_block), sizeof(moe_logical_weights_t),
+         sizeof(moe_weights_t), sizeof(moe_debug_t));
+  return 0;
+}''')
+    exe = tmp_path / "layout"
+    r = subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", f"-I{os.path.dirname(HEADER)}",
+                        "-I/opt/rocm/include", str(src), "-o", str(exe)],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.skip("cannot compile the header with gcc here: " + r.stderr[:200])
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    want = [ctypes.sizeof(api.moe_config_t), api.moe_config_t.routed_scale.offset,
+            api.moe_config_t.quant_block.offset, ctypes.sizeof(api.moe_logical_weights_t),
+            ctypes.sizeof(api.moe_weights_t), ctypes.sizeof(api.moe_debug_t)]
+    assert got == want
+
+
+def test_status_strings():
+    assert api.status_string(0) == "MOE_OK"
+    assert api.status_string(3) == "MOE_ERR_WORKSPACE_TOO_SMALL"
+    assert api.status_string(99) == "MOE_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_tokens", -1, api.MOE_ERR_INVALID_ARGUMENT),
+    ("top_k", 0, api.MOE_ERR_INVALID_ARGUMENT),
+    ("top_k", 17, api.MOE_ERR_INVALID_ARGUMENT),        # k > E
+    ("num_experts", 0, api.MOE_ERR_INVALID_ARGUMENT),
+    ("score", 7, api.MOE_ERR_INVALID_ARGUMENT),
+    ("renormalize", 2, api.MOE_ERR_INVALID_ARGUMENT),
+    ("routed_scale", float("nan"), api.MOE_ERR_INVALID_ARGUMENT),
+    ("d_model", 200, api.MOE_ERR_UNSUPPORTED),           # not a multiple of 128
+    ("d_ff", 96, api.MOE_ERR_UNSUPPORTED),
+    ("expert_dtype", BF16, api.MOE_ERR_UNSUPPORTED),     # f32 activations with bf16 experts
+    ("act_dtype", 5, api.MOE_ERR_INVALID_ARGUMENT),
+])
+def test_config_errors_return_status_without_launch(field, value, status):
+    cfg = api.config_struct(PRESETS["tiny_fp32"], **{field: value})
+    assert api.moe_workspace_size(cfg) == 0
+    L = api.lib()
+    w = api.moe_weights_t()
+    rc = L.moe_forward(ctypes.byref(cfg), 1, ctypes.byref(w), 1, None, 1, 1 << 40, None)
+    assert rc == status
+
+
+def test_large_and_fp8_constraints():
+    c = api.config_struct(PRESETS["fp8_block"], quant_block=64)
+    assert api.lib().moe_workspace_size(ctypes.byref(c)) == 0
+    c = api.config_struct(PRESETS["softmax_bf16"], num_experts=2048)
+    assert api.lib().moe_route_from_logits(ctypes.byref(c), 1, None, 1, 1, None) == \
+        api.MOE_ERR_UNSUPPORTED
+    c = api.config_struct(PRESETS["softmax_bf16"], top_k=65, num_experts=512)
+    assert api.lib().moe_route_from_logits(ctypes.byref(c), 1, None, 1, 1, None) == \
+        api.MOE_ERR_UNSUPPORTED
+
+
+def test_null_pointers_and_small_workspace():
+    L = api.lib()
+    cfg = api.config_struct(PRESETS["tiny_fp32"])
+    ws_need = api.moe_workspace_size(cfg)
+    assert ws_need > 0
+    w_ok = api.moe_weights_t(*([8] * 11))
+    cp = ctypes.byref(cfg)
+    # NULL x / out / weights / ws
+    assert L.moe_forward(cp, None, ctypes.byref(w_ok), 8, None, 8, ws_need, None) == 1
+    assert L.moe_forward(cp, 8, ctypes.byref(w_ok), None, None, 8, ws_need, None) == 1
+    assert L.moe_forward(cp, 8, None, 8, None, 8, ws_need, None) == 1
+    assert L.moe_forward(cp, 8, ctypes.byref(w_ok), 8, None, None, ws_need, None) == 1
+    # missing router / expert weights
+    w_bad = api.moe_weights_t(*([8] * 11))
+    w_bad.w_router = None
+    assert L.moe_forward(cp, 8, ctypes.byref(w_bad), 8, None, 8, ws_need, None) == 1
+    w_bad = api.moe_weights_t(*([8] * 11))
+    w_bad.ws_down = None
+    assert L.moe_forward(cp, 8, ctypes.byref(w_bad), 8, None, 8, ws_need, None) == 1
+    # workspace one byte short
+    assert L.moe_forward(cp, 8, ctypes.byref(w_ok), 8, None, 8, ws_need - 1, None) == 3
+    assert L.moe_permute(cp, 8, 8, 8, 8, 8, ws_need - 1, None) == 3
+    assert L.moe_permute(cp, None, 8, 8, 8, 8, ws_need, None) == 1
+    assert L.moe_expert_ffn(cp, 8, None, 8, 8, ctypes.byref(w_ok), 8, 8, ws_need - 1, None) == 3
+    assert L.moe_combine(cp, 8, None, 8, None, 8, ctypes.byref(w_ok), 8, 8, ws_need, None) == 1
+    assert L.moe_route(cp, 8, ctypes.byref(w_ok), None, None, 8, None, None, None, 0, None) == 1
+    assert L.moe_pack_weights(cp, None, None, None) == 1
+
+
+def test_zero_tokens_is_a_valid_noop():
+    L = api.lib()
+    cfg = api.config_struct(PRESETS["softmax_bf16"], num_tokens=0)
+    n = api.moe_workspace_size(cfg)
+    assert n > 0
+    w = api.moe_weights_t(*([8] * 11))
+    assert L.moe_forward(ctypes.byref(cfg), 8, ctypes.byref(w), 8, None, 8, n, None) == 0
+    assert L.moe_route_from_logits(ctypes.byref(cfg), 8, None, 8, 8, None) == 0
+
+
+def test_packed_sizes():
+    c = PRESETS["softmax_bf16"]
+    d, f, E = c.d_model, c.d_ff, c.num_experts
+    assert api.moe_packed_size(c, api.PACK_GATE_UP) == E * 2 * f * d * 2
+    assert api.moe_packed_size(c, api.PACK_DOWN) == E * f * d * 2
+    assert api.moe_packed_size(c, api.PACK_GATE_UP_SCALES) == 0
+    assert api.moe_packed_size(c, api.PACK_ROUTER) == 512 * d * 2
+    q = PRESETS["fp8_block"]
+    assert api.moe_packed_size(q, api.PACK_GATE_UP) == 896 * 2 * 512 * 4096
+    assert api.moe_packed_size(q, api.PACK_ROUTER) == 896 * 4096 * 4      # bf16 hi + lo planes
+    assert api.moe_packed_size(q, api.PACK_DOWN_SCALES) == 896 * (4096 // 16) * (512 // 128) * 4
+    t = PRESETS["tiny_fp32"]
+    assert api.moe_packed_size(t, api.PACK_SHARED_DOWN) == 256 * 256 * 4
+    assert api.moe_packed_size(t, 42) == 0
+    assert FP8_E4M3 == 2 and F32 == 0
