@@ -160,7 +160,7 @@ typedef struct {
   int32_t* expert_offsets;   /* [E + 1] */
   int32_t* perm_token;       /* [T*k] */
   int32_t* inv_perm;         /* [T*k] */
-  void* y_perm;              /* [T*k, d], fp32 for F32 experts, else bf16 */
+  void* y_perm;              /* [T*k, d], bf16 for FP8_E4M3 experts, else fp32 */
   hipEvent_t* stage_events;  /* host array of MOE_NUM_STAGE_EVENTS events, or NULL */
 } moe_debug_t;
 
@@ -221,7 +221,7 @@ MOE_API moe_status_t moe_permute(const moe_config_t* cfg, const int32_t* topk_id
  * for every row r of expert e, h = SiLU(x~ W_gate[e]) * (x~ W_up[e]) and
  * y_perm[r] = h W_down[e], with x~ = x[perm_token[r]] (FP8: the block-scaled
  * xq / xq_scales from moe_route, and h re-quantised per 128 values).
- * y_perm [T*k, d]: fp32 for F32 experts, bf16 otherwise. */
+ * y_perm [T*k, d]: bf16 for FP8_E4M3 experts, fp32 otherwise. */
 MOE_API moe_status_t moe_expert_ffn(const moe_config_t* cfg, const void* x_or_xq, const float* xq_scales,
                             const int32_t* expert_offsets, const int32_t* perm_token,
                             const moe_weights_t* weights, void* y_perm, void* ws,

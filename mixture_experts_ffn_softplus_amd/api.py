@@ -212,7 +212,7 @@ _TORCH_ACT = {F32: torch.float32, BF16: torch.bfloat16}
 
 
 def y_dtype(cfg: MoEConfig):
-    return torch.float32 if cfg.expert_dtype == F32 else torch.bfloat16
+    return torch.bfloat16 if cfg.expert_dtype == FP8_E4M3 else torch.float32
 
 
 def out_dtype(cfg: MoEConfig):

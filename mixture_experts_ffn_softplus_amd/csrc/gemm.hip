@@ -297,8 +297,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
         for (int e = 0; e < 4; ++e)
           sO[(wm * S::TM + i * 16 + 4 * kq + e) * OS + wn * S::TN + j * 16 + lr] = acc[i][j][e];
     __syncthreads();
-    constexpr bool out_f32 = DT == MOE_F32;
+    // y_perm rows are fp32 except for FP8 experts (bf16); the block output is fp32 only
+    // for fp32 activations
+    constexpr bool y_f32 = DT != MOE_FP8_E4M3;
+    constexpr bool out_f32 = EPI == kEpiStore ? y_f32 : DT == MOE_F32;
     constexpr int osz = out_f32 ? 4 : 2;
+    constexpr int ysz = y_f32 ? 4 : 2;
     constexpr int CPR = BN / 8;
     uint8_t* out = static_cast<uint8_t*>(a.out);
     for (int c = tid; c < BM * CPR; c += 256) {
@@ -314,8 +318,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
           const int64_t idx = static_cast<int64_t>(t) * a.top_k + j;
           const float w = a.topk_w[idx];
           const uint8_t* yr = y + static_cast<int64_t>(a.inv_perm[idx]) * a.ldy +
-                              static_cast<int64_t>(n0 + cc) * osz;
-          if constexpr (out_f32) {
+                              static_cast<int64_t>(n0 + cc) * ysz;
+          if constexpr (y_f32) {
             f32x4 y0 = *reinterpret_cast<const f32x4*>(yr);
             f32x4 y1 = *reinterpret_cast<const f32x4*>(yr + 16);
 #pragma unroll

@@ -20,7 +20,9 @@ int weight_bytes(const moe_config_t* c) {
   return c->expert_dtype == MOE_F32 ? 4 : c->expert_dtype == MOE_BF16 ? 2 : 1;
 }
 int act_bytes(const moe_config_t* c) { return c->act_dtype == MOE_F32 ? 4 : 2; }
-int y_bytes(const moe_config_t* c) { return c->expert_dtype == MOE_F32 ? 4 : 2; }
+// y_perm: fp32 unless the experts are FP8.  A bf16 y_perm would add a third bf16 rounding
+// (after h and the output) to a budget the output rounding alone half fills.
+int y_bytes(const moe_config_t* c) { return c->expert_dtype == MOE_FP8_E4M3 ? 2 : 4; }
 
 int e_pad(const moe_config_t* c) { return (c->num_experts + 15) / 16 * 16; }
 int64_t assignments(const moe_config_t* c) {
