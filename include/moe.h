@@ -196,7 +196,8 @@ MOE_API moe_status_t moe_pack_weights(const moe_config_t* cfg, const moe_logical
  * selected scores over their sum (or the score when renormalize == 0); times
  * routed_scale.  FP8 experts: xq [T,d] E4M3 codes and xq_scales [T,d/128]
  * (block-scaled activations, one fp32 scale = group max / 448 per 128 values)
- * are written when both are non-NULL. */
+ * are written when both are non-NULL.  ws / ws_bytes: the workspace (the
+ * padded fp32 logits live there); WORKSPACE_TOO_SMALL if it is short. */
 MOE_API moe_status_t moe_route(const moe_config_t* cfg, const void* x, const moe_weights_t* weights,
                        float* logits, int32_t* topk_ids, float* topk_w, void* xq,
                        float* xq_scales, void* ws, size_t ws_bytes, hipStream_t stream);

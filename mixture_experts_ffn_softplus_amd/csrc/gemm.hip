@@ -41,6 +41,9 @@ __device__ __forceinline__ int swz(int row, int ch) { return row * kBlockK + ((c
 
 template <int DT, int BM, int BN, int EPI>
 struct GemmShape {
+  // loads in flight: steps s+1 and s+2 while step s multiplies (one step for FP8, whose wide
+  // accumulators leave no room for a second register stage)
+  static constexpr int PF = DT == MOE_FP8_E4M3 ? 1 : 2;
   static constexpr int WM = BM >= 32 ? 2 : 1;
   static constexpr int WN = 4 / WM;
   static constexpr int TM = BM / WM, TN = BN / WN;
@@ -59,21 +62,23 @@ struct GemmShape {
   static_assert(!(kFp8 && EPI == kEpiSwiglu) || BN == 256, "FP8 h groups need 128 h columns");
 };
 
-template <int DT, int BM, int BN, int EPI>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
+// GROUPED: rows come from the device tile list of an expert-grouped problem (the routed
+// experts); otherwise one group of a.M rows (router, shared experts, combine).
+template <int DT, int BM, int BN, int EPI, bool GROUPED>
+__global__ __launch_bounds__(256, (DT == MOE_FP8_E4M3 ? 1 : 2)) void grouped_gemm_kernel(GemmArgs a) {
   using S = GemmShape<DT, BM, BN, EPI>;
   constexpr int esize = DT_<DT>::esize;
   __shared__ __attribute__((aligned(16))) uint8_t smem[S::SMEM];
 
   // ---------------------------------------------------------------- which tile
   const int NT = a.N / BN;
-  const int ntiles = a.tiles ? a.tiles_count[0] : (a.M + BM - 1) / BM;
+  const int ntiles = GROUPED ? a.tiles_count[0] : (a.M + BM - 1) / BM;
   const int nblocks = ntiles * NT;
   if (static_cast<int>(blockIdx.x) >= nblocks) return;
   const int L = xcd_remap(blockIdx.x, nblocks);
   const int tile = L / NT, nt = L - tile * NT;
   int group = 0, m0, rows;
-  if (a.tiles) {
+  if constexpr (GROUPED) {
     int4 ti = a.tiles[tile];
     group = ti.x;
     m0 = ti.y;
@@ -126,49 +131,49 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
       }
     }
 
-    i32x4 ra[S::A_PER], rb[S::B_PER];
-    float rsc = 0.0f;
-    auto load = [&](int step) {
+    // A rows repeat every a_steps steps when a_steps > 0 (the router's hi + lo weight planes
+    // are one [E, 2d] matrix multiplied by [x, x])
+    const int a_steps = a.a_steps > 0 ? a.a_steps : KB;
+    struct Stage {
+      i32x4 ra[S::A_PER], rb[S::B_PER];
+      float sc;
+    };
+    auto load = [&](int step, Stage& R) {
+      const int as = step < a_steps ? step : step - a_steps;
 #pragma unroll
       for (int i = 0; i < S::A_PER; ++i)
         if (S::A_CHUNKS % 256 == 0 || tid + 256 * i < S::A_CHUNKS)
-          ra[i] = *reinterpret_cast<const i32x4*>(a_ptr[i] + step * kBlockK);
+          R.ra[i] = *reinterpret_cast<const i32x4*>(a_ptr[i] + as * kBlockK);
 #pragma unroll
       for (int i = 0; i < S::B_PER; ++i)
         if (S::B_CHUNKS % 256 == 0 || tid + 256 * i < S::B_CHUNKS)
-          rb[i] = *reinterpret_cast<const i32x4*>(b_ptr[i] + step * kBlockK);
+          R.rb[i] = *reinterpret_cast<const i32x4*>(b_ptr[i] + step * kBlockK);
       if constexpr (S::kFp8) {
-        if (as_ptr) rsc = as_ptr[step];
-        else if (bs_ptr) rsc = bs_ptr[step];
+        if (as_ptr) R.sc = as_ptr[step];
+        else if (bs_ptr) R.sc = bs_ptr[step];
       }
     };
-    auto store = [&](int buf) {
+    auto store = [&](int buf, const Stage& R) {
       uint8_t* sa = smem + buf * S::STAGE;
       uint8_t* sb = sa + BM * kBlockK;
 #pragma unroll
       for (int i = 0; i < S::A_PER; ++i) {
         int c = tid + 256 * i;
         if (S::A_CHUNKS % 256 == 0 || c < S::A_CHUNKS)
-          *reinterpret_cast<i32x4*>(sa + swz(c >> 3, c & 7)) = ra[i];
+          *reinterpret_cast<i32x4*>(sa + swz(c >> 3, c & 7)) = R.ra[i];
       }
 #pragma unroll
       for (int i = 0; i < S::B_PER; ++i) {
         int c = tid + 256 * i;
         if (S::B_CHUNKS % 256 == 0 || c < S::B_CHUNKS)
-          *reinterpret_cast<i32x4*>(sb + swz(c >> 3, c & 7)) = rb[i];
+          *reinterpret_cast<i32x4*>(sb + swz(c >> 3, c & 7)) = R.rb[i];
       }
       if constexpr (S::kFp8) {
         float* ss = reinterpret_cast<float*>(smem + 2 * S::STAGE + buf * S::SCALE_STAGE);
-        if (tid < BM + BN / 16) ss[tid] = rsc;
+        if (tid < BM + BN / 16) ss[tid] = R.sc;
       }
     };
-
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int step = 0; step < KB; ++step) {
-      const int buf = step & 1;
-      if (step + 1 < KB) load(step + 1);
+    auto compute = [&](int buf) {
       const uint8_t* sa = smem + buf * S::STAGE;
       const uint8_t* sb = sa + BM * kBlockK;
       if constexpr (DT == MOE_BF16) {
@@ -206,6 +211,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
               for (int j = 0; j < S::FN; ++j) acc[i][j] = mfma_f32(af[i][e], bf[j][e], acc[i][j]);
         }
       } else {
+        // one E4M3 MFMA covers exactly one 128-deep scale block; its fp32 partial is promoted
+        // with the row's activation scale times the block's weight scale
         const float* ss = reinterpret_cast<const float*>(smem + 2 * S::STAGE + buf * S::SCALE_STAGE);
         i32x8 af[S::FM];
         float sav[S::FM][4];
@@ -233,8 +240,37 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
           }
         }
       }
-      if (step + 1 < KB) store(buf ^ 1);
+    };
+
+    if constexpr (S::PF == 2) {
+      // Registers R0 / R1 alternate: while step s multiplies out of LDS, the loads of steps
+      // s+1 and s+2 are in flight; step s+1 is written to the other LDS buffer afterwards.
+      Stage R0, R1;
+      load(0, R0);
+      if (KB > 1) load(1, R1);
+      store(0, R0);
       __syncthreads();
+      auto iter = [&](int step, Stage& Rfree, Stage& Rnext) {
+        if (step + 2 < KB) load(step + 2, Rfree);
+        compute(step & 1);
+        if (step + 1 < KB) store((step + 1) & 1, Rnext);
+        __syncthreads();
+      };
+      for (int step = 0; step < KB; step += 2) {
+        iter(step, R0, R1);
+        if (step + 1 < KB) iter(step + 1, R1, R0);
+      }
+    } else {
+      Stage R;
+      load(0, R);
+      store(0, R);
+      __syncthreads();
+      for (int step = 0; step < KB; ++step) {
+        if (step + 1 < KB) load(step + 1, R);
+        compute(step & 1);
+        if (step + 1 < KB) store((step + 1) & 1, R);
+        __syncthreads();
+      }
     }
   }
 
@@ -311,30 +347,54 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
       float v[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) v[q] = sO[r * OS + cc + q];
+      if constexpr (EPI == kEpiStore) {
+        if (a.col_bias) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[q] += n0 + cc + q < a.bias_cols ? a.col_bias[n0 + cc + q] : 0.0f;
+        }
+      }
       if constexpr (EPI == kEpiCombine) {
+        // the token's k rows of y_perm, weighted; four rows' loads are issued together
         const int t = m0 + r;
         const uint8_t* y = static_cast<const uint8_t*>(a.y);
-        for (int j = 0; j < a.top_k; ++j) {
-          const int64_t idx = static_cast<int64_t>(t) * a.top_k + j;
-          const float w = a.topk_w[idx];
-          const uint8_t* yr = y + static_cast<int64_t>(a.inv_perm[idx]) * a.ldy +
-                              static_cast<int64_t>(n0 + cc) * ysz;
+        const int64_t base = static_cast<int64_t>(t) * a.top_k;
+        for (int j0 = 0; j0 < a.top_k; j0 += 4) {
+          const int nj = min(4, a.top_k - j0);
+          float wj[4];
+          const uint8_t* yr[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int64_t idx = base + j0 + (u < nj ? u : 0);
+            wj[u] = u < nj ? a.topk_w[idx] : 0.0f;
+            yr[u] = y + static_cast<int64_t>(a.inv_perm[idx]) * a.ldy +
+                    static_cast<int64_t>(n0 + cc) * ysz;
+          }
           if constexpr (y_f32) {
-            f32x4 y0 = *reinterpret_cast<const f32x4*>(yr);
-            f32x4 y1 = *reinterpret_cast<const f32x4*>(yr + 16);
+            f32x4 y0[4], y1[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              v[q] = fmaf(w, y0[q], v[q]);
-              v[4 + q] = fmaf(w, y1[q], v[4 + q]);
+            for (int u = 0; u < 4; ++u) {
+              y0[u] = *reinterpret_cast<const f32x4*>(yr[u]);
+              y1[u] = *reinterpret_cast<const f32x4*>(yr[u] + 16);
             }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                v[q] = fmaf(wj[u], y0[u][q], v[q]);
+                v[4 + q] = fmaf(wj[u], y1[u][q], v[4 + q]);
+              }
           } else {
-            i32x4 yv = *reinterpret_cast<const i32x4*>(yr);
+            i32x4 yv[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              uint32_t u = static_cast<uint32_t>(yv[q]);
-              v[2 * q] = fmaf(w, __uint_as_float(u << 16), v[2 * q]);
-              v[2 * q + 1] = fmaf(w, __uint_as_float(u & 0xFFFF0000u), v[2 * q + 1]);
-            }
+            for (int u = 0; u < 4; ++u) yv[u] = *reinterpret_cast<const i32x4*>(yr[u]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                uint32_t bits = static_cast<uint32_t>(yv[u][q]);
+                v[2 * q] = fmaf(wj[u], __uint_as_float(bits << 16), v[2 * q]);
+                v[2 * q + 1] = fmaf(wj[u], __uint_as_float(bits & 0xFFFF0000u), v[2 * q + 1]);
+              }
           }
         }
       }
@@ -366,45 +426,50 @@ int gemm_bm(int dtype, int epi, int avg_rows) {
 
 int gemm_bn(int dtype, int epi) { return (dtype == MOE_FP8_E4M3 && epi == kEpiSwiglu) ? 256 : 128; }
 
-template <int DT, int BM, int BN, int EPI>
+template <int DT, int BM, int BN, int EPI, bool G>
 static hipError_t launch_one(const GemmArgs& a, int max_tiles, hipStream_t s) {
+  // grouped: worst-case tile count from the caller; one group: exact, for this BM
+  if (!G) max_tiles = (a.M + BM - 1) / BM;
   int nb = max_tiles * (a.N / BN);
   if (nb <= 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_kernel<DT, BM, BN, EPI>), dim3(nb), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((grouped_gemm_kernel<DT, BM, BN, EPI, G>), dim3(nb), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <int DT, int EPI>
+template <int DT, int EPI, bool G>
 static hipError_t launch_dt(int bm, const GemmArgs& a, int max_tiles, hipStream_t s) {
   if constexpr (DT == MOE_F32) {
-    return launch_one<DT, 32, 128, EPI>(a, max_tiles, s);
+    return launch_one<DT, 32, 128, EPI, G>(a, max_tiles, s);
   } else if constexpr (DT == MOE_FP8_E4M3) {
-    return launch_one<DT, 128, (EPI == kEpiSwiglu ? 256 : 128), EPI>(a, max_tiles, s);
+    return launch_one<DT, 128, (EPI == kEpiSwiglu ? 256 : 128), EPI, G>(a, max_tiles, s);
   } else {
     switch (bm) {
-      case 16: return launch_one<DT, 16, 128, EPI>(a, max_tiles, s);
-      case 32: return launch_one<DT, 32, 128, EPI>(a, max_tiles, s);
-      case 64: return launch_one<DT, 64, 128, EPI>(a, max_tiles, s);
-      default: return launch_one<DT, 128, 128, EPI>(a, max_tiles, s);
+      case 16: return launch_one<DT, 16, 128, EPI, G>(a, max_tiles, s);
+      case 32: return launch_one<DT, 32, 128, EPI, G>(a, max_tiles, s);
+      case 64: return launch_one<DT, 64, 128, EPI, G>(a, max_tiles, s);
+      default: return launch_one<DT, 128, 128, EPI, G>(a, max_tiles, s);
     }
   }
+}
+
+template <int DT>
+static hipError_t launch_epi(int epi, int bm, const GemmArgs& a, int max_tiles, hipStream_t s) {
+  const bool g = a.tiles != nullptr;
+  if (epi == kEpiSwiglu)
+    return g ? launch_dt<DT, kEpiSwiglu, true>(bm, a, max_tiles, s)
+             : launch_dt<DT, kEpiSwiglu, false>(bm, a, max_tiles, s);
+  if (epi == kEpiStore)
+    return g ? launch_dt<DT, kEpiStore, true>(bm, a, max_tiles, s)
+             : launch_dt<DT, kEpiStore, false>(bm, a, max_tiles, s);
+  return launch_dt<DT, kEpiCombine, false>(bm, a, max_tiles, s);
 }
 
 hipError_t launch_grouped_gemm(int dtype, int epi, int bm, bool /*out_f32*/, const GemmArgs& a,
                                int max_tiles, hipStream_t s) {
   switch (dtype) {
-    case MOE_F32:
-      if (epi == kEpiSwiglu) return launch_dt<MOE_F32, kEpiSwiglu>(bm, a, max_tiles, s);
-      if (epi == kEpiStore) return launch_dt<MOE_F32, kEpiStore>(bm, a, max_tiles, s);
-      return launch_dt<MOE_F32, kEpiCombine>(bm, a, max_tiles, s);
-    case MOE_BF16:
-      if (epi == kEpiSwiglu) return launch_dt<MOE_BF16, kEpiSwiglu>(bm, a, max_tiles, s);
-      if (epi == kEpiStore) return launch_dt<MOE_BF16, kEpiStore>(bm, a, max_tiles, s);
-      return launch_dt<MOE_BF16, kEpiCombine>(bm, a, max_tiles, s);
-    default:
-      if (epi == kEpiSwiglu) return launch_dt<MOE_FP8_E4M3, kEpiSwiglu>(bm, a, max_tiles, s);
-      if (epi == kEpiStore) return launch_dt<MOE_FP8_E4M3, kEpiStore>(bm, a, max_tiles, s);
-      return launch_dt<MOE_FP8_E4M3, kEpiCombine>(bm, a, max_tiles, s);
+    case MOE_F32: return launch_epi<MOE_F32>(epi, bm, a, max_tiles, s);
+    case MOE_BF16: return launch_epi<MOE_BF16>(epi, bm, a, max_tiles, s);
+    default: return launch_epi<MOE_FP8_E4M3>(epi, bm, a, max_tiles, s);
   }
 }
 

@@ -24,7 +24,8 @@ int act_bytes(const moe_config_t* c) { return c->act_dtype == MOE_F32 ? 4 : 2; }
 // (after h and the output) to a budget the output rounding alone half fills.
 int y_bytes(const moe_config_t* c) { return c->expert_dtype == MOE_FP8_E4M3 ? 2 : 4; }
 
-int e_pad(const moe_config_t* c) { return (c->num_experts + 15) / 16 * 16; }
+// Router columns padded to the GEMM's 128-wide N tiles.
+int e_pad(const moe_config_t* c) { return (c->num_experts + 127) / 128 * 128; }
 int64_t assignments(const moe_config_t* c) {
   return static_cast<int64_t>(c->num_tokens) * c->top_k;
 }
@@ -36,6 +37,14 @@ int router_kind(const moe_config_t* c) {
   if (c->router_dtype == MOE_F32 && c->act_dtype == MOE_F32) return kRouterF32;
   if (c->router_dtype == MOE_BF16) return kRouterBF16;
   return kRouterBF16HiLo;
+}
+
+// Row tile of the router GEMM: the largest that still gives every CU a tile.
+int router_bm(const moe_config_t* c) {
+  const int64_t nt = e_pad(c) / 128;
+  for (int bm : {128, 64, 32})
+    if ((c->num_tokens + bm - 1) / bm * nt >= 256) return bm;
+  return 16;
 }
 
 int routed_bm(const moe_config_t* c) {
@@ -80,8 +89,8 @@ moe_status_t check_config(const moe_config_t* c) {
 }
 
 struct WsLayout {
-  size_t ids, w, offsets, perm, inv, hist, tiles, tiles_count, xq, xq_scales, h, h_scales, hs,
-      hs_scales, y, total;
+  size_t logits, ids, w, offsets, perm, inv, hist, tiles, tiles_count, xq, xq_scales, h,
+      h_scales, hs, hs_scales, y, total;
 };
 
 WsLayout ws_layout(const moe_config_t* c) {
@@ -95,12 +104,13 @@ WsLayout ws_layout(const moe_config_t* c) {
     o += align_up(bytes);
     return at;
   };
+  L.logits = take(T * e_pad(c) * 4);
   L.ids = take(A * 4);
   L.w = take(A * 4);
   L.offsets = take((c->num_experts + 1) * 4);
   L.perm = take(A * 4);
   L.inv = take(A * 4);
-  L.hist = take(static_cast<size_t>(permute_num_chunks(c->num_tokens, c->top_k)) *
+  L.hist = take((static_cast<size_t>(permute_num_chunks(c->num_tokens, c->top_k)) + 1) *
                 c->num_experts * 4);
   L.tiles = take(routed_max_tiles(c) * 16);
   L.tiles_count = take(4);
@@ -145,25 +155,46 @@ moe_status_t check_weights(const moe_config_t* c, const moe_weights_t* w, bool r
 
 // ---------------------------------------------------------------- launch sequences
 
-hipError_t do_route(const moe_config_t* c, const void* x, const moe_weights_t* w, float* logits,
-                    int32_t* ids, float* tw, void* xq, float* xq_scales, hipStream_t s) {
+RouteArgs route_args(const moe_config_t* c, const float* select_bias, int32_t* ids, float* tw) {
   RouteArgs a{};
-  a.x = x;
-  a.w = w->w_router;
-  a.logit_bias = w->logit_bias;
-  a.select_bias = w->select_bias;
-  a.logits = logits;
+  a.select_bias = select_bias;
   a.ids = ids;
   a.weights = tw;
   a.T = c->num_tokens;
-  a.d = c->d_model;
   a.E = c->num_experts;
-  a.E_pad = e_pad(c);
   a.k = c->top_k;
   a.score = c->score;
   a.renorm = c->renormalize;
   a.gamma = c->routed_scale;
-  hipError_t e = launch_router_topk(router_kind(c), a, s);
+  return a;
+}
+
+// Router logits on the MFMA GEMM (fp32 out, logit bias in the epilogue) into the workspace,
+// then scoring and top-k; FP8 experts also get their block-scaled activations.
+hipError_t do_route(const moe_config_t* c, const void* x, const moe_weights_t* w, float* logits,
+                    int32_t* ids, float* tw, void* xq, float* xq_scales, void* ws,
+                    hipStream_t s) {
+  const WsLayout L = ws_layout(c);
+  const int kind = router_kind(c);
+  const int64_t d = c->d_model, Ep = e_pad(c);
+  float* lg = at<float>(ws, L.logits);
+  GemmArgs g{};
+  g.A = x;
+  g.lda = d * act_bytes(c);
+  g.B = w->w_router;
+  g.K = static_cast<int>(kind == kRouterBF16HiLo ? 2 * d : d);
+  g.a_steps = kind == kRouterBF16HiLo ? static_cast<int>(d * 2 / kBlockK) : 0;
+  g.N = static_cast<int>(Ep);
+  g.M = c->num_tokens;
+  g.out = lg;
+  g.ldo = Ep * 4;
+  g.col_bias = w->logit_bias;
+  g.bias_cols = c->num_experts;
+  const int bm = router_bm(c);
+  hipError_t e = launch_grouped_gemm(kind == kRouterF32 ? MOE_F32 : MOE_BF16, kEpiStore, bm,
+                                     true, g, (c->num_tokens + bm - 1) / bm, s);
+  if (e != hipSuccess) return e;
+  e = launch_topk(route_args(c, w->select_bias, ids, tw), lg, static_cast<int>(Ep), logits, s);
   if (e != hipSuccess) return e;
   if (is_fp8(c) && xq && xq_scales)
     e = launch_quant_x_fp8(static_cast<const uint16_t*>(x), static_cast<uint8_t*>(xq), xq_scales,
@@ -385,14 +416,13 @@ moe_status_t moe_pack_weights(const moe_config_t* c, const moe_logical_weights_t
 moe_status_t moe_route(const moe_config_t* c, const void* x, const moe_weights_t* w,
                        float* logits, int32_t* ids, float* tw, void* xq, float* xq_scales,
                        void* ws, size_t ws_bytes, hipStream_t s) {
-  (void)ws;
-  (void)ws_bytes;
   moe_status_t st = check_config(c);
   if (st != MOE_OK) return st;
   if (!x || !ids || !tw) return MOE_ERR_INVALID_ARGUMENT;
   if ((st = check_weights(c, w, true, false, false)) != MOE_OK) return st;
+  if ((st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
   if (c->num_tokens == 0) return MOE_OK;
-  return hip_status(do_route(c, x, w, logits, ids, tw, xq, xq_scales, s));
+  return hip_status(do_route(c, x, w, logits, ids, tw, xq, xq_scales, ws, s));
 }
 
 moe_status_t moe_route_from_logits(const moe_config_t* c, const float* logits,
@@ -402,20 +432,8 @@ moe_status_t moe_route_from_logits(const moe_config_t* c, const float* logits,
   if (st != MOE_OK) return st;
   if (!logits || !ids || !tw) return MOE_ERR_INVALID_ARGUMENT;
   if (c->num_tokens == 0) return MOE_OK;
-  RouteArgs a{};
-  a.select_bias = select_bias;
-  a.logits = const_cast<float*>(logits);
-  a.ids = ids;
-  a.weights = tw;
-  a.T = c->num_tokens;
-  a.d = c->d_model;
-  a.E = c->num_experts;
-  a.E_pad = e_pad(c);
-  a.k = c->top_k;
-  a.score = c->score;
-  a.renorm = c->renormalize;
-  a.gamma = c->routed_scale;
-  return hip_status(launch_topk_from_logits(a, s));
+  return hip_status(launch_topk(route_args(c, select_bias, ids, tw), logits, c->num_experts,
+                                nullptr, s));
 }
 
 moe_status_t moe_permute(const moe_config_t* c, const int32_t* ids, int32_t* offsets,
@@ -477,7 +495,7 @@ moe_status_t moe_forward(const moe_config_t* c, const void* x, const moe_weights
   const void* xa = is_fp8(c) ? static_cast<const void*>(xq) : x;
   hipEvent_t* ev = d.stage_events;
   hipError_t e = mark(ev, MOE_STAGE_BEGIN, s);
-  if (e == hipSuccess) e = do_route(c, x, w, d.logits, ids, tw, xq, xs, s);
+  if (e == hipSuccess) e = do_route(c, x, w, d.logits, ids, tw, xq, xs, ws, s);
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_ROUTED, s);
   if (e == hipSuccess)
     e = launch_permute(ids, c->num_tokens, c->top_k, c->num_experts, offsets, perm, inv,

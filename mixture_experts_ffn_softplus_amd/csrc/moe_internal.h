@@ -10,20 +10,17 @@ namespace moe {
 
 // ---- router (route.hip)
 struct RouteArgs {
-  const void* x;             // [T, d] act dtype
-  const void* w;             // packed router [E_pad, d] (or [2, E_pad, d] hi/lo)
-  const float* logit_bias;   // [E] or null
   const float* select_bias;  // [E] or null
-  float* logits;             // [T, E] or null
   int32_t* ids;              // [T, k]
   float* weights;            // [T, k]
-  int T, d, E, E_pad, k;
+  int T, E, k;
   int score, renorm;
   float gamma;
 };
 enum RouterKind { kRouterF32 = 0, kRouterBF16 = 1, kRouterBF16HiLo = 2 };
-hipError_t launch_router_topk(int kind, const RouteArgs& a, hipStream_t s);
-hipError_t launch_topk_from_logits(const RouteArgs& a, hipStream_t s);
+// Scoring + top-k of fp32 logits rows `ld` apart; copy: optional [T, E] copy of the logits.
+hipError_t launch_topk(const RouteArgs& a, const float* logits, int ld, float* copy,
+                       hipStream_t s);
 hipError_t launch_quant_x_fp8(const uint16_t* x, uint8_t* xq, float* scales, int T, int d,
                               hipStream_t s);
 
@@ -64,6 +61,11 @@ struct GemmArgs {
   const int32_t* inv_perm;
   const float* topk_w;
   int top_k;
+  // store epilogue: bias added to output column n < bias_cols (router logit bias)
+  const float* col_bias;
+  int bias_cols;
+  // A rows repeat every a_steps K-steps when > 0 (0: no repeat)
+  int a_steps;
 };
 
 // dtype: MOE_F32 / MOE_BF16 / MOE_FP8_E4M3 (operands); out_f32: output rows fp32.
@@ -84,7 +86,7 @@ hipError_t launch_pack_gate_up(const void* gate, const void* up, void* dst, int 
 hipError_t launch_pack_down(const void* down, void* dst, int N, int C, int sub, int groups,
                             int esize, hipStream_t s);
 // Router [d, E] -> [E_pad, d] (rows >= E zero).  hilo: fp32 source split into bf16 hi and
-// lo = bf16(w - hi) planes [2, E_pad, d]; otherwise the element type is kept.
+// lo = bf16(w - hi), one [E_pad, 2d] bf16 matrix; otherwise the element type is kept.
 hipError_t launch_pack_router(const void* wr, int esize, int hilo, void* dst, int d, int E,
                               int E_pad, hipStream_t s);
 // FP8 block scales, one per 16 packed rows and 128 K values:

@@ -51,6 +51,9 @@ __global__ __launch_bounds__(256) void pack_down_kernel(const T* __restrict__ do
   for (int nn = ty; nn < 64; nn += 4) d[static_cast<size_t>(n0 + nn) * F + f0 + tx] = tile[tx][nn];
 }
 
+// Router [d, E] -> [E_pad, d] K-contiguous, rows >= E zero.  HILO: an fp32 router is split
+// into bf16 hi = bf16(w) and lo = bf16(w - hi), stored side by side as one [E_pad, 2d] bf16
+// matrix that the GEMM multiplies by [x, x].
 template <typename T, bool HILO>
 __global__ __launch_bounds__(256) void pack_router_kernel(const T* __restrict__ wr,
                                                           uint8_t* __restrict__ dst, int d,
@@ -63,8 +66,9 @@ __global__ __launch_bounds__(256) void pack_router_kernel(const T* __restrict__ 
     float w = static_cast<float>(v);
     uint16_t hi = f32_to_bf16(w);
     uint16_t lo = f32_to_bf16(w - bf16_to_f32(hi));
-    reinterpret_cast<uint16_t*>(dst)[i] = hi;
-    reinterpret_cast<uint16_t*>(dst)[static_cast<int64_t>(E_pad) * d + i] = lo;
+    uint16_t* row = reinterpret_cast<uint16_t*>(dst) + static_cast<int64_t>(e) * 2 * d;
+    row[k] = hi;
+    row[d + k] = lo;
   } else {
     reinterpret_cast<T*>(dst)[i] = v;
   }

@@ -2,32 +2,25 @@
 //
 // The pages select routed experts per token ("keep the top 10", router row of
 // "Qwen3.5-397B-A17B vs DeepSeek-V4-Pro"), which the grouped expert GEMMs need as contiguous
-// per-expert row ranges.  A counting sort, deterministic by construction:
-//   1. per-chunk expert histograms (LDS atomics only count; they decide no order),
-//   2. one workgroup scans each expert's counts over the chunks, then over the experts
-//      (expert_offsets), leaving every chunk's base row per expert,
-//   3. one wave per chunk walks its assignments in order, 64 at a time, ranking equal
-//      experts among lower lanes with ballots, and scatters token ids to their rows.
+// per-expert row ranges.  A counting sort, deterministic by construction, over chunks of 256
+// consecutive assignments:
+//   1. per-chunk expert histograms, stored expert-major (LDS atomics only count; they decide
+//      no order),
+//   2. one workgroup per expert scans its counts over the chunks (each chunk's first row
+//      within the expert), then one workgroup scans the expert totals (expert_offsets),
+//   3. per chunk, each of 4 waves ranks its 64 assignments among equal experts in lower lanes
+//      with ballots; the waves' per-expert counts, summed in lane order through LDS, place
+//      every assignment, and token ids are scattered to their rows.
 #include "moe_common.h"
 #include "moe_internal.h"
 
 namespace moe {
 
-constexpr int kMaxChunks = 512;
-
-static int chunk_size(int64_t A) {
-  int64_t chunks = (A + 255) / 256;
-  if (chunks > kMaxChunks) chunks = kMaxChunks;
-  if (chunks < 1) chunks = 1;
-  int64_t cs = (A + chunks - 1) / chunks;
-  cs = (cs + 63) / 64 * 64;
-  return static_cast<int>(cs < 64 ? 64 : cs);
-}
+constexpr int kChunk = 256;  // assignments per chunk = 4 waves x 64 lanes
 
 int permute_num_chunks(int T, int k) {
   int64_t A = static_cast<int64_t>(T) * k;
-  int cs = chunk_size(A);
-  return static_cast<int>((A + cs - 1) / cs);
+  return static_cast<int>((A + kChunk - 1) / kChunk);
 }
 
 // Exclusive scan of one value per thread over a block of up to 1024 threads.
@@ -59,77 +52,88 @@ __device__ int block_exclusive_scan(int v, int* s_tot, int* total) {
   return r;
 }
 
+// hist[e][c]: assignments of chunk c routed to expert e.
 __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ ids, int64_t A,
-                                                   int cs, int E, int32_t* __restrict__ hist) {
+                                                   int chunks, int E, int32_t* __restrict__ hist) {
   extern __shared__ int s_hist[];
   for (int e = threadIdx.x; e < E; e += blockDim.x) s_hist[e] = 0;
   __syncthreads();
-  const int64_t a0 = static_cast<int64_t>(blockIdx.x) * cs;
-  const int64_t a1 = min(a0 + cs, A);
-  for (int64_t a = a0 + threadIdx.x; a < a1; a += blockDim.x) atomicAdd(&s_hist[ids[a]], 1);
+  const int64_t a = static_cast<int64_t>(blockIdx.x) * kChunk + threadIdx.x;
+  if (a < A) atomicAdd(&s_hist[ids[a]], 1);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x)
-    hist[static_cast<size_t>(blockIdx.x) * E + e] = s_hist[e];
+    hist[static_cast<size_t>(e) * chunks + blockIdx.x] = s_hist[e];
 }
 
-// hist[c][e] (counts) -> hist[c][e] = first row of chunk c's assignments to expert e.
-__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ hist, int chunks,
-                                                    int E, int64_t A,
-                                                    int32_t* __restrict__ offsets) {
+// One workgroup per expert: hist[e][c] -> first row of chunk c within expert e's rows;
+// counts[e] = expert e's total.
+__global__ __launch_bounds__(256) void scan_chunks_kernel(int32_t* __restrict__ hist, int chunks,
+                                                          int32_t* __restrict__ counts) {
+  __shared__ int s_tot[kWave + 1];
+  int32_t* h = hist + static_cast<size_t>(blockIdx.x) * chunks;
+  const int per = (chunks + blockDim.x - 1) / blockDim.x;
+  const int c0 = threadIdx.x * per, c1 = min(c0 + per, chunks);
+  int sum = 0;
+  for (int c = c0; c < c1; ++c) sum += h[c];
+  int total;
+  int run = block_exclusive_scan(sum, s_tot, &total);
+  for (int c = c0; c < c1; ++c) {
+    int v = h[c];
+    h[c] = run;
+    run += v;
+  }
+  if (threadIdx.x == 0) counts[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(1024) void offsets_kernel(const int32_t* __restrict__ counts, int E,
+                                                       int64_t A, int32_t* __restrict__ offsets) {
   __shared__ int s_tot[kWave + 1];
   const int e = threadIdx.x;
-  int count = 0;
-  if (e < E) {
-    for (int c = 0; c < chunks; ++c) {
-      int v = hist[static_cast<size_t>(c) * E + e];
-      hist[static_cast<size_t>(c) * E + e] = count;
-      count += v;
-    }
-  }
   int total;
-  int off = block_exclusive_scan(e < E ? count : 0, s_tot, &total);
-  if (e < E) {
-    offsets[e] = off;
-    for (int c = 0; c < chunks; ++c) hist[static_cast<size_t>(c) * E + e] += off;
-  }
+  int off = block_exclusive_scan(e < E ? counts[e] : 0, s_tot, &total);
+  if (e < E) offsets[e] = off;
   if (e == 0) offsets[E] = static_cast<int32_t>(A);
 }
 
-__global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ ids, int64_t A,
-                                                     int cs, int k, int E,
-                                                     const int32_t* __restrict__ base,
-                                                     int32_t* __restrict__ perm_token,
-                                                     int32_t* __restrict__ inv_perm) {
-  extern __shared__ int s_base[];
-  for (int e = threadIdx.x; e < E; e += kWave)
-    s_base[e] = base[static_cast<size_t>(blockIdx.x) * E + e];
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ ids, int64_t A,
+                                                      int k, int E, int chunks,
+                                                      const int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ hist,
+                                                      int32_t* __restrict__ perm_token,
+                                                      int32_t* __restrict__ inv_perm) {
+  extern __shared__ int sm[];
+  int* s_base = sm;          // [E] first row of this chunk's assignments to each expert
+  int* s_cnt = sm + E;       // [4][E] per-wave counts
+  const int c = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    s_base[e] = offsets[e] + hist[static_cast<size_t>(e) * chunks + c];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) s_cnt[w * E + e] = 0;
+  }
   __syncthreads();
-  const int l = lane_id();
+  const int l = lane_id(), wv = threadIdx.x / kWave;
   const uint64_t lt_mask = (l == 0) ? 0ull : (~0ull >> (kWave - l));
-  const int64_t a0 = static_cast<int64_t>(blockIdx.x) * cs;
-  const int64_t a1 = min(a0 + cs, A);
-  for (int64_t s = a0; s < a1; s += kWave) {
-    const int64_t a = s + l;
-    const bool valid = a < a1;
-    const int e = valid ? ids[a] : -1;
-    uint64_t remaining = __ballot(valid);
-    uint64_t peers = 0;
-    while (remaining) {
-      int leader = __ffsll(static_cast<unsigned long long>(remaining)) - 1;
-      int le = __shfl(e, leader, kWave);
-      uint64_t m = __ballot(valid && e == le);
-      if (valid && e == le) peers = m;
-      remaining &= ~m;
-    }
-    if (valid) {
-      int rank = __popcll(peers & lt_mask);
-      int cnt = __popcll(peers);
-      int pos = s_base[e] + rank;
-      perm_token[pos] = static_cast<int32_t>(a / k);
-      inv_perm[a] = pos;
-      if (rank == cnt - 1) s_base[e] += cnt;
-    }
-    __syncthreads();
+  const int64_t a = static_cast<int64_t>(c) * kChunk + threadIdx.x;
+  const bool valid = a < A;
+  const int e = valid ? ids[a] : -1;
+  uint64_t remaining = __ballot(valid);
+  uint64_t peers = 0;
+  while (remaining) {
+    int leader = __ffsll(static_cast<unsigned long long>(remaining)) - 1;
+    int le = __shfl(e, leader, kWave);
+    uint64_t m = __ballot(valid && e == le);
+    if (valid && e == le) peers = m;
+    remaining &= ~m;
+  }
+  const int rank = __popcll(peers & lt_mask);
+  const int cnt = __popcll(peers);
+  if (valid && rank == cnt - 1) s_cnt[wv * E + e] = cnt;
+  __syncthreads();
+  if (valid) {
+    int pos = s_base[e] + rank;
+    for (int w = 0; w < wv; ++w) pos += s_cnt[w * E + e];
+    perm_token[pos] = static_cast<int32_t>(a / k);
+    inv_perm[a] = pos;
   }
 }
 
@@ -168,6 +172,7 @@ __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
   if (i < n) p[i] = v;
 }
 
+// hist: workspace of (chunks + 1) * E ints (histograms, then the per-expert totals).
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
                           int32_t* perm_token, int32_t* inv_perm, int32_t* hist,
                           hipStream_t s) {
@@ -177,13 +182,14 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offs
                        E + 1, 0);
     return hipGetLastError();
   }
-  const int cs = chunk_size(A);
-  const int chunks = static_cast<int>((A + cs - 1) / cs);
-  hipLaunchKernelGGL(hist_kernel, dim3(chunks), dim3(256), sizeof(int) * E, s, ids, A, cs, E,
-                     hist);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, hist, chunks, E, A, offsets);
-  hipLaunchKernelGGL(scatter_kernel, dim3(chunks), dim3(64), sizeof(int) * E, s, ids, A, cs, k,
-                     E, hist, perm_token, inv_perm);
+  const int chunks = static_cast<int>((A + kChunk - 1) / kChunk);
+  int32_t* counts = hist + static_cast<size_t>(chunks) * E;
+  hipLaunchKernelGGL(hist_kernel, dim3(chunks), dim3(kChunk), sizeof(int) * E, s, ids, A, chunks,
+                     E, hist);
+  hipLaunchKernelGGL(scan_chunks_kernel, dim3(E), dim3(256), 0, s, hist, chunks, counts);
+  hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(1024), 0, s, counts, E, A, offsets);
+  hipLaunchKernelGGL(scatter_kernel, dim3(chunks), dim3(kChunk), sizeof(int) * 5 * E, s, ids, A,
+                     k, E, chunks, offsets, hist, perm_token, inv_perm);
   return hipGetLastError();
 }
 

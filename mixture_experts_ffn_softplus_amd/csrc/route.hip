@@ -1,4 +1,4 @@
-// route.hip -- router GEMM fused with scoring and top-k, plus the FP8 activation quantiser.
+// route.hip -- router scoring and top-k, and the FP8 activation quantiser.
 //
 // The router of the archdiff.com pages ("Qwen3.5-397B-A17B vs DeepSeek-V4-Pro", component
 // table, router row): a linear map of the token to one logit per expert; then either a
@@ -7,11 +7,9 @@
 // choosing the top k, the chosen unbiased scores normalised and scaled by 2.5 (DeepSeek-V4-Pro
 // cell).  Ties at equal keys go to the lower expert index.
 //
-// One workgroup (4 waves) owns 16 tokens and all E_pad experts: the 16 x E_pad logit tile is
-// accumulated on MFMA (each wave a quarter of the 16-expert column blocks, operands streamed
-// straight from global memory: x rows are shared through L1, every router column is read by
-// exactly one wave), parked in LDS, then each wave selects the top k of four tokens with k
-// rounds of a 64-lane argmax.
+// The logits come from the grouped MFMA GEMM (one group, fp32 out, logit bias added in its
+// epilogue).  Here one wave owns one token: each lane scores E/64 experts held in registers,
+// then k rounds of a 64-lane argmax pick the experts in key order.
 #include <math.h>
 
 #include "moe_common.h"
@@ -19,8 +17,6 @@
 
 namespace moe {
 
-constexpr int kRouterRows = 16;       // tokens per workgroup
-constexpr int kMaxColBlocks = 16;     // 16-expert blocks per wave: E_pad <= 1024
 constexpr int kMaxPerLane = 16;       // experts per lane in top-k: E <= 1024
 
 // Score of the sigma family, evaluated in fp64 and rounded once to fp32, so the
@@ -115,83 +111,16 @@ __device__ void topk_row(const float* row, int t, const RouteArgs& a) {
   }
 }
 
-template <int KIND>
-__global__ __launch_bounds__(256) void router_topk_kernel(RouteArgs a) {
-  extern __shared__ float sL[];
-  const int LS = a.E_pad + 4;
-  const int wv = threadIdx.x / kWave, l = lane_id();
-  const int t0 = blockIdx.x * kRouterRows;
-  const int nb = a.E_pad / 16;
-  const int row = min(t0 + (l & 15), a.T - 1);
-  const int kq = l >> 4;  // K-slice of this lane
-
-  f32x4 acc[kMaxColBlocks];
-#pragma unroll
-  for (int i = 0; i < kMaxColBlocks; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if constexpr (KIND == kRouterF32) {
-    const float* xr = static_cast<const float*>(a.x) + static_cast<size_t>(row) * a.d + 4 * kq;
-    const float* wb = static_cast<const float*>(a.w) + 4 * kq;
-    for (int k0 = 0; k0 < a.d; k0 += 16) {
-      f32x4 av = *reinterpret_cast<const f32x4*>(xr + k0);
-#pragma unroll
-      for (int i = 0; i < kMaxColBlocks; ++i) {
-        int b = wv + 4 * i;
-        if (b < nb) {
-          f32x4 bv = *reinterpret_cast<const f32x4*>(
-              wb + static_cast<size_t>(b * 16 + (l & 15)) * a.d + k0);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i] = mfma_f32(av[j], bv[j], acc[i]);
-        }
-      }
-    }
-  } else {
-    const uint16_t* xr =
-        static_cast<const uint16_t*>(a.x) + static_cast<size_t>(row) * a.d + 8 * kq;
-    const uint16_t* wb = static_cast<const uint16_t*>(a.w) + 8 * kq;
-    const size_t lo_off = static_cast<size_t>(a.E_pad) * a.d;
-#pragma unroll 2
-    for (int k0 = 0; k0 < a.d; k0 += 32) {
-      bf16x8 av = *reinterpret_cast<const bf16x8*>(xr + k0);
-#pragma unroll
-      for (int i = 0; i < kMaxColBlocks; ++i) {
-        int b = wv + 4 * i;
-        if (b < nb) {
-          const uint16_t* p = wb + static_cast<size_t>(b * 16 + (l & 15)) * a.d + k0;
-          acc[i] = mfma_bf16(av, *reinterpret_cast<const bf16x8*>(p), acc[i]);
-          if constexpr (KIND == kRouterBF16HiLo)
-            acc[i] = mfma_bf16(av, *reinterpret_cast<const bf16x8*>(p + lo_off), acc[i]);
-        }
-      }
-    }
-  }
-
-#pragma unroll
-  for (int i = 0; i < kMaxColBlocks; ++i) {
-    int b = wv + 4 * i;
-    if (b < nb) {
-      int col = b * 16 + (l & 15);
-      float z = (a.logit_bias && col < a.E) ? a.logit_bias[col] : 0.0f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sL[(4 * kq + j) * LS + col] = acc[i][j] + z;
-    }
-  }
-  __syncthreads();
-
-  const int rows = min(kRouterRows, a.T - t0);
-  if (a.logits) {
-    for (int idx = threadIdx.x; idx < rows * a.E; idx += blockDim.x) {
-      int r = idx / a.E, c = idx - r * a.E;
-      a.logits[static_cast<size_t>(t0 + r) * a.E + c] = sL[r * LS + c];
-    }
-  }
-  for (int r = wv; r < rows; r += 4) topk_row(sL + r * LS, t0 + r, a);
-}
-
-__global__ __launch_bounds__(256) void topk_from_logits_kernel(RouteArgs a) {
+// One wave per token.  `logits` rows are `ld` floats apart; when `copy` is non-null the E
+// valid logits of each row are also written there as [T, E].
+__global__ __launch_bounds__(256) void topk_kernel(RouteArgs a, const float* __restrict__ logits,
+                                                   int ld, float* __restrict__ copy) {
   int t = blockIdx.x * 4 + threadIdx.x / kWave;
   if (t >= a.T) return;  // whole waves leave together
-  topk_row(a.logits + static_cast<size_t>(t) * a.E, t, a);
+  const float* row = logits + static_cast<size_t>(t) * ld;
+  if (copy)
+    for (int e = lane_id(); e < a.E; e += kWave) copy[static_cast<size_t>(t) * a.E + e] = row[e];
+  topk_row(row, t, a);
 }
 
 // Block-scaled FP8 activations: one fp32 scale = max|x| / 448 (1 for an all-zero group)
@@ -234,27 +163,10 @@ __global__ __launch_bounds__(256) void quant_x_fp8_kernel(const uint16_t* __rest
   }
 }
 
-hipError_t launch_router_topk(int kind, const RouteArgs& a, hipStream_t s) {
+hipError_t launch_topk(const RouteArgs& a, const float* logits, int ld, float* copy,
+                       hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  dim3 grid((a.T + kRouterRows - 1) / kRouterRows);
-  size_t lds = sizeof(float) * kRouterRows * (a.E_pad + 4);
-  switch (kind) {
-    case kRouterF32:
-      hipLaunchKernelGGL(router_topk_kernel<kRouterF32>, grid, dim3(256), lds, s, a);
-      break;
-    case kRouterBF16:
-      hipLaunchKernelGGL(router_topk_kernel<kRouterBF16>, grid, dim3(256), lds, s, a);
-      break;
-    default:
-      hipLaunchKernelGGL(router_topk_kernel<kRouterBF16HiLo>, grid, dim3(256), lds, s, a);
-      break;
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_topk_from_logits(const RouteArgs& a, hipStream_t s) {
-  if (a.T == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_from_logits_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a, logits, ld, copy);
   return hipGetLastError();
 }
 
