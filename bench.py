@@ -151,6 +151,9 @@ def main():
     ap.add_argument("--workload", default="softmax_bf16")
     ap.add_argument("--cpu-tokens", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (3 times): the reference for "
+                         "scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs the block on one GPU; --gpus {args.gpus} is not "
@@ -161,6 +164,16 @@ def main():
     import torch
 
     from mixture_experts_ffn_softplus_amd import PRESETS, api, synth
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {n} bytes 3 times")
+        return
 
     cfg = PRESETS[args.workload]
     dev = torch.device("cuda:0")

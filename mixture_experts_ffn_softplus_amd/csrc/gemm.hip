@@ -12,7 +12,8 @@
 //                  (shared-expert row of the same page: the shared output is added to the
 //                  routed sum).
 //
-// Structure.  256 threads (4 waves) per workgroup, a BM x BN output tile, K consumed 128 bytes
+// Structure.  4 or 8 waves per workgroup (each wave a 64 x 64 or smaller sub-tile), a BM x BN
+// output tile, K consumed 128 bytes
 // per step (64 bf16, 32 fp32 or 128 E4M3 values -- exactly one FP8 scale block).  Each step's
 // A rows (gathered through a_map: no permuted copy of x is ever written) and B rows are
 // fetched with 16-byte loads into registers while the MFMAs of the previous step run, then
@@ -39,18 +40,24 @@ struct DT_<MOE_FP8_E4M3> { static constexpr int esize = 1; };
 
 __device__ __forceinline__ int swz(int row, int ch) { return row * kBlockK + ((ch ^ (row & 7)) << 4); }
 
+// NW waves per workgroup: 8 for the wide bf16 tiles (BN = 256, each wave still 64 x 64), else 4.
+template <int DT, int BN>
+constexpr int gemm_waves() { return (DT == MOE_BF16 && BN >= 256) ? 8 : 4; }
+
 template <int DT, int BM, int BN, int EPI>
 struct GemmShape {
-  // loads in flight: steps s+1 and s+2 while step s multiplies (one step for FP8, whose wide
+  static constexpr int NW = gemm_waves<DT, BN>();
+  static constexpr int NT = NW * kWave;
+  // loads in flight while step s multiplies: steps s+1 and s+2 (one step for FP8, whose wide
   // accumulators leave no room for a second register stage)
   static constexpr int PF = DT == MOE_FP8_E4M3 ? 1 : 2;
   static constexpr int WM = BM >= 32 ? 2 : 1;
-  static constexpr int WN = 4 / WM;
+  static constexpr int WN = NW / WM;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 16, FN = TN / 16;
   static constexpr bool kFp8 = DT == MOE_FP8_E4M3;
   static constexpr int A_CHUNKS = BM * 8, B_CHUNKS = BN * 8;  // 16-byte chunks per step
-  static constexpr int A_PER = (A_CHUNKS + 255) / 256, B_PER = (B_CHUNKS + 255) / 256;
+  static constexpr int A_PER = (A_CHUNKS + NT - 1) / NT, B_PER = (B_CHUNKS + NT - 1) / NT;
   static constexpr int STAGE = (BM + BN) * kBlockK;
   static constexpr int SCALE_STAGE = kFp8 ? (BM + BN / 16) * 4 : 0;
   static constexpr int MAIN = 2 * STAGE + 2 * SCALE_STAGE;
@@ -65,7 +72,8 @@ struct GemmShape {
 // GROUPED: rows come from the device tile list of an expert-grouped problem (the routed
 // experts); otherwise one group of a.M rows (router, shared experts, combine).
 template <int DT, int BM, int BN, int EPI, bool GROUPED>
-__global__ __launch_bounds__(256, (DT == MOE_FP8_E4M3 ? 1 : 2)) void grouped_gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__((gemm_waves<DT, BN>() * kWave), (DT == MOE_FP8_E4M3 ? 1 : 2))
+void grouped_gemm_kernel(GemmArgs a) {
   using S = GemmShape<DT, BM, BN, EPI>;
   constexpr int esize = DT_<DT>::esize;
   __shared__ __attribute__((aligned(16))) uint8_t smem[S::SMEM];
@@ -102,24 +110,34 @@ __global__ __launch_bounds__(256, (DT == MOE_FP8_E4M3 ? 1 : 2)) void grouped_gem
     for (int j = 0; j < S::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (KB > 0) {
-    // ------------------------------------------------------------ per-thread load addresses
-    const uint8_t* a_ptr[S::A_PER];
-    const uint8_t* b_ptr[S::B_PER];
-    const float* as_ptr = nullptr;
-    const float* bs_ptr = nullptr;
+    // ------------------------------------------------------------ per-thread load offsets
+    // A rows (gathered through a_map) and B rows are read with buffer loads: one 32-bit lane
+    // offset each, advanced by a wave-uniform step offset.
+    const __amdgpu_buffer_rsrc_t a_rs = buffer_rsrc(a.A, static_cast<uint32_t>(a.a_bytes));
+    const uint8_t* bg = static_cast<const uint8_t*>(a.B) + group * a.b_group_stride;
+    const __amdgpu_buffer_rsrc_t b_rs =
+        buffer_rsrc(bg, static_cast<uint32_t>(static_cast<int64_t>(a.N) * ldb));
+    uint32_t a_off[S::A_PER], b_off[S::B_PER];
 #pragma unroll
     for (int i = 0; i < S::A_PER; ++i) {
-      int c = tid + 256 * i;
-      int r = min(c >> 3, rows - 1);  // rows past the group's end re-read a valid row
-      int arow = a.a_map ? a.a_map[m0 + r] : m0 + r;
-      a_ptr[i] = static_cast<const uint8_t*>(a.A) + static_cast<int64_t>(arow) * a.lda + (c & 7) * 16;
+      int c = tid + S::NT * i;
+      int r = c >> 3;
+      // rows past the tile's end get an offset beyond the buffer: the load returns zeros
+      // without a memory request (their outputs are never stored)
+      if (r < rows) {
+        int arow = a.a_map ? a.a_map[m0 + r] : m0 + r;
+        a_off[i] = static_cast<uint32_t>(static_cast<int64_t>(arow) * a.lda + (c & 7) * 16);
+      } else {
+        a_off[i] = 0x80000000u;
+      }
     }
-    const uint8_t* bg = static_cast<const uint8_t*>(a.B) + group * a.b_group_stride;
 #pragma unroll
     for (int i = 0; i < S::B_PER; ++i) {
-      int c = tid + 256 * i;
-      b_ptr[i] = bg + static_cast<int64_t>(n0 + (c >> 3)) * ldb + (c & 7) * 16;
+      int c = tid + S::NT * i;
+      b_off[i] = static_cast<uint32_t>(static_cast<int64_t>(n0 + (c >> 3)) * ldb + (c & 7) * 16);
     }
+    const float* as_ptr = nullptr;
+    const float* bs_ptr = nullptr;
     if constexpr (S::kFp8) {
       if (tid < BM) {
         int r = min(tid, rows - 1);
@@ -139,15 +157,16 @@ __global__ __launch_bounds__(256, (DT == MOE_FP8_E4M3 ? 1 : 2)) void grouped_gem
       float sc;
     };
     auto load = [&](int step, Stage& R) {
-      const int as = step < a_steps ? step : step - a_steps;
+      const uint32_t as = static_cast<uint32_t>(step < a_steps ? step : step - a_steps) * kBlockK;
+      const uint32_t bs = static_cast<uint32_t>(step) * kBlockK;
 #pragma unroll
       for (int i = 0; i < S::A_PER; ++i)
-        if (S::A_CHUNKS % 256 == 0 || tid + 256 * i < S::A_CHUNKS)
-          R.ra[i] = *reinterpret_cast<const i32x4*>(a_ptr[i] + as * kBlockK);
+        if (S::A_CHUNKS % S::NT == 0 || tid + S::NT * i < S::A_CHUNKS)
+          R.ra[i] = buffer_load16(a_rs, a_off[i], as);
 #pragma unroll
       for (int i = 0; i < S::B_PER; ++i)
-        if (S::B_CHUNKS % 256 == 0 || tid + 256 * i < S::B_CHUNKS)
-          R.rb[i] = *reinterpret_cast<const i32x4*>(b_ptr[i] + step * kBlockK);
+        if (S::B_CHUNKS % S::NT == 0 || tid + S::NT * i < S::B_CHUNKS)
+          R.rb[i] = buffer_load16<kNonTemporal>(b_rs, b_off[i], bs);  // weights: streamed
       if constexpr (S::kFp8) {
         if (as_ptr) R.sc = as_ptr[step];
         else if (bs_ptr) R.sc = bs_ptr[step];
@@ -158,14 +177,14 @@ __global__ __launch_bounds__(256, (DT == MOE_FP8_E4M3 ? 1 : 2)) void grouped_gem
       uint8_t* sb = sa + BM * kBlockK;
 #pragma unroll
       for (int i = 0; i < S::A_PER; ++i) {
-        int c = tid + 256 * i;
-        if (S::A_CHUNKS % 256 == 0 || c < S::A_CHUNKS)
+        int c = tid + S::NT * i;
+        if (S::A_CHUNKS % S::NT == 0 || c < S::A_CHUNKS)
           *reinterpret_cast<i32x4*>(sa + swz(c >> 3, c & 7)) = R.ra[i];
       }
 #pragma unroll
       for (int i = 0; i < S::B_PER; ++i) {
-        int c = tid + 256 * i;
-        if (S::B_CHUNKS % 256 == 0 || c < S::B_CHUNKS)
+        int c = tid + S::NT * i;
+        if (S::B_CHUNKS % S::NT == 0 || c < S::B_CHUNKS)
           *reinterpret_cast<i32x4*>(sb + swz(c >> 3, c & 7)) = R.rb[i];
       }
       if constexpr (S::kFp8) {
@@ -245,20 +264,27 @@ __global__ __launch_bounds__(256, (DT == MOE_FP8_E4M3 ? 1 : 2)) void grouped_gem
     if constexpr (S::PF == 2) {
       // Registers R0 / R1 alternate: while step s multiplies out of LDS, the loads of steps
       // s+1 and s+2 are in flight; step s+1 is written to the other LDS buffer afterwards.
+      // Unconditional on purpose: a guarded load hides its count from the compiler's vmcnt
+      // bookkeeping, which then drains every load in flight before the LDS store.  Past the
+      // last step the buffer loads read bytes of the next row or, beyond the buffer, zeros,
+      // and the store fills an LDS buffer no one reads again.
       Stage R0, R1;
       load(0, R0);
-      if (KB > 1) load(1, R1);
+      load(1, R1);
       store(0, R0);
       __syncthreads();
       auto iter = [&](int step, Stage& Rfree, Stage& Rnext) {
-        if (step + 2 < KB) load(step + 2, Rfree);
-        compute(step & 1);
-        if (step + 1 < KB) store((step + 1) & 1, Rnext);
+        load(step + 2, Rfree);
+        // keep the loads ahead of the MFMAs: sunk below them they would share registers with
+        // the fragments and serialise on them
+        __builtin_amdgcn_sched_barrier(0);
+        if (step < KB) compute(step & 1);
+        store((step + 1) & 1, Rnext);
         __syncthreads();
       };
       for (int step = 0; step < KB; step += 2) {
         iter(step, R0, R1);
-        if (step + 1 < KB) iter(step + 1, R1, R0);
+        iter(step + 1, R1, R0);
       }
     } else {
       Stage R;
@@ -294,7 +320,7 @@ __global__ __launch_bounds__(256, (DT == MOE_FP8_E4M3 ? 1 : 2)) void grouped_gem
     if constexpr (DT == MOE_FP8_E4M3) {
       // one 128-value group per row: scale = max|h| / 448, codes = E4M3(h / scale)
       const int groups = (a.N / 2) / 128;
-      for (int r = wv; r < rows; r += 4) {
+      for (int r = wv; r < rows; r += S::NW) {
         float v0 = sH[r * HS + 2 * l], v1 = sH[r * HS + 2 * l + 1];
         float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
         float s = amax > 0.0f ? amax / 448.0f : 1.0f;
@@ -305,7 +331,7 @@ __global__ __launch_bounds__(256, (DT == MOE_FP8_E4M3 ? 1 : 2)) void grouped_gem
       }
     } else {
       constexpr int CPR = HC / 8;  // 8-value chunks per row
-      for (int c = tid; c < BM * CPR; c += 256) {
+      for (int c = tid; c < BM * CPR; c += S::NT) {
         const int r = c / CPR, cc = (c - r * CPR) * 8;
         if (r >= rows) continue;
         const float* v = sH + r * HS + cc;
@@ -341,7 +367,7 @@ __global__ __launch_bounds__(256, (DT == MOE_FP8_E4M3 ? 1 : 2)) void grouped_gem
     constexpr int ysz = y_f32 ? 4 : 2;
     constexpr int CPR = BN / 8;
     uint8_t* out = static_cast<uint8_t*>(a.out);
-    for (int c = tid; c < BM * CPR; c += 256) {
+    for (int c = tid; c < BM * CPR; c += S::NT) {
       const int r = c / CPR, cc = (c - r * CPR) * 8;
       if (r >= rows) continue;
       float v[8];
@@ -424,7 +450,6 @@ int gemm_bm(int dtype, int epi, int avg_rows) {
   return 128;
 }
 
-int gemm_bn(int dtype, int epi) { return (dtype == MOE_FP8_E4M3 && epi == kEpiSwiglu) ? 256 : 128; }
 
 template <int DT, int BM, int BN, int EPI, bool G>
 static hipError_t launch_one(const GemmArgs& a, int max_tiles, hipStream_t s) {
@@ -432,7 +457,8 @@ static hipError_t launch_one(const GemmArgs& a, int max_tiles, hipStream_t s) {
   if (!G) max_tiles = (a.M + BM - 1) / BM;
   int nb = max_tiles * (a.N / BN);
   if (nb <= 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_kernel<DT, BM, BN, EPI, G>), dim3(nb), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((grouped_gemm_kernel<DT, BM, BN, EPI, G>), dim3(nb),
+                     dim3(gemm_waves<DT, BN>() * kWave), 0, s, a);
   return hipGetLastError();
 }
 
@@ -447,7 +473,9 @@ static hipError_t launch_dt(int bm, const GemmArgs& a, int max_tiles, hipStream_
       case 16: return launch_one<DT, 16, 128, EPI, G>(a, max_tiles, s);
       case 32: return launch_one<DT, 32, 128, EPI, G>(a, max_tiles, s);
       case 64: return launch_one<DT, 64, 128, EPI, G>(a, max_tiles, s);
-      default: return launch_one<DT, 128, 128, EPI, G>(a, max_tiles, s);
+      default:  // the wide tile halves the activation re-reads per weight byte
+        return a.N % 256 == 0 ? launch_one<DT, 128, 256, EPI, G>(a, max_tiles, s)
+                              : launch_one<DT, 128, 128, EPI, G>(a, max_tiles, s);
     }
   }
 }

@@ -181,6 +181,7 @@ hipError_t do_route(const moe_config_t* c, const void* x, const moe_weights_t* w
   GemmArgs g{};
   g.A = x;
   g.lda = d * act_bytes(c);
+  g.a_bytes = c->num_tokens * g.lda;
   g.B = w->w_router;
   g.K = static_cast<int>(kind == kRouterBF16HiLo ? 2 * d : d);
   g.a_steps = kind == kRouterBF16HiLo ? static_cast<int>(d * 2 / kBlockK) : 0;
@@ -224,6 +225,7 @@ hipError_t do_expert_ffn(const moe_config_t* c, const void* xa, const float* xs,
   GemmArgs g{};
   g.A = xa;
   g.lda = d * (is_fp8(c) ? 1 : act_bytes(c));
+  g.a_bytes = c->num_tokens * g.lda;
   g.a_map = perm;
   g.a_scales = xs;
   g.B = w->w_gate_up;
@@ -245,6 +247,7 @@ hipError_t do_expert_ffn(const moe_config_t* c, const void* xa, const float* xs,
   GemmArgs h{};
   h.A = at<uint8_t>(ws, L.h);
   h.lda = f * wb;
+  h.a_bytes = A * h.lda;
   h.a_map = nullptr;
   h.a_scales = is_fp8(c) ? at<float>(ws, L.h_scales) : nullptr;
   h.B = w->w_down;
@@ -276,6 +279,7 @@ hipError_t do_combine(const moe_config_t* c, const void* xa, const float* xs, co
     GemmArgs g{};
     g.A = xa;
     g.lda = d * (is_fp8(c) ? 1 : act_bytes(c));
+    g.a_bytes = T * g.lda;
     g.a_scales = xs;
     g.B = w->ws_gate_up;
     g.b_scales = w->ws_gate_up_scales;
@@ -293,6 +297,7 @@ hipError_t do_combine(const moe_config_t* c, const void* xa, const float* xs, co
   GemmArgs h{};
   h.A = at<uint8_t>(ws, L.hs);
   h.lda = F * wb;
+  h.a_bytes = T * h.lda;
   h.a_scales = is_fp8(c) ? at<float>(ws, L.hs_scales) : nullptr;
   h.B = w->ws_down;
   h.b_scales = w->ws_down_scales;

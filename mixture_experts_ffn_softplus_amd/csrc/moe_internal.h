@@ -38,6 +38,7 @@ enum Epilogue { kEpiSwiglu = 0, kEpiStore = 1, kEpiCombine = 2 };
 struct GemmArgs {
   // A: activations, K-contiguous rows
   const void* A;
+  int64_t a_bytes;            // bytes of the whole A operand (< 4 GiB)
   int64_t lda;                // bytes per A row
   const int32_t* a_map;       // row of the M space -> A row, or null (identity)
   const float* a_scales;      // FP8: [A rows, K/128]
