@@ -48,9 +48,6 @@ template <int DT, int BM, int BN, int EPI>
 struct GemmShape {
   static constexpr int NW = gemm_waves<DT, BN>();
   static constexpr int NT = NW * kWave;
-  // loads in flight while step s multiplies: steps s+1 and s+2 (one step for FP8, whose wide
-  // accumulators leave no room for a second register stage)
-  static constexpr int PF = DT == MOE_FP8_E4M3 ? 1 : 2;
   static constexpr int WM = BM >= 32 ? 2 : 1;
   static constexpr int WN = NW / WM;
   static constexpr int TM = BM / WM, TN = BN / WN;
@@ -58,24 +55,43 @@ struct GemmShape {
   static constexpr bool kFp8 = DT == MOE_FP8_E4M3;
   static constexpr int A_CHUNKS = BM * 8, B_CHUNKS = BN * 8;  // 16-byte chunks per step
   static constexpr int A_PER = (A_CHUNKS + NT - 1) / NT, B_PER = (B_CHUNKS + NT - 1) / NT;
+  // LDS ring: step s multiplies out of slot s % 3 while steps s+1 and s+2 land in the others
+  static constexpr int NSLOT = 3;
   static constexpr int STAGE = (BM + BN) * kBlockK;
-  static constexpr int SCALE_STAGE = kFp8 ? (BM + BN / 16) * 4 : 0;
-  static constexpr int MAIN = 2 * STAGE + 2 * SCALE_STAGE;
+  // FP8 scales per slot: BM row scales, 64 weight-block scales, 64 floats for idle waves
+  static constexpr int SCALES = kFp8 ? (BM + 128) * 4 : 0;
+  static constexpr int SLOT = STAGE + SCALES;
+  static constexpr int DUMMY = NW * 1024;  // destination of the loads a wave issues for nothing
+  static constexpr int MAIN = NSLOT * SLOT + DUMMY;
+  // direct-to-LDS loads each wave issues per step (the same count in every wave)
+  static constexpr int LPS = A_PER + B_PER + (kFp8 ? 1 : 0);
   static constexpr int EPI_BYTES =
       EPI == kEpiSwiglu ? BM * (BN / 2 + 4) * 4 : BM * (BN + 4) * 4;
   static constexpr int SMEM = MAIN > EPI_BYTES ? MAIN : EPI_BYTES;
   static_assert(FM >= 1 && FN >= 1, "tile too small for 4 waves");
+  static_assert(!kFp8 || NW >= BM / 64 + 1, "FP8 scale loads need BM / 64 + 1 waves");
+  static_assert(LPS < 64, "vmcnt holds at most 63");
   static_assert(EPI != kEpiSwiglu || FN % 2 == 0, "gate/up pairs must stay within one wave");
   static_assert(!(kFp8 && EPI == kEpiSwiglu) || BN == 256, "FP8 h groups need 128 h columns");
 };
 
+// Waves per SIMD the register allocation aims for: what the LDS footprint lets run (160 KiB
+// per CU), capped at 2.
+template <int DT, int BM, int BN, int EPI>
+constexpr int gemm_occupancy() {
+  using S = GemmShape<DT, BM, BN, EPI>;
+  const int per_cu = (160 * 1024) / S::SMEM * S::NW / 4;
+  return per_cu < 1 ? 1 : per_cu > 2 ? 2 : per_cu;
+}
+
 // GROUPED: rows come from the device tile list of an expert-grouped problem (the routed
 // experts); otherwise one group of a.M rows (router, shared experts, combine).
 template <int DT, int BM, int BN, int EPI, bool GROUPED>
-__global__ __launch_bounds__((gemm_waves<DT, BN>() * kWave), (DT == MOE_FP8_E4M3 ? 1 : 2))
+__global__ __launch_bounds__((gemm_waves<DT, BN>() * kWave), (gemm_occupancy<DT, BM, BN, EPI>()))
 void grouped_gemm_kernel(GemmArgs a) {
   using S = GemmShape<DT, BM, BN, EPI>;
   constexpr int esize = DT_<DT>::esize;
+  constexpr int STAGE_BYTES = S::STAGE;
   __shared__ __attribute__((aligned(16))) uint8_t smem[S::SMEM];
 
   // ---------------------------------------------------------------- which tile
@@ -110,90 +126,87 @@ void grouped_gemm_kernel(GemmArgs a) {
     for (int j = 0; j < S::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (KB > 0) {
-    // ------------------------------------------------------------ per-thread load offsets
-    // A rows (gathered through a_map) and B rows are read with buffer loads: one 32-bit lane
-    // offset each, advanced by a wave-uniform step offset.
-    const __amdgpu_buffer_rsrc_t a_rs = buffer_rsrc(a.A, static_cast<uint32_t>(a.a_bytes));
+    // ------------------------------------------------------------ direct-to-LDS loads
+    // Every load writes 16 bytes per lane straight into LDS at (wave base + 16 * lane): the
+    // lane-to-chunk map is chosen on the global side so that the tile lands in the swizzled
+    // layout the fragment reads expect (row r's logical chunk c at slot r*8 + (c ^ (r & 7))).
+    // No staging registers, no LDS store instructions.
+    const i32x4 a_rs = rsrc_words(a.A, static_cast<uint32_t>(a.a_bytes));
     const uint8_t* bg = static_cast<const uint8_t*>(a.B) + group * a.b_group_stride;
-    const __amdgpu_buffer_rsrc_t b_rs =
-        buffer_rsrc(bg, static_cast<uint32_t>(static_cast<int64_t>(a.N) * ldb));
+    const i32x4 b_rs = rsrc_words(bg, static_cast<uint32_t>(static_cast<int64_t>(a.N) * ldb));
+    constexpr uint32_t kOob = 0x80000000u;  // beyond every buffer: reads zeros
+    // A rows repeat every a_steps steps when a_steps > 0 (the router's hi + lo weight planes
+    // are one [E, 2d] matrix multiplied by [x, x])
+    const int a_steps = a.a_steps > 0 ? a.a_steps : KB;
     uint32_t a_off[S::A_PER], b_off[S::B_PER];
+    int a_dst[S::A_PER], b_dst[S::B_PER];  // LDS byte offsets within a slot (-1: dummy)
 #pragma unroll
     for (int i = 0; i < S::A_PER; ++i) {
-      int c = tid + S::NT * i;
-      int r = c >> 3;
-      // rows past the tile's end get an offset beyond the buffer: the load returns zeros
-      // without a memory request (their outputs are never stored)
-      if (r < rows) {
-        int arow = a.a_map ? a.a_map[m0 + r] : m0 + r;
-        a_off[i] = static_cast<uint32_t>(static_cast<int64_t>(arow) * a.lda + (c & 7) * 16);
-      } else {
-        a_off[i] = 0x80000000u;
+      const int c = tid + S::NT * i, r = c >> 3;
+      const int wbase = (c - l) * 16;  // this wave's 1 KiB destination
+      a_dst[i] = c < S::A_CHUNKS ? wbase : -1;
+      a_off[i] = kOob;
+      // rows past the tile's end read zeros (their outputs are never stored)
+      if (c < S::A_CHUNKS && r < rows) {
+        const int arow = a.a_map ? a.a_map[m0 + r] : m0 + r;
+        a_off[i] = static_cast<uint32_t>(static_cast<int64_t>(arow) * a.lda +
+                                         (((c & 7) ^ (r & 7)) << 4));
       }
     }
 #pragma unroll
     for (int i = 0; i < S::B_PER; ++i) {
-      int c = tid + S::NT * i;
-      b_off[i] = static_cast<uint32_t>(static_cast<int64_t>(n0 + (c >> 3)) * ldb + (c & 7) * 16);
+      const int c = tid + S::NT * i, r = c >> 3;
+      b_dst[i] = c < S::B_CHUNKS ? BM * kBlockK + (c - l) * 16 : -1;
+      b_off[i] = c < S::B_CHUNKS ? static_cast<uint32_t>(static_cast<int64_t>(n0 + r) * ldb +
+                                                         (((c & 7) ^ (r & 7)) << 4))
+                                 : kOob;
     }
-    const float* as_ptr = nullptr;
-    const float* bs_ptr = nullptr;
+    // FP8: wave w < BM/64 loads the row scales of rows [64w, 64w+64), wave BM/64 the weight
+    // block scales, any other wave a dummy slice
+    i32x4 s_rs = rsrc_words(a.A, 0);  // replaced below for FP8
+    uint32_t s_off = kOob;
+    int s_dst = 0;
     if constexpr (S::kFp8) {
-      if (tid < BM) {
-        int r = min(tid, rows - 1);
-        int arow = a.a_map ? a.a_map[m0 + r] : m0 + r;
-        as_ptr = a.a_scales + static_cast<int64_t>(arow) * KB;
-      } else if (tid < BM + BN / 16) {
-        bs_ptr = a.b_scales + group * a.bs_group_stride +
-                 static_cast<int64_t>(n0 / 16 + (tid - BM)) * KB;
+      const int kb_bytes = KB * 4;
+      if (wv < BM / 64) {
+        const uint32_t a_rows = static_cast<uint32_t>(a.a_bytes / a.lda);
+        s_rs = rsrc_words(a.a_scales, a_rows * kb_bytes);
+        const int r = wv * 64 + l;
+        if (r < rows) {
+          const int arow = a.a_map ? a.a_map[m0 + r] : m0 + r;
+          s_off = static_cast<uint32_t>(arow) * kb_bytes;
+        }
+        s_dst = STAGE_BYTES + wv * 256;
+      } else if (wv == BM / 64) {
+        s_rs = rsrc_words(a.b_scales + group * a.bs_group_stride,
+                          static_cast<uint32_t>((a.N / 16) * kb_bytes));
+        if (l < BN / 16) s_off = static_cast<uint32_t>(n0 / 16 + l) * kb_bytes;
+        s_dst = STAGE_BYTES + BM * 4;
+      } else {
+        s_rs = rsrc_words(a.b_scales, 4);
+        s_dst = STAGE_BYTES + BM * 4 + 256;
       }
     }
-
-    // A rows repeat every a_steps steps when a_steps > 0 (the router's hi + lo weight planes
-    // are one [E, 2d] matrix multiplied by [x, x])
-    const int a_steps = a.a_steps > 0 ? a.a_steps : KB;
-    struct Stage {
-      i32x4 ra[S::A_PER], rb[S::B_PER];
-      float sc;
+    const uint32_t smem_base = lds_addr(smem);
+    auto lds_ptr = [&](int slot, int dst) {
+      const int o = dst >= 0 ? slot * S::SLOT + dst : S::NSLOT * S::SLOT + wv * 1024;
+      return smem_base + static_cast<uint32_t>(o);
     };
-    auto load = [&](int step, Stage& R) {
-      const uint32_t as = static_cast<uint32_t>(step < a_steps ? step : step - a_steps) * kBlockK;
+    auto issue = [&](int step) {
+      const int slot = step % S::NSLOT;
+      const uint32_t as =
+          static_cast<uint32_t>(step < a_steps ? step : step - a_steps) * kBlockK;
       const uint32_t bs = static_cast<uint32_t>(step) * kBlockK;
 #pragma unroll
-      for (int i = 0; i < S::A_PER; ++i)
-        if (S::A_CHUNKS % S::NT == 0 || tid + S::NT * i < S::A_CHUNKS)
-          R.ra[i] = buffer_load16(a_rs, a_off[i], as);
+      for (int i = 0; i < S::A_PER; ++i) lds_dma<16, false>(a_rs, lds_ptr(slot, a_dst[i]), a_off[i], as);
 #pragma unroll
-      for (int i = 0; i < S::B_PER; ++i)
-        if (S::B_CHUNKS % S::NT == 0 || tid + S::NT * i < S::B_CHUNKS)
-          R.rb[i] = buffer_load16<kNonTemporal>(b_rs, b_off[i], bs);  // weights: streamed
-      if constexpr (S::kFp8) {
-        if (as_ptr) R.sc = as_ptr[step];
-        else if (bs_ptr) R.sc = bs_ptr[step];
-      }
+      for (int i = 0; i < S::B_PER; ++i)  // weights: streamed
+        lds_dma<16, true>(b_rs, lds_ptr(slot, b_dst[i]), b_off[i], bs);
+      if constexpr (S::kFp8)
+        lds_dma<4, false>(s_rs, lds_ptr(slot, s_dst), s_off, static_cast<uint32_t>(step) * 4);
     };
-    auto store = [&](int buf, const Stage& R) {
-      uint8_t* sa = smem + buf * S::STAGE;
-      uint8_t* sb = sa + BM * kBlockK;
-#pragma unroll
-      for (int i = 0; i < S::A_PER; ++i) {
-        int c = tid + S::NT * i;
-        if (S::A_CHUNKS % S::NT == 0 || c < S::A_CHUNKS)
-          *reinterpret_cast<i32x4*>(sa + swz(c >> 3, c & 7)) = R.ra[i];
-      }
-#pragma unroll
-      for (int i = 0; i < S::B_PER; ++i) {
-        int c = tid + S::NT * i;
-        if (S::B_CHUNKS % S::NT == 0 || c < S::B_CHUNKS)
-          *reinterpret_cast<i32x4*>(sb + swz(c >> 3, c & 7)) = R.rb[i];
-      }
-      if constexpr (S::kFp8) {
-        float* ss = reinterpret_cast<float*>(smem + 2 * S::STAGE + buf * S::SCALE_STAGE);
-        if (tid < BM + BN / 16) ss[tid] = R.sc;
-      }
-    };
-    auto compute = [&](int buf) {
-      const uint8_t* sa = smem + buf * S::STAGE;
+    auto compute = [&](int slot) {
+      const uint8_t* sa = smem + slot * S::SLOT;
       const uint8_t* sb = sa + BM * kBlockK;
       if constexpr (DT == MOE_BF16) {
 #pragma unroll
@@ -232,7 +245,7 @@ void grouped_gemm_kernel(GemmArgs a) {
       } else {
         // one E4M3 MFMA covers exactly one 128-deep scale block; its fp32 partial is promoted
         // with the row's activation scale times the block's weight scale
-        const float* ss = reinterpret_cast<const float*>(smem + 2 * S::STAGE + buf * S::SCALE_STAGE);
+        const float* ss = reinterpret_cast<const float*>(sa + STAGE_BYTES);
         i32x8 af[S::FM];
         float sav[S::FM][4];
 #pragma unroll
@@ -261,43 +274,21 @@ void grouped_gemm_kernel(GemmArgs a) {
       }
     };
 
-    if constexpr (S::PF == 2) {
-      // Registers R0 / R1 alternate: while step s multiplies out of LDS, the loads of steps
-      // s+1 and s+2 are in flight; step s+1 is written to the other LDS buffer afterwards.
-      // Unconditional on purpose: a guarded load hides its count from the compiler's vmcnt
-      // bookkeeping, which then drains every load in flight before the LDS store.  Past the
-      // last step the buffer loads read bytes of the next row or, beyond the buffer, zeros,
-      // and the store fills an LDS buffer no one reads again.
-      Stage R0, R1;
-      load(0, R0);
-      load(1, R1);
-      store(0, R0);
+    // Step s: wait for this wave's loads of step s (those of s+1 stay in flight), barrier (all
+    // waves' step-s data is in LDS and every wave has finished step s-1), issue step s+2 into
+    // the slot step s-1 used, multiply step s.  Issue is unconditional: past the last step the
+    // loads read bytes of the next row or zeros into slots no one reads, so every wave keeps
+    // the same count of loads in flight for the wait below.
+    issue(0);
+    issue(1);
+    for (int step = 0; step < KB; ++step) {
+      lds_dma_wait<S::LPS>();
       __syncthreads();
-      auto iter = [&](int step, Stage& Rfree, Stage& Rnext) {
-        load(step + 2, Rfree);
-        // keep the loads ahead of the MFMAs: sunk below them they would share registers with
-        // the fragments and serialise on them
-        __builtin_amdgcn_sched_barrier(0);
-        if (step < KB) compute(step & 1);
-        store((step + 1) & 1, Rnext);
-        __syncthreads();
-      };
-      for (int step = 0; step < KB; step += 2) {
-        iter(step, R0, R1);
-        iter(step + 1, R1, R0);
-      }
-    } else {
-      Stage R;
-      load(0, R);
-      store(0, R);
-      __syncthreads();
-      for (int step = 0; step < KB; ++step) {
-        if (step + 1 < KB) load(step + 1, R);
-        compute(step & 1);
-        if (step + 1 < KB) store((step + 1) & 1, R);
-        __syncthreads();
-      }
+      issue(step + 2);
+      compute(step % S::NSLOT);
     }
+    lds_dma_wait<0>();  // the epilogue reuses the ring
+    __syncthreads();
   }
 
   // ---------------------------------------------------------------- epilogues

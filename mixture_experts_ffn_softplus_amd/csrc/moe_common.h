@@ -87,6 +87,49 @@ __device__ __forceinline__ i32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
                                                AUX);
 }
 
+// ----------------------------------------------------------------------------- LDS DMA
+// Buffer loads whose data goes straight to LDS: lane l's BYTES land at (lds + BYTES * l), the
+// base taken from M0.  Issued from inline asm on purpose: the compiler cannot tell which LDS
+// bytes such a load writes, so for its own bookkeeping it would wait for every one in flight
+// before any LDS read, serialising a multi-slot ring.  These loads have no register results;
+// their completion is awaited explicitly with lds_dma_wait (vector-memory counts complete in
+// issue order), followed by a barrier.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return i32x4{uniform(static_cast<int>(static_cast<uint32_t>(p))),
+               uniform(static_cast<int>(static_cast<uint32_t>(p >> 32) & 0xFFFFu)),
+               uniform(static_cast<int>(bytes)), 0x00020000};
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const uint8_t*)(p)));
+}
+// M0 is written here and listed nowhere: no compiler-generated code in these kernels keeps a
+// value in M0 (LDS instructions ignore it on gfx9 and later, and no register array is indexed
+// dynamically).
+template <int BYTES, bool NT>
+__device__ __forceinline__ void lds_dma(i32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  static_assert(BYTES == 16 || BYTES == 4, "dwordx4 or dword");
+  const int l = uniform(static_cast<int>(lds)), so = uniform(static_cast<int>(soff));
+  rsrc = i32x4{uniform(rsrc[0]), uniform(rsrc[1]), uniform(rsrc[2]), uniform(rsrc[3])};
+  if constexpr (BYTES == 16 && NT)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+                 :: "s"(l), "v"(voff), "s"(rsrc), "s"(so) : "memory");
+  else if constexpr (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(l), "v"(voff), "s"(rsrc), "s"(so) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(l), "v"(voff), "s"(rsrc), "s"(so) : "memory");
+}
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void lds_dma_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
 // ----------------------------------------------------------------------------- wave utilities
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
