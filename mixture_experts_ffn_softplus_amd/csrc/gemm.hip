@@ -13,16 +13,20 @@
 //                  routed sum).
 //
 // Structure.  4 or 8 waves per workgroup (each wave a 64 x 64 or smaller sub-tile), a BM x BN
-// output tile, K consumed 128 bytes
-// per step (64 bf16, 32 fp32 or 128 E4M3 values -- exactly one FP8 scale block).  Each step's
-// A rows (gathered through a_map: no permuted copy of x is ever written) and B rows are
-// fetched with 16-byte loads into registers while the MFMAs of the previous step run, then
-// written to a double-buffered LDS tile whose 16-byte chunks are XOR-swizzled by row so that
-// the fragment reads of 16 consecutive rows hit distinct banks.  Workgroups map to tiles
-// through an XCD-aware remap so that neighbouring tiles (the N-tiles of one expert, which share
-// its A rows) run in the same XCD's L2.  Grids are sized for the worst case and read the
+// output tile, K consumed 128 bytes per step (64 bf16, 32 fp32 or 128 E4M3 values -- exactly
+// one FP8 scale block).  Each step's A rows (gathered through a_map: no permuted copy of x is
+// ever written) and B rows go straight from global memory into a three-slot LDS ring with
+// buffer loads that write LDS directly, issued three steps ahead; their 16-byte chunks land
+// XOR-swizzled by row so that the fragment reads of 16 consecutive rows hit distinct banks.
+// Fragments of step s+1 are read from LDS while the MFMAs of step s run, one barrier per step.
+// Weights of an expert whose rows fit one tile are loaded non-temporally (read once); others
+// keep the default policy so the expert's other row tiles find them in L2.  Workgroups map to
+// tiles through an XCD-aware remap so that neighbouring tiles (the N-tiles of one expert, which
+// share its A rows) run in the same XCD's L2.  Grids are sized for the worst case and read the
 // device tile count, so no per-expert count travels to the host.
 #include <math.h>
+
+#include <type_traits>
 
 #include "moe_common.h"
 #include "moe_internal.h"
@@ -42,7 +46,7 @@ __device__ __forceinline__ int swz(int row, int ch) { return row * kBlockK + ((c
 
 // NW waves per workgroup: 8 for the wide bf16 tiles (BN = 256, each wave still 64 x 64), else 4.
 template <int DT, int BN>
-constexpr int gemm_waves() { return (DT == MOE_BF16 && BN >= 256) ? 8 : 4; }
+constexpr int gemm_waves() { return (DT != MOE_F32 && BN >= 256) ? 8 : 4; }
 
 template <int DT, int BM, int BN, int EPI>
 struct GemmShape {
@@ -70,9 +74,24 @@ struct GemmShape {
   static constexpr int SMEM = MAIN > EPI_BYTES ? MAIN : EPI_BYTES;
   static_assert(FM >= 1 && FN >= 1, "tile too small for 4 waves");
   static_assert(!kFp8 || NW >= BM / 64 + 1, "FP8 scale loads need BM / 64 + 1 waves");
-  static_assert(LPS < 64, "vmcnt holds at most 63");
+  static_assert(2 * LPS < 64, "vmcnt holds at most 63");
+  static_assert(!kFp8 || (TN <= 128 && 128 % TN == 0), "FP8: two weight scales per wave");
   static_assert(EPI != kEpiSwiglu || FN % 2 == 0, "gate/up pairs must stay within one wave");
   static_assert(!(kFp8 && EPI == kEpiSwiglu) || BN == 256, "FP8 h groups need 128 h columns");
+};
+
+// Register fragments of one pipeline step: two 16x16x32 (bf16) or 16x16x4-by-4 (fp32) K-halves,
+// or one 16x16x128 E4M3 block with its row scales and the wave's two weight-block scales.
+template <int DT, int FM, int FN>
+struct Frags {
+  using V = typename std::conditional<DT == MOE_BF16, bf16x8, f32x4>::type;
+  V a[2][FM], b[2][FN];
+};
+template <int FM, int FN>
+struct Frags<MOE_FP8_E4M3, FM, FN> {
+  i32x8 a[1][FM], b[1][FN];
+  f32x4 sa[FM];
+  float sb[2];
 };
 
 // Waves per SIMD the register allocation aims for: what the LDS footprint lets run (160 KiB
@@ -102,22 +121,24 @@ void grouped_gemm_kernel(GemmArgs a) {
   const int L = xcd_remap(blockIdx.x, nblocks);
   const int tile = L / NT, nt = L - tile * NT;
   int group = 0, m0, rows;
+  bool stream_b = false;
   if constexpr (GROUPED) {
     int4 ti = a.tiles[tile];
     group = ti.x;
     m0 = ti.y;
     rows = ti.z;
+    stream_b = a.b_stream && ti.w == 1;  // no other row tile of this group reads these weights
   } else {
     m0 = tile * BM;
     rows = min(BM, a.M - m0);
   }
   const int n0 = nt * BN;
 
-  const int tid = threadIdx.x, l = lane_id(), wv = tid / kWave;
+  const int tid = threadIdx.x, l = lane_id(), wv = uniform(tid / kWave);
   const int wm = wv / S::WN, wn = wv % S::WN;
   const int lr = l & 15, kq = l >> 4;
   const int KB = a.K * esize / kBlockK;  // pipeline steps
-  const int64_t ldb = static_cast<int64_t>(a.K) * esize;
+  const int64_t ldb = a.ldb;
 
   f32x4 acc[S::FM][S::FN];
 #pragma unroll
@@ -143,8 +164,8 @@ void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < S::A_PER; ++i) {
       const int c = tid + S::NT * i, r = c >> 3;
-      const int wbase = (c - l) * 16;  // this wave's 1 KiB destination
-      a_dst[i] = c < S::A_CHUNKS ? wbase : -1;
+      const int wc = wv * kWave + S::NT * i;  // this wave's first chunk: 1 KiB destination
+      a_dst[i] = wc < S::A_CHUNKS ? wc * 16 : -1;
       a_off[i] = kOob;
       // rows past the tile's end read zeros (their outputs are never stored)
       if (c < S::A_CHUNKS && r < rows) {
@@ -156,7 +177,8 @@ void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < S::B_PER; ++i) {
       const int c = tid + S::NT * i, r = c >> 3;
-      b_dst[i] = c < S::B_CHUNKS ? BM * kBlockK + (c - l) * 16 : -1;
+      const int wc = wv * kWave + S::NT * i;
+      b_dst[i] = wc < S::B_CHUNKS ? BM * kBlockK + wc * 16 : -1;
       b_off[i] = c < S::B_CHUNKS ? static_cast<uint32_t>(static_cast<int64_t>(n0 + r) * ldb +
                                                          (((c & 7) ^ (r & 7)) << 4))
                                  : kOob;
@@ -199,93 +221,176 @@ void grouped_gemm_kernel(GemmArgs a) {
       const uint32_t bs = static_cast<uint32_t>(step) * kBlockK;
 #pragma unroll
       for (int i = 0; i < S::A_PER; ++i) lds_dma<16, false>(a_rs, lds_ptr(slot, a_dst[i]), a_off[i], as);
+      if (stream_b) {  // weights read by one tile only: do not keep them in the caches
 #pragma unroll
-      for (int i = 0; i < S::B_PER; ++i)  // weights: streamed
-        lds_dma<16, true>(b_rs, lds_ptr(slot, b_dst[i]), b_off[i], bs);
+        for (int i = 0; i < S::B_PER; ++i) lds_dma<16, true>(b_rs, lds_ptr(slot, b_dst[i]), b_off[i], bs);
+      } else {
+#pragma unroll
+        for (int i = 0; i < S::B_PER; ++i) lds_dma<16, false>(b_rs, lds_ptr(slot, b_dst[i]), b_off[i], bs);
+      }
       if constexpr (S::kFp8)
         lds_dma<4, false>(s_rs, lds_ptr(slot, s_dst), s_off, static_cast<uint32_t>(step) * 4);
     };
-    auto compute = [&](int slot) {
+    // Operand fragments of one step, read from its LDS slot into registers one step ahead of
+    // the MFMAs that use them.
+    using F = Frags<DT, S::FM, S::FN>;
+    auto load = [&](F& f, int slot) {
       const uint8_t* sa = smem + slot * S::SLOT;
       const uint8_t* sb = sa + BM * kBlockK;
-      if constexpr (DT == MOE_BF16) {
+      if constexpr (DT == MOE_FP8_E4M3) {
+        const float* ss = reinterpret_cast<const float*>(sa + STAGE_BYTES);
+#pragma unroll
+        for (int i = 0; i < S::FM; ++i) {
+          const int r = wm * S::TM + i * 16 + lr;
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(sa + swz(r, 2 * kq));
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(sa + swz(r, 2 * kq + 1));
+          f.a[0][i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          f.sa[i] = *reinterpret_cast<const f32x4*>(ss + wm * S::TM + i * 16 + 4 * kq);
+        }
+#pragma unroll
+        for (int j = 0; j < S::FN; ++j) {
+          const int r = wn * S::TN + j * 16 + lr;
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(sb + swz(r, 2 * kq));
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(sb + swz(r, 2 * kq + 1));
+          f.b[0][j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+        // a wave's columns lie in one 128-wide weight block per gate/up half (even/odd
+        // 16-row blocks of the packed rows), so two weight scales cover all its fragments
+        f.sb[0] = ss[BM + wn * S::TN / 16];
+        f.sb[1] = ss[BM + wn * S::TN / 16 + 1];
+      } else {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           const int ch = 4 * s + kq;
-          bf16x8 af[S::FM], bf[S::FN];
 #pragma unroll
           for (int i = 0; i < S::FM; ++i)
-            af[i] = *reinterpret_cast<const bf16x8*>(sa + swz(wm * S::TM + i * 16 + lr, ch));
+            f.a[s][i] = *reinterpret_cast<const typename F::V*>(sa + swz(wm * S::TM + i * 16 + lr, ch));
 #pragma unroll
           for (int j = 0; j < S::FN; ++j)
-            bf[j] = *reinterpret_cast<const bf16x8*>(sb + swz(wn * S::TN + j * 16 + lr, ch));
+            f.b[s][j] = *reinterpret_cast<const typename F::V*>(sb + swz(wn * S::TN + j * 16 + lr, ch));
+        }
+      }
+    };
+    auto mma = [&](const F& f) {
+      if constexpr (DT == MOE_BF16) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
           for (int i = 0; i < S::FM; ++i)
 #pragma unroll
-            for (int j = 0; j < S::FN; ++j) acc[i][j] = mfma_bf16(af[i], bf[j], acc[i][j]);
-        }
+            for (int j = 0; j < S::FN; ++j) acc[i][j] = mfma_bf16(f.a[s][i], f.b[s][j], acc[i][j]);
       } else if constexpr (DT == MOE_F32) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int ch = kq + 4 * s;
-          f32x4 af[S::FM], bf[S::FN];
-#pragma unroll
-          for (int i = 0; i < S::FM; ++i)
-            af[i] = *reinterpret_cast<const f32x4*>(sa + swz(wm * S::TM + i * 16 + lr, ch));
-#pragma unroll
-          for (int j = 0; j < S::FN; ++j)
-            bf[j] = *reinterpret_cast<const f32x4*>(sb + swz(wn * S::TN + j * 16 + lr, ch));
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
 #pragma unroll
             for (int i = 0; i < S::FM; ++i)
 #pragma unroll
-              for (int j = 0; j < S::FN; ++j) acc[i][j] = mfma_f32(af[i][e], bf[j][e], acc[i][j]);
-        }
-      } else {
-        // one E4M3 MFMA covers exactly one 128-deep scale block; its fp32 partial is promoted
-        // with the row's activation scale times the block's weight scale
+              for (int j = 0; j < S::FN; ++j)
+                acc[i][j] = mfma_f32(f.a[s][i][e], f.b[s][j][e], acc[i][j]);
+      }  // FP8: mma_refill_fp8
+    };
+    // FP8 step: one E4M3 MFMA covers exactly one 128-deep scale block; its fp32 partial is
+    // promoted with the row's activation scale times the block's weight scale.  Written in
+    // issue order (sched_barrier pins it): MFMA n runs while partial n-1 is promoted, so only
+    // two partials are live, and f is refilled from slot `next` as soon as each fragment's last
+    // MFMA has issued (A row block i after its row of MFMAs, the B columns after the last row).
+    auto mma_refill_fp8 = [&](F& f, int next) {
+      if constexpr (S::kFp8) {
+        const uint8_t* sa = smem + next * S::SLOT;
+        const uint8_t* sb = sa + BM * kBlockK;
         const float* ss = reinterpret_cast<const float*>(sa + STAGE_BYTES);
-        i32x8 af[S::FM];
-        float sav[S::FM][4];
+        f32x4 prev = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 q[2], qp[2];
 #pragma unroll
         for (int i = 0; i < S::FM; ++i) {
-          const int r = wm * S::TM + i * 16 + lr;
-          i32x4 lo = *reinterpret_cast<const i32x4*>(sa + swz(r, 2 * kq));
-          i32x4 hi = *reinterpret_cast<const i32x4*>(sa + swz(r, 2 * kq + 1));
-          af[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sav[i][e] = ss[wm * S::TM + i * 16 + 4 * kq + e];
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) q[h][e] = f.sa[i][e] * f.sb[h];
+#pragma unroll
+          for (int j = 0; j < S::FN; ++j) {
+            const f32x4 cur = mfma_fp8(f.a[0][i], f.b[0][j], f32x4{0.f, 0.f, 0.f, 0.f});
+            if (i + j > 0) {
+              const int pi = j > 0 ? i : i - 1, pj = j > 0 ? j - 1 : S::FN - 1;
+              const f32x4& qq = j > 0 ? q[pj & 1] : qp[pj & 1];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[pi][pj][e] = fmaf(prev[e], qq[e], acc[pi][pj][e]);
+            }
+            prev = cur;
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          qp[0] = q[0];
+          qp[1] = q[1];
+          // row block i is done with its A fragment and row scales
+          const int r = wm * S::TM + i * 16 + lr;
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(sa + swz(r, 2 * kq));
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(sa + swz(r, 2 * kq + 1));
+          f.a[0][i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          f.sa[i] = *reinterpret_cast<const f32x4*>(ss + wm * S::TM + i * 16 + 4 * kq);
+          __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[S::FM - 1][S::FN - 1][e] = fmaf(prev[e], qp[(S::FN - 1) & 1][e], acc[S::FM - 1][S::FN - 1][e]);
 #pragma unroll
         for (int j = 0; j < S::FN; ++j) {
           const int r = wn * S::TN + j * 16 + lr;
-          i32x4 lo = *reinterpret_cast<const i32x4*>(sb + swz(r, 2 * kq));
-          i32x4 hi = *reinterpret_cast<const i32x4*>(sb + swz(r, 2 * kq + 1));
-          i32x8 bfr = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          const float sbv = ss[BM + (wn * S::TN + j * 16) / 16];
-#pragma unroll
-          for (int i = 0; i < S::FM; ++i) {
-            f32x4 p = mfma_fp8(af[i], bfr, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(p[e], sav[i][e] * sbv, acc[i][j][e]);
-          }
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(sb + swz(r, 2 * kq));
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(sb + swz(r, 2 * kq + 1));
+          f.b[0][j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
+        f.sb[0] = ss[BM + wn * S::TN / 16];
+        f.sb[1] = ss[BM + wn * S::TN / 16 + 1];
       }
     };
 
-    // Step s: wait for this wave's loads of step s (those of s+1 stay in flight), barrier (all
-    // waves' step-s data is in LDS and every wave has finished step s-1), issue step s+2 into
-    // the slot step s-1 used, multiply step s.  Issue is unconditional: past the last step the
-    // loads read bytes of the next row or zeros into slots no one reads, so every wave keeps
-    // the same count of loads in flight for the wait below.
+    // FP8 keeps one fragment set (two do not fit beside the accumulators at two waves per
+    // SIMD) and refills it in place once the MFMAs reading it are issued.
+    constexpr bool kTwoSets = !S::kFp8;
+    F f0, f1;
     issue(0);
     issue(1);
-    for (int step = 0; step < KB; ++step) {
+    issue(2);
+    lds_dma_wait<2 * S::LPS>();
+    __syncthreads();
+    load(f0, 0);
+    // The refill after the last step reads a slot no one wrote for it: harmless, and it keeps
+    // the loop body one basic block for the scheduler.
+    auto iter = [&](int step, F& cur, F& nxt) {
       lds_dma_wait<S::LPS>();
       __syncthreads();
-      issue(step + 2);
-      compute(step % S::NSLOT);
+      issue(step + 3);
+      const int next = (step + 1) % S::NSLOT;
+      if constexpr (kTwoSets) {
+        // one fragment read, then its share of the MFMAs, repeated: the reads of step s+1
+        // spread over the MFMAs of step s instead of bunching at either end
+        constexpr int NR = 2 * (S::FM + S::FN);
+        constexpr int NM = 2 * S::FM * S::FN * (DT == MOE_F32 ? 4 : 1);
+        constexpr int PER = NM / NR;
+        __builtin_amdgcn_sched_barrier(0);
+        load(nxt, next);
+        mma(cur);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
+          __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // MFMA
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NM - PER * NR, 0);
+      } else {
+        mma_refill_fp8(cur, next);
+      }
+    };
+    int step = 0;
+    if constexpr (kTwoSets) {
+      for (; step + 1 < KB; step += 2) {
+        iter(step, f0, f1);
+        iter(step + 1, f1, f0);
+      }
+      if (step < KB) iter(step, f0, f1);
+    } else {
+      for (; step < KB; ++step) iter(step, f0, f0);
     }
     lds_dma_wait<0>();  // the epilogue reuses the ring
     __syncthreads();

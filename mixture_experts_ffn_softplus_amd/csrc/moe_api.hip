@@ -184,6 +184,7 @@ hipError_t do_route(const moe_config_t* c, const void* x, const moe_weights_t* w
   g.a_bytes = c->num_tokens * g.lda;
   g.B = w->w_router;
   g.K = static_cast<int>(kind == kRouterBF16HiLo ? 2 * d : d);
+  g.ldb = static_cast<int64_t>(g.K) * (kind == kRouterF32 ? 4 : 2);
   g.a_steps = kind == kRouterBF16HiLo ? static_cast<int>(d * 2 / kBlockK) : 0;
   g.N = static_cast<int>(Ep);
   g.M = c->num_tokens;
@@ -229,7 +230,8 @@ hipError_t do_expert_ffn(const moe_config_t* c, const void* xa, const float* xs,
   g.a_map = perm;
   g.a_scales = xs;
   g.B = w->w_gate_up;
-  g.b_group_stride = 2 * f * d * wb;
+  g.ldb = d * wb;
+  g.b_group_stride = 2 * f * g.ldb;
   g.b_scales = w->w_gate_up_scales;
   g.bs_group_stride = (2 * f / 16) * (d / 128);
   g.K = static_cast<int>(d);
@@ -240,6 +242,8 @@ hipError_t do_expert_ffn(const moe_config_t* c, const void* xa, const float* xs,
   g.out = at<uint8_t>(ws, L.h);
   g.ldo = f * wb;
   g.out_scales = is_fp8(c) ? at<float>(ws, L.h_scales) : nullptr;
+  // an expert whose rows fit one tile streams its weights past the caches
+  g.b_stream = 1;
   e = launch_grouped_gemm(c->expert_dtype, kEpiSwiglu, bm, false, g, max_tiles, s);
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_GATE_UP, s);
   if (e != hipSuccess) return e;
@@ -251,7 +255,8 @@ hipError_t do_expert_ffn(const moe_config_t* c, const void* xa, const float* xs,
   h.a_map = nullptr;
   h.a_scales = is_fp8(c) ? at<float>(ws, L.h_scales) : nullptr;
   h.B = w->w_down;
-  h.b_group_stride = d * f * wb;
+  h.ldb = f * wb;
+  h.b_group_stride = d * h.ldb;
   h.b_scales = w->w_down_scales;
   h.bs_group_stride = (d / 16) * (f / 128);
   h.K = static_cast<int>(f);
@@ -261,6 +266,7 @@ hipError_t do_expert_ffn(const moe_config_t* c, const void* xa, const float* xs,
   h.M = static_cast<int>(A);
   h.out = y;
   h.ldo = d * y_bytes(c);
+  h.b_stream = g.b_stream;
   e = launch_grouped_gemm(c->expert_dtype, kEpiStore, bm, false, h, max_tiles, s);
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_DOWN, s);
   return e;
@@ -282,6 +288,7 @@ hipError_t do_combine(const moe_config_t* c, const void* xa, const float* xs, co
     g.a_bytes = T * g.lda;
     g.a_scales = xs;
     g.B = w->ws_gate_up;
+    g.ldb = d * wb;
     g.b_scales = w->ws_gate_up_scales;
     g.K = static_cast<int>(d);
     g.N = static_cast<int>(2 * F);
@@ -300,6 +307,7 @@ hipError_t do_combine(const moe_config_t* c, const void* xa, const float* xs, co
   h.a_bytes = T * h.lda;
   h.a_scales = is_fp8(c) ? at<float>(ws, L.hs_scales) : nullptr;
   h.B = w->ws_down;
+  h.ldb = F * wb;
   h.b_scales = w->ws_down_scales;
   h.K = static_cast<int>(F);
   h.N = static_cast<int>(d);

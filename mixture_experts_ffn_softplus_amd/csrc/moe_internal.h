@@ -45,6 +45,8 @@ struct GemmArgs {
   // B: packed weights of each group, [N, K] K-contiguous
   const void* B;
   int64_t b_group_stride;     // bytes per group
+  int64_t ldb;                // bytes between rows of B
+  int b_stream;               // B of a group with one row tile: load it non-temporally
   const float* b_scales;      // FP8: [N/128, K/128] per group
   int64_t bs_group_stride;    // floats per group
   int K, N;
