@@ -90,7 +90,7 @@ moe_status_t check_config(const moe_config_t* c) {
 
 struct WsLayout {
   size_t logits, ids, w, offsets, perm, inv, hist, tiles, tiles_count, xq, xq_scales, h,
-      h_scales, hs, hs_scales, y, total;
+      h_scales, hs, hs_scales, so, y, total;
 };
 
 WsLayout ws_layout(const moe_config_t* c) {
@@ -120,6 +120,7 @@ WsLayout ws_layout(const moe_config_t* c) {
   L.h_scales = take(is_fp8(c) ? A * (f / 128) * 4 : 0);
   L.hs = take(T * fs * hb);
   L.hs_scales = take(is_fp8(c) ? T * (fs / 128) * 4 : 0);
+  L.so = take(c->num_shared > 0 ? T * d * 4 : 0);  // shared experts' output, fp32
   L.y = take(A * d * y_bytes(c));
   L.total = o;
   return L;
@@ -190,13 +191,14 @@ hipError_t do_route(const moe_config_t* c, const void* x, const moe_weights_t* w
   g.M = c->num_tokens;
   g.out = lg;
   g.ldo = Ep * 4;
-  g.col_bias = w->logit_bias;
-  g.bias_cols = c->num_experts;
+  g.out_f32 = 1;
   const int bm = router_bm(c);
-  hipError_t e = launch_grouped_gemm(kind == kRouterF32 ? MOE_F32 : MOE_BF16, kEpiStore, bm,
-                                     true, g, (c->num_tokens + bm - 1) / bm, s);
+  hipError_t e = launch_grouped_gemm(kind == kRouterF32 ? MOE_F32 : MOE_BF16, kEpiStore, bm, g,
+                                     (c->num_tokens + bm - 1) / bm, s);
   if (e != hipSuccess) return e;
-  e = launch_topk(route_args(c, w->select_bias, ids, tw), lg, static_cast<int>(Ep), logits, s);
+  RouteArgs ra = route_args(c, w->select_bias, ids, tw);
+  ra.logit_bias = w->logit_bias;
+  e = launch_topk(ra, lg, static_cast<int>(Ep), logits, s);
   if (e != hipSuccess) return e;
   if (is_fp8(c) && xq && xq_scales)
     e = launch_quant_x_fp8(static_cast<const uint16_t*>(x), static_cast<uint8_t*>(xq), xq_scales,
@@ -244,7 +246,7 @@ hipError_t do_expert_ffn(const moe_config_t* c, const void* xa, const float* xs,
   g.out_scales = is_fp8(c) ? at<float>(ws, L.h_scales) : nullptr;
   // an expert whose rows fit one tile streams its weights past the caches
   g.b_stream = 1;
-  e = launch_grouped_gemm(c->expert_dtype, kEpiSwiglu, bm, false, g, max_tiles, s);
+  e = launch_grouped_gemm(c->expert_dtype, kEpiSwiglu, bm, g, max_tiles, s);
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_GATE_UP, s);
   if (e != hipSuccess) return e;
 
@@ -266,8 +268,9 @@ hipError_t do_expert_ffn(const moe_config_t* c, const void* xa, const float* xs,
   h.M = static_cast<int>(A);
   h.out = y;
   h.ldo = d * y_bytes(c);
+  h.out_f32 = y_bytes(c) == 4;
   h.b_stream = g.b_stream;
-  e = launch_grouped_gemm(c->expert_dtype, kEpiStore, bm, false, h, max_tiles, s);
+  e = launch_grouped_gemm(c->expert_dtype, kEpiStore, bm, h, max_tiles, s);
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_DOWN, s);
   return e;
 }
@@ -280,7 +283,8 @@ hipError_t do_combine(const moe_config_t* c, const void* xa, const float* xs, co
   const int wb = weight_bytes(c);
   const int bm = shared_bm(c);
   const int max_tiles = static_cast<int>((T + bm - 1) / bm);
-  hipError_t e;
+  hipError_t e = hipSuccess;
+  float* shared_out = nullptr;
   if (c->num_shared > 0) {
     GemmArgs g{};
     g.A = xa;
@@ -296,30 +300,31 @@ hipError_t do_combine(const moe_config_t* c, const void* xa, const float* xs, co
     g.out = at<uint8_t>(ws, L.hs);
     g.ldo = F * wb;
     g.out_scales = is_fp8(c) ? at<float>(ws, L.hs_scales) : nullptr;
-    e = launch_grouped_gemm(c->expert_dtype, kEpiSwiglu, bm, false, g, max_tiles, s);
+    e = launch_grouped_gemm(c->expert_dtype, kEpiSwiglu, bm, g, max_tiles, s);
+    if (e == hipSuccess) e = mark(ev, MOE_STAGE_SHARED_GATE_UP, s);
     if (e != hipSuccess) return e;
+    shared_out = at<float>(ws, L.so);
+    GemmArgs h{};
+    h.A = at<uint8_t>(ws, L.hs);
+    h.lda = F * wb;
+    h.a_bytes = T * h.lda;
+    h.a_scales = is_fp8(c) ? at<float>(ws, L.hs_scales) : nullptr;
+    h.B = w->ws_down;
+    h.ldb = F * wb;
+    h.b_scales = w->ws_down_scales;
+    h.K = static_cast<int>(F);
+    h.N = static_cast<int>(d);
+    h.M = static_cast<int>(T);
+    h.out = shared_out;
+    h.ldo = d * 4;
+    h.out_f32 = 1;
+    e = launch_grouped_gemm(c->expert_dtype, kEpiStore, bm, h, max_tiles, s);
+  } else {
+    e = mark(ev, MOE_STAGE_SHARED_GATE_UP, s);
   }
-  e = mark(ev, MOE_STAGE_SHARED_GATE_UP, s);
-  if (e != hipSuccess) return e;
-  GemmArgs h{};
-  h.A = at<uint8_t>(ws, L.hs);
-  h.lda = F * wb;
-  h.a_bytes = T * h.lda;
-  h.a_scales = is_fp8(c) ? at<float>(ws, L.hs_scales) : nullptr;
-  h.B = w->ws_down;
-  h.ldb = F * wb;
-  h.b_scales = w->ws_down_scales;
-  h.K = static_cast<int>(F);
-  h.N = static_cast<int>(d);
-  h.M = static_cast<int>(T);
-  h.out = out;
-  h.ldo = d * act_bytes(c);
-  h.y = y;
-  h.ldy = d * y_bytes(c);
-  h.inv_perm = inv;
-  h.topk_w = tw;
-  h.top_k = c->top_k;
-  e = launch_grouped_gemm(c->expert_dtype, kEpiCombine, bm, false, h, max_tiles, s);
+  if (e == hipSuccess)
+    e = launch_combine(y, y_bytes(c) == 4, inv, tw, c->top_k, shared_out, out,
+                       act_bytes(c) == 4, static_cast<int>(T), static_cast<int>(d), s);
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_COMBINE, s);
   return e;
 }

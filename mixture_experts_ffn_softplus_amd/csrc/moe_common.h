@@ -87,6 +87,23 @@ __device__ __forceinline__ i32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
                                                AUX);
 }
 
+// Stores through a buffer resource: bytes at or past the resource's end are dropped.
+__device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t r, uint32_t voff, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, static_cast<int>(voff), 0, 0);
+}
+__device__ __forceinline__ void buffer_store8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint2 v) {
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(i32x2{static_cast<int>(v.x), static_cast<int>(v.y)}, r,
+                                        static_cast<int>(voff), 0, 0);
+}
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(static_cast<int>(v), r, static_cast<int>(voff), 0, 0);
+}
+__device__ __forceinline__ uint2 pack_bf16x4(f32x4 v) {
+  return uint2{f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16),
+               f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16)};
+}
+
 // ----------------------------------------------------------------------------- LDS DMA
 // Buffer loads whose data goes straight to LDS: lane l's BYTES land at (lds + BYTES * l), the
 // base taken from M0.  Issued from inline asm on purpose: the compiler cannot tell which LDS
@@ -123,7 +140,37 @@ __device__ __forceinline__ void lds_dma(i32x4 rsrc, uint32_t lds, uint32_t voff,
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                  :: "s"(l), "v"(voff), "s"(rsrc), "s"(so) : "memory");
 }
-// Wait until at most N vector-memory operations of this wave are outstanding.
+// Scalar loads of wave-uniform data, for use inside a loop that keeps direct-to-LDS loads in
+// flight: they are counted by lgkmcnt, not vmcnt, so waiting for them never drains the vector
+// memory pipeline.  Each waits for its own data inside the asm block.
+__device__ __forceinline__ i32x4 scalar_load16(const void* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const int lo = uniform(static_cast<int>(static_cast<uint32_t>(a)));
+  const int hi = uniform(static_cast<int>(static_cast<uint32_t>(a >> 32)));
+  const uint64_t ua = (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+  i32x4 v;
+  asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ua) : "memory");
+  return v;
+}
+// Eight consecutive int32 at byte offset `off` of buffer `rsrc` (zeros past its end).
+__device__ __forceinline__ i32x8 scalar_buffer_load32(i32x4 rsrc, uint32_t off) {
+  rsrc = i32x4{uniform(rsrc[0]), uniform(rsrc[1]), uniform(rsrc[2]), uniform(rsrc[3])};
+  const int so = uniform(static_cast<int>(off));
+  i32x8 v;
+  asm volatile("s_buffer_load_dwordx8 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(rsrc), "s"(so) : "memory");
+  return v;
+}
+// Element `idx` (0..7, per lane) of eight wave-uniform values.
+__device__ __forceinline__ int select8(i32x8 v, int idx) {
+  int r = v[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) r = idx == i ? v[i] : r;
+  return r;
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.  The counter
+// retires loads and stores in issue order, so vmcnt(N) means every operation but the N most
+// recently issued is complete.
 template <int N>
 __device__ __forceinline__ void lds_dma_wait() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -154,6 +201,11 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
   return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// SiLU from the hardware exp2 and reciprocal (a few ulp of fp32; its result is rounded to bf16
+// or E4M3 next, or kept in fp32 well inside the fp32 tolerance).
+__device__ __forceinline__ float silu_fast(float z) {
+  const float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 }  // namespace moe

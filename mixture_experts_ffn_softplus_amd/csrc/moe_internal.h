@@ -10,6 +10,7 @@ namespace moe {
 
 // ---- router (route.hip)
 struct RouteArgs {
+  const float* logit_bias;   // [E] added to the logits, or null
   const float* select_bias;  // [E] or null
   int32_t* ids;              // [T, k]
   float* weights;            // [T, k]
@@ -18,7 +19,8 @@ struct RouteArgs {
   float gamma;
 };
 enum RouterKind { kRouterF32 = 0, kRouterBF16 = 1, kRouterBF16HiLo = 2 };
-// Scoring + top-k of fp32 logits rows `ld` apart; copy: optional [T, E] copy of the logits.
+// Scoring + top-k of fp32 logits rows `ld` apart (plus logit_bias); copy: optional [T, E]
+// copy of the biased logits.
 hipError_t launch_topk(const RouteArgs& a, const float* logits, int ld, float* copy,
                        hipStream_t s);
 hipError_t launch_quant_x_fp8(const uint16_t* x, uint8_t* xq, float* scales, int T, int d,
@@ -33,7 +35,7 @@ hipError_t launch_tile_list(const int32_t* offsets, int E, int bm, int4* tiles,
                             int32_t* tiles_count, hipStream_t s);
 
 // ---- grouped GEMMs (gemm.hip)
-enum Epilogue { kEpiSwiglu = 0, kEpiStore = 1, kEpiCombine = 2 };
+enum Epilogue { kEpiSwiglu = 0, kEpiStore = 1 };
 
 struct GemmArgs {
   // A: activations, K-contiguous rows
@@ -58,23 +60,23 @@ struct GemmArgs {
   void* out;
   int64_t ldo;                // bytes per output row
   float* out_scales;          // FP8 h: [rows, out_cols/128]
-  // combine epilogue
-  const void* y;              // y_perm [T*k, N]
-  int64_t ldy;                // bytes per y row
-  const int32_t* inv_perm;
-  const float* topk_w;
-  int top_k;
-  // store epilogue: bias added to output column n < bias_cols (router logit bias)
-  const float* col_bias;
-  int bias_cols;
+  int out_f32;                // store epilogue: fp32 rows (else bf16)
   // A rows repeat every a_steps K-steps when > 0 (0: no repeat)
   int a_steps;
 };
 
-// dtype: MOE_F32 / MOE_BF16 / MOE_FP8_E4M3 (operands); out_f32: output rows fp32.
+// dtype: MOE_F32 / MOE_BF16 / MOE_FP8_E4M3 (operands).  max_tiles: upper bound of the device
+// tile count (grouped) for sizing the persistent grid.
 int gemm_bm(int dtype, int epi, int avg_rows);
-hipError_t launch_grouped_gemm(int dtype, int epi, int bm, bool out_f32, const GemmArgs& a,
-                               int max_tiles, hipStream_t s);
+hipError_t launch_grouped_gemm(int dtype, int epi, int bm, const GemmArgs& a, int max_tiles,
+                               hipStream_t s);
+
+// ---- un-permute and weighted combine (combine.hip)
+// out[t] = base[t] + sum_j w[t*k+j] * y[inv[t*k+j]] over d columns; y rows fp32 (y_f32) or
+// bf16, base fp32 [T, d] or null, out fp32 (out_f32) or bf16.
+hipError_t launch_combine(const void* y, bool y_f32, const int32_t* inv, const float* w, int k,
+                          const float* base, void* out, bool out_f32, int T, int d,
+                          hipStream_t s);
 
 // ---- packing (pack.hip)
 // Packed gate/up of one group: [2F, K] K-contiguous, rows in blocks of 16 alternating

@@ -42,7 +42,7 @@ __device__ void topk_row(const float* row, int t, const RouteArgs& a) {
     key[i] = -INFINITY;
     val[i] = 0.0f;
     if (e < a.E) {
-      float lg = row[e];
+      const float lg = a.logit_bias ? __fadd_rn(row[e], a.logit_bias[e]) : row[e];
       if (a.score == MOE_SCORE_SOFTMAX) {
         key[i] = lg;
         val[i] = lg;
@@ -111,15 +111,18 @@ __device__ void topk_row(const float* row, int t, const RouteArgs& a) {
   }
 }
 
-// One wave per token.  `logits` rows are `ld` floats apart; when `copy` is non-null the E
-// valid logits of each row are also written there as [T, E].
+// One wave per token.  `logits` rows are `ld` floats apart; a.logit_bias (if any) is added to
+// each (one fp32 add, the last step of the logits); when `copy` is non-null the E finished
+// logits of each row are also written there as [T, E].
 __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a, const float* __restrict__ logits,
                                                    int ld, float* __restrict__ copy) {
   int t = blockIdx.x * 4 + threadIdx.x / kWave;
   if (t >= a.T) return;  // whole waves leave together
   const float* row = logits + static_cast<size_t>(t) * ld;
   if (copy)
-    for (int e = lane_id(); e < a.E; e += kWave) copy[static_cast<size_t>(t) * a.E + e] = row[e];
+    for (int e = lane_id(); e < a.E; e += kWave)
+      copy[static_cast<size_t>(t) * a.E + e] =
+          a.logit_bias ? __fadd_rn(row[e], a.logit_bias[e]) : row[e];
   topk_row(row, t, a);
 }
 
