@@ -41,11 +41,15 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
       float wj[kCombineBatch];
 #pragma unroll
       for (int u = 0; u < kCombineBatch; ++u) {
-        const int j = j0 + u < k ? j0 + u : k - 1;  // a repeated row with weight 0 past the end
-        wj[u] = j0 + u < k ? wt[j] : 0.0f;
-        const i32x4* src = reinterpret_cast<const i32x4*>(y + rows[j] * ldy + c * 8 * ysz);
-        raw[u][0] = src[0];
-        if constexpr (Y_F32) raw[u][Y_F32 ? 1 : 0] = src[1];
+        wj[u] = 0.0f;
+        raw[u][0] = i32x4{0, 0, 0, 0};
+        if constexpr (Y_F32) raw[u][Y_F32 ? 1 : 0] = i32x4{0, 0, 0, 0};
+        if (j0 + u < k) {  // uniform: k is the same for the whole grid
+          wj[u] = wt[j0 + u];
+          const i32x4* src = reinterpret_cast<const i32x4*>(y + rows[j0 + u] * ldy + c * 8 * ysz);
+          raw[u][0] = src[0];
+          if constexpr (Y_F32) raw[u][Y_F32 ? 1 : 0] = src[1];
+        }
       }
 #pragma unroll
       for (int u = 0; u < kCombineBatch; ++u) {

@@ -452,7 +452,8 @@ void grouped_gemm_kernel(GemmArgs a) {
       const int hc0 = g.n0 / 2 + wn * HP * 16;  // first h column of this wave
       if constexpr (S::kFp8) {
         // one 128-value group per row and tile: scale = max|h| / 448, codes = E4M3(h / scale).
-        // Row maxima: over this wave's columns (lanes sharing kq), then over the WN waves.
+        // Row maxima: over this wave's columns (the 16 lanes sharing kq), then over the WN
+        // waves through LDS.
         float* amax = reinterpret_cast<float*>(smem + S::MAIN);
 #pragma unroll
         for (int i = 0; i < S::FM; ++i)
@@ -461,37 +462,27 @@ void grouped_gemm_kernel(GemmArgs a) {
             float m = 0.0f;
 #pragma unroll
             for (int p = 0; p < HP; ++p) m = fmaxf(m, fabsf(hv[i][p][e]));
-#pragma unroll
-            for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+            m = row16_max(m);
             if (lr == 0) amax[(wm * S::TM + i * 16 + 4 * kq + e) * S::WN + wn] = m;
           }
         __syncthreads();
         const int groups = (a.N / 2) / 128;
         const int grp = g.n0 / BN;
-        uint8_t* stage_b = reinterpret_cast<uint8_t*>(stage);
 #pragma unroll
         for (int i = 0; i < S::FM; ++i) {
-          float inv[4];
+          // staged layout: this lane holds 4 consecutive h of row `row`
+          const int row = wm * S::TM + i * 16 + srow;
+          float m = 0.0f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = wm * S::TM + i * 16 + 4 * kq + e;
-            float m = 0.0f;
-#pragma unroll
-            for (int w2 = 0; w2 < S::WN; ++w2) m = fmaxf(m, amax[r * S::WN + w2]);
-            const float sc = m > 0.0f ? m / 448.0f : 1.0f;
-            inv[e] = __builtin_amdgcn_rcpf(sc);
-            if (wn == 0 && lr == 0 && r < g.rows)
-              a.out_scales[static_cast<int64_t>(g.m0 + r) * groups + grp] = sc;
-          }
+          for (int w2 = 0; w2 < S::WN; ++w2) m = fmaxf(m, amax[row * S::WN + w2]);
+          const float sc = m > 0.0f ? m / 448.0f : 1.0f;
+          const float inv = __builtin_amdgcn_rcpf(sc);
+          if (wn == 0 && (l & 3) == 0 && row < g.rows)
+            a.out_scales[static_cast<int64_t>(g.m0 + row) * groups + grp] = sc;
 #pragma unroll
           for (int p = 0; p < HP; ++p) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              stage_b[(4 * kq + e) * kEpiPitch * 4 + lr] =
-                  static_cast<uint8_t>(f32_to_e4m3(hv[i][p][e] * inv[e]));
-            const uint32_t codes =
-                *reinterpret_cast<const uint32_t*>(stage_b + srow * kEpiPitch * 4 + scol);
-            const int row = wm * S::TM + i * 16 + srow;
+            const f32x4 v = stage_block(hv[i][p]);
+            const uint32_t codes = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
             buffer_store4(orsrc, static_cast<uint32_t>(row * a.ldo + hc0 + p * 16 + scol), codes);
           }
         }
@@ -635,7 +626,12 @@ static hipError_t launch_dt(int bm, const GemmArgs& a, int max_tiles, hipStream_
   if constexpr (DT == MOE_F32) {
     return launch_one<DT, 32, 128, EPI, G>(a, max_tiles, s);
   } else if constexpr (DT == MOE_FP8_E4M3) {
-    return launch_one<DT, 128, (EPI == kEpiSwiglu ? 256 : 128), EPI, G>(a, max_tiles, s);
+    // 8 waves, two per SIMD: one wave's promotion and loads overlap the other's MFMAs.  The
+    // SwiGLU output (N = 2 d_ff, d_ff a multiple of 128) always takes the wide tile.
+    if constexpr (EPI == kEpiSwiglu) return launch_one<DT, 128, 256, EPI, G>(a, max_tiles, s);
+    else
+      return a.N % 256 == 0 ? launch_one<DT, 128, 256, EPI, G>(a, max_tiles, s)
+                            : launch_one<DT, 128, 128, EPI, G>(a, max_tiles, s);
   } else {
     switch (bm) {
       case 16: return launch_one<DT, 16, 128, EPI, G>(a, max_tiles, s);

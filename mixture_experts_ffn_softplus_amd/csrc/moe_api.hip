@@ -24,8 +24,10 @@ int act_bytes(const moe_config_t* c) { return c->act_dtype == MOE_F32 ? 4 : 2; }
 // (after h and the output) to a budget the output rounding alone half fills.
 int y_bytes(const moe_config_t* c) { return c->expert_dtype == MOE_FP8_E4M3 ? 2 : 4; }
 
-// Router columns padded to the GEMM's 128-wide N tiles.
-int e_pad(const moe_config_t* c) { return (c->num_experts + 127) / 128 * 128; }
+// Router columns padded to the GEMM's N tiles: 128 for small E, else 256 (the wide 8-wave tile).
+int e_pad(const moe_config_t* c) {
+  return c->num_experts <= 128 ? 128 : (c->num_experts + 255) / 256 * 256;
+}
 int64_t assignments(const moe_config_t* c) {
   return static_cast<int64_t>(c->num_tokens) * c->top_k;
 }
@@ -39,11 +41,14 @@ int router_kind(const moe_config_t* c) {
   return kRouterBF16HiLo;
 }
 
-// Row tile of the router GEMM: the largest that still gives every CU a tile.
+// Row tile of the router GEMM: the wide 128 x 256 tile when it still gives every CU one, else
+// the largest 128-column tile that does.
 int router_bm(const moe_config_t* c) {
+  const int64_t T = c->num_tokens;
+  if (e_pad(c) % 256 == 0 && (T + 127) / 128 * (e_pad(c) / 256) >= 256) return 128;
   const int64_t nt = e_pad(c) / 128;
-  for (int bm : {128, 64, 32})
-    if ((c->num_tokens + bm - 1) / bm * nt >= 256) return bm;
+  for (int bm : {64, 32})
+    if ((T + bm - 1) / bm * nt >= 256) return bm;
   return 16;
 }
 

@@ -46,6 +46,19 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float r) {
   return sign | (e << 3) | m;
 }
 
+// Four E4M3FN codes (byte i from value i) by the hardware conversion (round to nearest even,
+// the same codes as f32_to_e4m3 for |r| <= 448); inputs are clamped to +-448 first.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const float lim = 448.0f;
+  a = fminf(fmaxf(a, -lim), lim);
+  b = fminf(fmaxf(b, -lim), lim);
+  c = fminf(fmaxf(c, -lim), lim);
+  d = fminf(fmaxf(d, -lim), lim);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return static_cast<uint32_t>(r);
+}
+
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   uint32_t e = (c >> 3) & 15u, m = c & 7u;
   float mag = e == 0 ? static_cast<float>(m) * 0.001953125f
@@ -189,6 +202,16 @@ __device__ __forceinline__ float wave_max(float v) {
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Maximum over each row of 16 lanes (lanes 16q .. 16q+15), by DPP lane permutes: quad swaps,
+// then the half-row and row mirrors.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
   return v;
 }
 

@@ -147,7 +147,7 @@ def test_packed_sizes():
     assert api.moe_packed_size(c, api.PACK_ROUTER) == 512 * d * 2
     q = PRESETS["fp8_block"]
     assert api.moe_packed_size(q, api.PACK_GATE_UP) == 896 * 2 * 512 * 4096
-    assert api.moe_packed_size(q, api.PACK_ROUTER) == 896 * 4096 * 4      # bf16 hi + lo planes
+    assert api.moe_packed_size(q, api.PACK_ROUTER) == 1024 * 4096 * 4     # bf16 hi + lo planes, 256-padded
     assert api.moe_packed_size(q, api.PACK_DOWN_SCALES) == 896 * (4096 // 16) * (512 // 128) * 4
     t = PRESETS["tiny_fp32"]
     assert api.moe_packed_size(t, api.PACK_SHARED_DOWN) == 256 * 256 * 4
