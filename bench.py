@@ -195,26 +195,22 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
+    # The timed region: the library records a HIP event on the stream at each stage boundary of
+    # every step (a marker each, no synchronisation), so the per-kernel durations below come
+    # from these same steps.
+    hip = HipEvents()
+    n_ev = api.NUM_STAGE_EVENTS
+    ev = [hip.create(n_ev) for _ in range(args.steps)]
     stream = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for _ in range(args.steps):
-        api.moe_forward(cfg, x, w, out, ws)
+    for i in range(args.steps):
+        api.moe_forward(cfg, x, w, out, ws, {"stage_events": ctypes.addressof(ev[i])})
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     log(f"timed {args.steps} steps: {ms:.4f} ms/step")
-
-    # per-stage times: the same steps again, with the library recording HIP events on the
-    # stream at each stage boundary
-    hip = HipEvents()
-    n_ev = api.NUM_STAGE_EVENTS
-    ev = [hip.create(n_ev) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        api.moe_forward(cfg, x, w, out, ws, {"stage_events": ctypes.addressof(ev[i])})
-    torch.cuda.synchronize()
     stage_ms = {}
     for s, name in enumerate(api.STAGES):
         stage_ms[name] = sum(hip.elapsed_ms(ev[i][s], ev[i][s + 1])
@@ -225,18 +221,27 @@ def main():
 
     step_bytes, step_flops, gu_bytes, gu_flops = algorithmic(cfg, touched)
     gu_ms = stage_ms["gate_up"]
-    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
     # HBM bytes per launch measured by rocprofv3 counters (profiles/), if the kernel sources
     # are unchanged since; otherwise null
     from mixture_experts_ffn_softplus_amd import profiling
     traffic = profiling.traffic_if_current(
         os.path.join(ROOT, "profiles", f"gate_up_gemm_{cfg.name}.txt"))
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+    # the binding roof of the dominant kernel: MFMA when its arithmetic intensity is above the
+    # ridge point of its dtype, else HBM
+    mfma_peak = MFMA_PEAK_TFLOPS[cfg.expert_dtype]
+    ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if gu_flops / gu_bytes > ridge:
+        achieved = gu_flops / (gu_ms * 1e-3) / 1e12
+        bound, peak, unit = "mfma", mfma_peak, "TFLOP/s"
+    else:
+        achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+        bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
+    roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak,
+                "unit": unit, "frac": round(achieved / peak, 4),
                 "traffic": None if traffic is None else int(traffic),
                 "kernel": "grouped_gemm_kernel (routed gate/up + SiLU*up)",
-                "kernel_ms": round(gu_ms, 5), "bytes_per_launch": gu_bytes}
-    mfma_peak = MFMA_PEAK_TFLOPS[cfg.expert_dtype]
+                "kernel_ms": round(gu_ms, 5), "bytes_per_launch": gu_bytes,
+                "flops_per_launch": gu_flops}
     step = {"bytes": step_bytes, "flops": step_flops,
             "GB_s": round(step_bytes / (ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
