@@ -110,6 +110,9 @@ constexpr int gemm_occupancy() {
   return per_cu < 1 ? 1 : per_cu > 2 ? 2 : per_cu;
 }
 
+// Row tiles of one expert swept together per N-tile (see geo in the kernel).
+constexpr int kGroupM = 8;
+
 // One output tile: its group, first row and row count (of the M space), first column, and
 // the number of row tiles its group has.
 struct TileGeo {
@@ -140,14 +143,32 @@ void grouped_gemm_kernel(GemmArgs a) {
   const int lo = xcd * q + (xcd < qr ? xcd : qr), span = q + (xcd < qr ? 1 : 0);
   const int n_my = wg < span ? (span - wg + per_xcd - 1) / per_xcd : 0;
   if (n_my == 0) return;
+  // Within one expert the workgroups of an XCD sweep each N-tile across a group of up to
+  // kGroupM row tiles before the next N-tile: co-running workgroups then share every weight
+  // tile kGroupM ways and every activation tile about 32 / kGroupM ways.  An expert occupies
+  // the logical range [NT * first, NT * (first + count)) whatever the order inside it.
   auto geo = [&](int t) {
     const int L = lo + wg + t * per_xcd;
-    const int tile = L / NT, nt = L - tile * NT;
     TileGeo g;
     if constexpr (GROUPED) {
-      const i32x4 ti = scalar_load16(a.tiles + tile);
-      g = TileGeo{ti[0], ti[1], ti[2], nt * BN, ti[3]};
+      const i32x4 t0 = scalar_load16(a.tiles + L / NT);  // some tile of L's expert
+      const int count = t0[3], first = L / NT - (t0[2] >> 8);
+      const int local = L - NT * first;
+      const int full = count / kGroupM, span_full = full * NT * kGroupM;
+      int m, nt;
+      if (local < span_full) {
+        const int grp = local / (NT * kGroupM), rem = local - grp * (NT * kGroupM);
+        nt = rem / kGroupM;
+        m = grp * kGroupM + (rem - nt * kGroupM);
+      } else {
+        const int r = count - full * kGroupM, rem = local - span_full;
+        nt = rem / r;
+        m = full * kGroupM + (rem - nt * r);
+      }
+      const i32x4 ti = scalar_load16(a.tiles + first + m);
+      g = TileGeo{ti[0], ti[1], ti[2] & 0xFF, nt * BN, count};
     } else {
+      const int tile = L / NT, nt = L - tile * NT;
       g = TileGeo{0, tile * BM, min(BM, a.M - tile * BM), nt * BN, 1};
     }
     return g;

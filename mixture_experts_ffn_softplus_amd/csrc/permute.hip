@@ -137,8 +137,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   }
 }
 
-// Device tile list of a grouped GEMM with row tile `bm`: tiles[i] = {group, first row, rows,
-// row tiles of that group},
+// Device tile list of a grouped GEMM with row tile `bm`: tiles[i] = {group, first row,
+// rows | (index of the tile within its group << 8), row tiles of that group},
 // groups in order, tiles of a group in row order; tiles_count[0] = number of tiles.  The
 // GEMM grid is sized for the worst case (ceil(T*k/bm) + E tiles) and reads the real count,
 // so per-expert counts never travel to the host.
@@ -160,7 +160,8 @@ __global__ __launch_bounds__(1024) void tile_list_kernel(const int32_t* __restri
     const int first = carry + block_exclusive_scan(nt, s_tot, &chunk_total);
     for (int i = 0; i < nt; ++i) {
       int m0 = r0 + i * bm;
-      tiles[first + i] = int4{e, m0, min(bm, r0 + n - m0), nt};  // w: tiles of expert e
+      // z: rows | index of the tile within its expert << 8;  w: tiles of expert e
+      tiles[first + i] = int4{e, m0, min(bm, r0 + n - m0) | (i << 8), nt};
     }
     carry += chunk_total;
   }
