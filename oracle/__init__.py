@@ -23,8 +23,9 @@ What it computes, and the passages it follows (archdiff.com comparison pages):
   E4M3FN, one fp32 scale (group max / 448) per 128-value group.
 * ``moe_tokens`` -- "Qwen3.5-397B-A17B vs Gemma 4 31B", component table,
   routed-experts row (SwiGLU experts) and shared-expert row (the shared
-  expert's output is added to the routed sum); blueprint shared-expert box
-  "1-2, always active".
+  expert's output is added to the routed sum; in the Qwen3.5 cell scaled
+  first by a per-token sigmoid gate of a learned vector); blueprint
+  shared-expert box "1-2, always active".
 
 Parity status per function is listed in the module docstrings of the tests
 that pin it (``tests/test_oracle_*.py``).
@@ -59,7 +60,8 @@ class _ExpertSet(ctypes.Structure):
 
 class _FfnCfg(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int), ("f", ctypes.c_int), ("k", ctypes.c_int),
-                ("f_shared", ctypes.c_int), ("quant", ctypes.c_int), ("block", ctypes.c_int)]
+                ("f_shared", ctypes.c_int), ("quant", ctypes.c_int), ("block", ctypes.c_int),
+                ("shared_gate", ctypes.POINTER(ctypes.c_double))]
 
 
 def lib():
@@ -256,14 +258,20 @@ class ExpertSet:
 
 
 def moe_tokens(x, ids, w, routed: ExpertSet, shared: ExpertSet, d, f, f_shared, quant=False,
-               block=128):
-    """Block output for the given token rows: shared SwiGLU(s) + sum_j w_j SwiGLU_{ids_j}."""
+               block=128, shared_gate=None):
+    """Block output for the given token rows: G * shared SwiGLU(s) + sum_j w_j SwiGLU_{ids_j},
+    G = sigmoid(x~ . shared_gate) when a gate vector [d] is given (exact values), else 1."""
     x = np.ascontiguousarray(x, dtype=np.float64)
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     w = np.ascontiguousarray(w, dtype=np.float64)
     n, k = ids.shape
     assert x.shape == (n, d)
-    cfg = _FfnCfg(d, f, k, f_shared, int(bool(quant)), block)
+    gate = None
+    if shared_gate is not None:
+        gate = np.ascontiguousarray(shared_gate, dtype=np.float64)
+        assert gate.shape == (d,)
+    cfg = _FfnCfg(d, f, k, f_shared, int(bool(quant)), block,
+                  None if gate is None else _ptr(gate, _dp))
     rs, keep_r = routed._c()
     if shared is not None and shared.n > 0:
         ss, keep_s = shared._c()

@@ -305,6 +305,7 @@ typedef struct {
   int f_shared;   /* shared-expert intermediate size */
   int quant;      /* 1: block-scaled FP8 activations (x and h) */
   int block;      /* quantisation group / block edge (128) */
+  const double* shared_gate;  /* [d] gate vector w of the shared output, or NULL (ungated) */
 } orc_ffn_cfg;
 
 static double orc_silu(double z) { return z / (1.0 + exp(-z)); }
@@ -344,14 +345,16 @@ static int orc_swiglu(const orc_ffn_cfg* c, int f, const orc_expert_set* s, int 
 }
 
 /* The block output for n tokens:
- * out[t] = sum_s SharedSwiGLU_s(x~[t]) + sum_j w[t,j] * SwiGLU_{ids[t,j]}(x~[t]),
+ * out[t] = G(t) * sum_s SharedSwiGLU_s(x~[t]) + sum_j w[t,j] * SwiGLU_{ids[t,j]}(x~[t]),
  * with x~ = x, or for FP8 the dequantised block-scaled x.  Shared experts are
- * always active and ungated (blueprint shared-expert box "1-2, always
- * active"; the DeepSeek-style reading of the Qwen3.5 vs Gemma 4 shared-expert
- * row); the routed sum is weighted by the router weights.  The residual add
- * outside the block is not part of it.  x is [n, d] fp64 (exact values of the
- * stored inputs), ids/w are [n, k], out is [n, d].  Returns 0, or -1 if a
- * needed expert was not supplied. */
+ * always active (blueprint shared-expert box "1-2, always active"); ungated,
+ * G = 1 (DeepSeek-style), or with a gate vector w_g the per-token sigmoid gate
+ * G(t) = sigma(x~[t] . w_g) of the Qwen3.5 cell of the shared-expert row of
+ * "Qwen3.5-397B-A17B vs Gemma 4 31B" (it scales the shared output before the
+ * routed sum is added).  The routed sum is weighted by the router weights.  The
+ * residual add outside the block is not part of it.  x is [n, d] fp64 (exact
+ * values of the stored inputs), ids/w are [n, k], out is [n, d].  Returns 0,
+ * or -1 if a needed expert was not supplied. */
 int orc_moe_tokens(const orc_ffn_cfg* c, int n, const double* x, const int32_t* ids,
                    const double* w, const orc_expert_set* routed, const orc_expert_set* shared,
                    double* out) {
@@ -368,9 +371,16 @@ int orc_moe_tokens(const orc_ffn_cfg* c, int n, const double* x, const int32_t* 
     memcpy(xr, x + (size_t)t * c->d, sizeof(double) * (size_t)c->d);
     if (c->quant) orc_quant_rows(xr, 1, c->d, c->block, NULL, NULL, xr);
     for (i = 0; i < c->d; ++i) y[i] = 0.0;
-    if (shared)
+    if (shared) {
+      double gate = 1.0;
+      if (c->shared_gate) {
+        double z = 0.0;
+        for (i = 0; i < c->d; ++i) z += xr[i] * c->shared_gate[i];
+        gate = 1.0 / (1.0 + exp(-z));
+      }
       for (s = 0; s < shared->n; ++s)
-        if (orc_swiglu(c, c->f_shared, shared, s, xr, 1.0, y, h, g, u)) bad = 1;
+        if (orc_swiglu(c, c->f_shared, shared, s, xr, gate, y, h, g, u)) bad = 1;
+    }
     for (j = 0; j < c->k; ++j) {
       int e = ids[(size_t)t * c->k + j];
       if (e < 0 || e >= routed->n) {

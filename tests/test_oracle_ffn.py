@@ -2,8 +2,10 @@
 
 Passages (archdiff.com): "Qwen3.5-397B-A17B vs Gemma 4 31B", component table, routed-experts
 row (SwiGLU experts) and shared-expert row (shared output added to the routed sum); blueprint
-shared-expert box "1-2, always active".  Shared experts are ungated here (the DeepSeek-style
-reading of that row).  Pins: a hand-computed one-token example, E = k = 1 reducing to a plain
+shared-expert box "1-2, always active".  Shared experts are ungated by default (the DeepSeek-style
+reading of that row); the Qwen3.5 cell's per-token sigmoid gate sigma(w . x) on the shared output
+is pinned by its closed forms (w = 0 halves the shared part, saturation gives the ungated or the
+routed-only output) and a per-token numpy check, for bf16 and block-scaled FP8 inputs.  Pins: a hand-computed one-token example, E = k = 1 reducing to a plain
 SwiGLU MLP (numpy matmul), a dense brute force (every expert on every token, then mask), the
 identity-like experts invariant, zero routed down-projections, and shared-expert
 concatenation; for block-scaled FP8, the same dense brute force with torch's float8 cast.
@@ -220,6 +222,45 @@ def test_fp8_dense_brute_force():
         m = np.array([w[t][list(ids[t]).index(e)] if e in ids[t] else 0.0 for t in range(6)])
         ref = ref + m[:, None] * ye
     assert np.max(np.abs(out - ref)) < 1e-10 * np.max(np.abs(ref))
+
+
+def _gate_case(quant):
+    rng = np.random.default_rng(21 if quant else 20)
+    T, d, f, fs, E, k = 9, 256, 128, 128, 5, 2
+    x = rng.standard_normal((T, d))
+    mk = lambda *s: (rng.standard_normal(s) / math.sqrt(s[0])).astype(np.float32)  # noqa: E731
+    routed = _set([mk(d, f) for _ in range(E)], [mk(d, f) for _ in range(E)],
+                  [mk(f, d) for _ in range(E)])
+    shared = _set([mk(d, fs)], [mk(d, fs)], [mk(fs, d)])
+    ids, w, _ = oracle.route(rng.standard_normal((T, E)), k)
+    run = lambda w_, gate=None: oracle.moe_tokens(  # noqa: E731
+        x, ids, w_, routed, shared, d, f, fs, quant=quant, shared_gate=gate)
+    ungated = run(w)
+    S = run(np.zeros_like(w))          # the shared experts alone
+    return x, rng, run, w, ungated, S, ungated - S
+
+
+@pytest.mark.parametrize("quant", [False, True])
+def test_gated_shared_expert_closed_forms(quant):
+    x, rng, run, w, ungated, S, R = _gate_case(quant)
+    d = x.shape[1]
+    # w_g = 0: sigma(0) = 1/2 exactly
+    assert np.max(np.abs(run(w, np.zeros(d)) - (0.5 * S + R))) < 1e-12
+    # a gate vector along one token's (quantised) input: sigma(+-40) saturates the gate to
+    # within 5e-18 of 1 (the ungated block) or of 0 (the routed sum alone)
+    xt = _torch_qdq_rows(x) if quant else x
+    for sign, want in ((1.0, ungated), (-1.0, R)):
+        g = sign * 40.0 * xt[0] / np.dot(xt[0], xt[0])
+        assert np.max(np.abs(run(w, g)[0] - want[0])) < 1e-12 * np.max(np.abs(want[0]))
+
+
+@pytest.mark.parametrize("quant", [False, True])
+def test_gated_shared_expert_per_token(quant):
+    x, rng, run, w, ungated, S, R = _gate_case(quant)
+    g = rng.standard_normal(x.shape[1]) / math.sqrt(x.shape[1])
+    xt = _torch_qdq_rows(x) if quant else x      # the gate reads what the experts read
+    G = 1.0 / (1.0 + np.exp(-(xt @ g)))
+    assert np.max(np.abs(run(w, g) - (G[:, None] * S + R))) < 1e-12
 
 
 def test_missing_expert_is_an_error():
