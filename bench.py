@@ -122,8 +122,9 @@ def cpu_baseline(cfg, inp, n_tokens, seed=0):
     routed = expert_set(cfg.num_experts, [parts.get(e) for e in range(cfg.num_experts)])
     log(f"cpu_baseline: {len(tok)} tokens use {len(used)} experts; running the oracle")
     t0 = time.perf_counter()
+    gate = None if inp.get("shared_gate") is None else exact64(inp["shared_gate"])
     oracle.moe_tokens(x, ids, w, routed, shared, cfg.d_model, cfg.d_ff, cfg.d_ff_shared,
-                      quant=quant)
+                      quant=quant, shared_gate=gate)
     t_cpu += time.perf_counter() - t0
     log(f"cpu_baseline: {t_cpu:.1f} s of oracle time")
     return {"value": len(tok) / t_cpu, "unit": "tokens/s", "cores": oracle.num_threads(),
@@ -172,7 +173,7 @@ def main():
     log(f"workload {cfg.describe()}")
     inp = synth.inputs(cfg, dev)
     pw = api.pack(cfg, inp["w_router"], inp["routed"], inp["shared"], inp["logit_bias"],
-                  inp["select_bias"])
+                  inp["select_bias"], shared_gate=inp["shared_gate"])
     torch.cuda.synchronize()
     inp["routed"] = None   # the packed copy is what the kernels read
     torch.cuda.empty_cache()

@@ -6,9 +6,10 @@
  *   -> weighted sum of the routed experts plus the always-active shared expert(s).
  * Passages: "Qwen3.5-397B-A17B vs DeepSeek-V4-Pro", component table, router row
  * (softmax top-k renormalised; sqrt-softplus with a selection-only bias, scaled
- * by 2.5) and blueprint diagram, Mixture-of-experts group (router "sigma /
- * sqrt-softplus, bias balancing", routed experts "top-6-22 of 256-896, SwiGLU",
- * shared expert "1-2, always active", training box "block-scaled FP8");
+ * by 2.5) and blueprint diagram, Mixture-of-experts group (a sigma or
+ * sqrt-softplus router balanced by a bias; 6 to 22 of 256 to 896 SwiGLU
+ * experts per token; one or two shared experts that every token uses; FP8
+ * with block scales in the training box);
  * "Qwen3.5-397B-A17B vs Gemma 4 31B", component table, routed-experts row
  * (SwiGLU experts) and shared-expert row (shared output added to the routed sum).
  *
@@ -80,6 +81,12 @@ typedef struct {
   int32_t expert_dtype;  /* expert weights; MOE_FP8_E4M3 also quantises x and h */
   int32_t router_dtype;  /* storage of W_r: MOE_F32 or MOE_BF16 */
   int32_t quant_block;   /* FP8 block edge; must be 128 */
+  int32_t shared_gate;   /* 1: the shared experts' output is multiplied per token by
+                            sigmoid(x~ . w_sg), a learned gate, before it joins the routed
+                            sum (shared-expert row, Qwen3.5 cell of "Qwen3.5-397B-A17B vs
+                            Gemma 4 31B"); x~ is what the shared experts read (the
+                            block-scaled x for FP8 experts).  0: ungated (the DeepSeek-style
+                            shared expert). */
 } moe_config_t;
 
 /* Weights in the caller's logical layout, for moe_pack_weights (device pointers).
@@ -120,8 +127,8 @@ enum {
  * pointers come from moe_pack_weights; logit_bias and select_bias are fp32
  * [E] or NULL.  logit_bias z is added to every logit before scoring;
  * select_bias b is added to the sigma / sqrt-softplus score only to choose
- * the experts ("a per-expert bias used only to pick the top 6", router row,
- * DeepSeek-V4-Pro cell) and never enters the weights. */
+ * the experts (router row, DeepSeek-V4-Pro cell: one bias per expert that
+ * takes part in the selection only) and never enters the weights. */
 typedef struct {
   const void* w_router;
   const float* logit_bias;
@@ -134,6 +141,8 @@ typedef struct {
   const float* ws_gate_up_scales;
   const void* ws_down;
   const float* ws_down_scales;
+  const void* ws_gate_vec;       /* [d] router_dtype gate vector w_sg; required when
+                                    shared_gate = 1 and num_shared > 0, else ignored */
 } moe_weights_t;
 
 /* Stage boundaries of moe_forward, for moe_debug_t.stage_events. */
@@ -185,9 +194,9 @@ MOE_API size_t moe_packed_size(const moe_config_t* cfg, int which);
 MOE_API moe_status_t moe_pack_weights(const moe_config_t* cfg, const moe_logical_weights_t* logical,
                               void* const* packed, hipStream_t stream);
 
-/* Router: l = x W_r + z, scores, top-k ids and weights ("a linear router scores
- * 512 experts; softmax, keep the top 10, renormalize", router row, Qwen3.5
- * cell; the sqrt-softplus / sigma variant of the DeepSeek-V4-Pro cell).
+/* Router: l = x W_r + z, scores, top-k ids and weights (router row, Qwen3.5
+ * cell: linear logits over 512 experts, softmax, the 10 largest kept and
+ * renormalised; the sqrt-softplus / sigma variant of the DeepSeek-V4-Pro cell).
  * x [T,d] act_dtype.  logits [T,E] fp32 or NULL.  topk_ids/topk_w [T,k]: slot j
  * holds the j-th largest key (softmax: the logit; sigma / sqrt-softplus: the
  * score rounded to fp32 plus select_bias in fp32), equal keys ordered by the
@@ -218,7 +227,7 @@ MOE_API moe_status_t moe_permute(const moe_config_t* cfg, const int32_t* topk_id
                          int32_t* expert_offsets, int32_t* perm_token, int32_t* inv_perm,
                          void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Routed SwiGLU experts ("SwiGLU experts", routed-experts row, Qwen3.5 cell):
+/* Routed SwiGLU experts (routed-experts row, Qwen3.5 cell):
  * for every row r of expert e, h = SiLU(x~ W_gate[e]) * (x~ W_up[e]) and
  * y_perm[r] = h W_down[e], with x~ = x[perm_token[r]] (FP8: the block-scaled
  * xq / xq_scales from moe_route, and h re-quantised per 128 values).
@@ -228,9 +237,11 @@ MOE_API moe_status_t moe_expert_ffn(const moe_config_t* cfg, const void* x_or_xq
                             const moe_weights_t* weights, void* y_perm, void* ws,
                             size_t ws_bytes, hipStream_t stream);
 
-/* Shared experts and weighted combine ("runs on every token ... added to the
- * routed sum", shared-expert row; "always active", blueprint):
- * out[t] = sum_s SwiGLU_s(x~[t]) + sum_j topk_w[t,j] * y_perm[inv_perm[t*k+j]].
+/* Shared experts and weighted combine (shared-expert row: the shared experts
+ * see every token and their output joins the routed sum; blueprint: always
+ * active):
+ * out[t] = G[t] * sum_s SwiGLU_s(x~[t]) + sum_j topk_w[t,j] * y_perm[inv_perm[t*k+j]],
+ * G[t] = sigmoid(x~[t] . ws_gate_vec) when cfg->shared_gate (else 1).
  * out [T,d] act_dtype.  The residual add outside the block is not included. */
 MOE_API moe_status_t moe_combine(const moe_config_t* cfg, const void* x_or_xq, const float* xq_scales,
                          const void* y_perm, const int32_t* inv_perm, const float* topk_w,

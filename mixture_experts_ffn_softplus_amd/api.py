@@ -33,7 +33,8 @@ class moe_config_t(ctypes.Structure):
                 ("d_ff_shared", ctypes.c_int32), ("score", ctypes.c_int32),
                 ("renormalize", ctypes.c_int32), ("routed_scale", ctypes.c_float),
                 ("act_dtype", ctypes.c_int32), ("expert_dtype", ctypes.c_int32),
-                ("router_dtype", ctypes.c_int32), ("quant_block", ctypes.c_int32)]
+                ("router_dtype", ctypes.c_int32), ("quant_block", ctypes.c_int32),
+                ("shared_gate", ctypes.c_int32)]
 
 
 _vp = ctypes.c_void_p
@@ -49,7 +50,8 @@ class moe_logical_weights_t(ctypes.Structure):
 class moe_weights_t(ctypes.Structure):
     _fields_ = [(n, _vp) for n in (
         "w_router", "logit_bias", "select_bias", "w_gate_up", "w_gate_up_scales", "w_down",
-        "w_down_scales", "ws_gate_up", "ws_gate_up_scales", "ws_down", "ws_down_scales")]
+        "w_down_scales", "ws_gate_up", "ws_gate_up_scales", "ws_down", "ws_down_scales",
+        "ws_gate_vec")]
 
 
 NUM_STAGE_EVENTS = 8
@@ -137,7 +139,7 @@ def config_struct(cfg: MoEConfig, **override) -> moe_config_t:
     c = moe_config_t(cfg.num_tokens, cfg.d_model, cfg.num_experts, cfg.top_k, cfg.d_ff,
                      cfg.num_shared, cfg.d_ff_shared, cfg.score, cfg.renormalize,
                      cfg.routed_scale, cfg.act_dtype, cfg.expert_dtype, cfg.router_dtype,
-                     cfg.quant_block)
+                     cfg.quant_block, cfg.shared_gate)
     for k, v in override.items():
         setattr(c, k, v)
     return c
@@ -229,11 +231,13 @@ def workspace(cfg: MoEConfig, device="cuda") -> torch.Tensor:
 class PackedWeights:
     """Packed device buffers of one layer plus the per-expert biases."""
 
-    def __init__(self, cfg: MoEConfig, buffers, logit_bias=None, select_bias=None):
+    def __init__(self, cfg: MoEConfig, buffers, logit_bias=None, select_bias=None,
+                 shared_gate=None):
         self.cfg = cfg
         self.buffers = buffers
         self.logit_bias = logit_bias
         self.select_bias = select_bias
+        self.shared_gate = shared_gate
 
     def struct(self) -> moe_weights_t:
         b = self.buffers
@@ -242,14 +246,14 @@ class PackedWeights:
             _p(b[PACK_GATE_UP]), _p(b[PACK_GATE_UP_SCALES]), _p(b[PACK_DOWN]),
             _p(b[PACK_DOWN_SCALES]), _p(b[PACK_SHARED_GATE_UP]),
             _p(b[PACK_SHARED_GATE_UP_SCALES]), _p(b[PACK_SHARED_DOWN]),
-            _p(b[PACK_SHARED_DOWN_SCALES]))
+            _p(b[PACK_SHARED_DOWN_SCALES]), _p(self.shared_gate))
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in self.buffers if t is not None)
 
 
 def pack(cfg: MoEConfig, w_router, routed: dict, shared: dict = None, logit_bias=None,
-         select_bias=None, stream=None) -> PackedWeights:
+         select_bias=None, stream=None, shared_gate=None) -> PackedWeights:
     """Allocate the packed buffers and fill them with moe_pack_weights."""
     dev = w_router.device
     bufs = []
@@ -263,4 +267,4 @@ def pack(cfg: MoEConfig, w_router, routed: dict, shared: dict = None, logit_bias
         _p(routed.get("down_scales")), _p(sh.get("gate")), _p(sh.get("up")), _p(sh.get("down")),
         _p(sh.get("gate_scales")), _p(sh.get("up_scales")), _p(sh.get("down_scales")))
     moe_pack_weights(cfg, lw, bufs, stream)
-    return PackedWeights(cfg, bufs, logit_bias, select_bias)
+    return PackedWeights(cfg, bufs, logit_bias, select_bias, shared_gate)

@@ -12,11 +12,15 @@ Sources for the shapes (archdiff.com comparison pages):
   7,168 from that page's residual-stream row.  Expert and shared widths, the
   shared count of 2 and the Zipf load skew are workload choices.
 * ``decode_bf16`` -- 256 experts, the low end of the blueprint's routed-experts
-  box "top-6-22 of 256-896"; 64 tokens, so the step streams expert weights.
+  box (6 to 22 of 256 to 896 experts); 64 tokens, so the step streams expert weights.
 * ``fp8_block`` -- 896 experts, top 22, the high end of that box; the
-  blueprint's "block-scaled FP8" training box for the number format.
+  blueprint's training box (FP8 with block scales) for the number format.
 * ``tiny_fp32`` -- a small fp32 layer that the oracle finishes in well under a
   second, used for parity at every step.
+* ``qwen_gated_bf16`` -- ``softmax_bf16`` with the Qwen3.5 shared expert as the
+  shared-expert row of "Qwen3.5-397B-A17B vs Gemma 4 31B" states it: its output
+  scaled by a per-token sigmoid gate of a learned d-vector before the routed sum
+  is added.
 """
 from dataclasses import dataclass, replace
 
@@ -46,6 +50,7 @@ class MoEConfig:
     seed: int = 0
     select_bias_range: float = 0.0   # b_e ~ U(-r, r) when r > 0 (selection-only bias)
     zipf_s: float = 0.0              # per-expert logit bias skewing load when > 0
+    shared_gate: int = 0             # 1: sigmoid(x . w_sg) scales the shared output (Qwen3.5)
 
     @property
     def assignments(self) -> int:
@@ -58,7 +63,8 @@ class MoEConfig:
         sc = {SOFTMAX: "softmax", SIGMOID: "sigmoid", SQRT_SOFTPLUS: "sqrt_softplus"}[self.score]
         return (f"{self.name}: T={self.num_tokens} d={self.d_model} E={self.num_experts} "
                 f"top-{self.top_k} d_ff={self.d_ff} shared={self.num_shared}x{self.d_ff_shared} "
-                f"{sc} experts={_DT_NAMES[self.expert_dtype]}")
+                f"{sc} experts={_DT_NAMES[self.expert_dtype]}"
+                + (" gated-shared" if self.shared_gate else ""))
 
 
 PRESETS = {
@@ -82,3 +88,5 @@ PRESETS = {
         num_shared=1, d_ff_shared=2048, score=SOFTMAX, renormalize=1, routed_scale=1.0,
         act_dtype=BF16, expert_dtype=FP8_E4M3, router_dtype=F32, seed=4),
 }
+PRESETS["qwen_gated_bf16"] = PRESETS["softmax_bf16"].with_(name="qwen_gated_bf16", shared_gate=1)
+

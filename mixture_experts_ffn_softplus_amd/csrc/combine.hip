@@ -5,6 +5,10 @@
 // and shared-expert rows of "Qwen3.5-397B-A17B vs Gemma 4 31B"; the block's equation of the
 // DeepSeek-V4 blueprint).  Pure streaming: one workgroup per token, each thread owning
 // 8-column chunks and keeping up to eight row loads of y in flight.
+//
+// Gated shared expert (shared-expert row, Qwen3.5 cell): the shared output is first scaled by
+// the token's sigmoid(x~ . w_sg), one dot product of length d per token reduced across the
+// workgroup before the streaming loop; x~ is the activation row the shared experts read.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -13,15 +17,80 @@ namespace moe {
 constexpr int kCombineThreads = 256;
 constexpr int kCombineBatch = 8;  // y rows loaded together
 
+struct CombineGate {
+  const uint8_t* vec;  // [d] fp32 or bf16, null: no gate
+  const uint8_t* x;    // [T, d] activations (fp32 / bf16 / E4M3 codes)
+  const float* xs;     // E4M3: [T, d/128] scales
+  int vec_f32, x_kind;
+};
+
+// Eight consecutive values of a row of bf16 (16 B) or fp32 (32 B) elements.
+template <bool F32>
+__device__ __forceinline__ void load8(const uint8_t* p, float* v) {
+  if constexpr (F32) {
+    const f32x4 a = reinterpret_cast<const f32x4*>(p)[0], b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[q] = a[q];
+      v[4 + q] = b[q];
+    }
+  } else {
+    const i32x4 r = *reinterpret_cast<const i32x4*>(p);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t bits = static_cast<uint32_t>(r[q]);
+      v[2 * q] = __uint_as_float(bits << 16);
+      v[2 * q + 1] = __uint_as_float(bits & 0xFFFF0000u);
+    }
+  }
+}
+
+// sigmoid(x~[t] . vec), reduced over the whole workgroup (every thread gets the value).
+__device__ float shared_gate(const CombineGate& g, int t, int d) {
+  __shared__ float part[kCombineThreads / kWave];
+  float z = 0.0f;
+  for (int c = threadIdx.x; c < d / 8; c += kCombineThreads) {
+    float xv[8], gv[8];
+    const int64_t i = static_cast<int64_t>(t) * d + c * 8;
+    if (g.x_kind == 0) {
+      load8<true>(g.x + i * 4, xv);
+    } else if (g.x_kind == 1) {
+      load8<false>(g.x + i * 2, xv);
+    } else {
+      const uint2 codes = *reinterpret_cast<const uint2*>(g.x + i);
+      const float sc = g.xs[static_cast<int64_t>(t) * (d / 128) + (c * 8) / 128];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        xv[q] = e4m3_to_f32((codes.x >> (8 * q)) & 0xFFu) * sc;
+        xv[4 + q] = e4m3_to_f32((codes.y >> (8 * q)) & 0xFFu) * sc;
+      }
+    }
+    if (g.vec_f32)
+      load8<true>(g.vec + c * 32, gv);
+    else
+      load8<false>(g.vec + c * 16, gv);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) z = fmaf(xv[q], gv[q], z);
+  }
+  z = wave_sum(z);
+  if (lane_id() == 0) part[threadIdx.x / kWave] = z;
+  __syncthreads();
+  z = 0.0f;
+#pragma unroll
+  for (int q = 0; q < kCombineThreads / kWave; ++q) z += part[q];
+  return 1.0f / (1.0f + expf(-z));
+}
+
 template <bool Y_F32, bool OUT_F32>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const uint8_t* __restrict__ y, const int32_t* __restrict__ inv, const float* __restrict__ w,
-    int k, const float* __restrict__ base, uint8_t* __restrict__ out, int d) {
+    int k, const float* __restrict__ base, CombineGate gate, uint8_t* __restrict__ out, int d) {
   constexpr int ysz = Y_F32 ? 4 : 2, osz = OUT_F32 ? 4 : 2;
   const int t = blockIdx.x;
   const int64_t ldy = static_cast<int64_t>(d) * ysz;
   const int32_t* rows = inv + static_cast<int64_t>(t) * k;
   const float* wt = w + static_cast<int64_t>(t) * k;
+  const float G = gate.vec ? shared_gate(gate, t, d) : 1.0f;  // uniform branch
   for (int c = threadIdx.x; c < d / 8; c += kCombineThreads) {
     float v[8];
     if (base) {
@@ -29,8 +98,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
       const f32x4 b0 = b[0], b1 = b[1];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        v[q] = b0[q];
-        v[4 + q] = b1[q];
+        v[q] = G * b0[q];
+        v[4 + q] = G * b1[q];
       }
     } else {
 #pragma unroll
@@ -84,21 +153,33 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   }
 }
 
-hipError_t launch_combine(const void* y, bool y_f32, const int32_t* inv, const float* w, int k,
-                          const float* base, void* out, bool out_f32, int T, int d,
-                          hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  const uint8_t* yb = static_cast<const uint8_t*>(y);
-  uint8_t* ob = static_cast<uint8_t*>(out);
-  const dim3 grid(T), block(kCombineThreads);
-  if (y_f32 && out_f32)
-    hipLaunchKernelGGL((combine_kernel<true, true>), grid, block, 0, s, yb, inv, w, k, base, ob, d);
-  else if (y_f32)
-    hipLaunchKernelGGL((combine_kernel<true, false>), grid, block, 0, s, yb, inv, w, k, base, ob, d);
-  else if (out_f32)
-    hipLaunchKernelGGL((combine_kernel<false, true>), grid, block, 0, s, yb, inv, w, k, base, ob, d);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  const uint8_t* yb = static_cast<const uint8_t*>(a.y);
+  uint8_t* ob = static_cast<uint8_t*>(a.out);
+  CombineGate g{};
+  if (a.gate_vec && a.base) {
+    if (!a.x || a.x_kind < 0 || a.x_kind > 2 || (a.x_kind == 2 && !a.x_scales))
+      return hipErrorInvalidValue;
+    g.vec = static_cast<const uint8_t*>(a.gate_vec);
+    g.x = static_cast<const uint8_t*>(a.x);
+    g.xs = a.x_scales;
+    g.vec_f32 = a.gate_f32;
+    g.x_kind = a.x_kind;
+  }
+  const dim3 grid(a.T), block(kCombineThreads);
+  if (a.y_f32 && a.out_f32)
+    hipLaunchKernelGGL((combine_kernel<true, true>), grid, block, 0, s, yb, a.inv, a.w, a.k,
+                       a.base, g, ob, a.d);
+  else if (a.y_f32)
+    hipLaunchKernelGGL((combine_kernel<true, false>), grid, block, 0, s, yb, a.inv, a.w, a.k,
+                       a.base, g, ob, a.d);
+  else if (a.out_f32)
+    hipLaunchKernelGGL((combine_kernel<false, true>), grid, block, 0, s, yb, a.inv, a.w, a.k,
+                       a.base, g, ob, a.d);
   else
-    hipLaunchKernelGGL((combine_kernel<false, false>), grid, block, 0, s, yb, inv, w, k, base, ob, d);
+    hipLaunchKernelGGL((combine_kernel<false, false>), grid, block, 0, s, yb, a.inv, a.w, a.k,
+                       a.base, g, ob, a.d);
   return hipGetLastError();
 }
 

@@ -4,7 +4,7 @@
 // stored [N, K] K-contiguous (the packed weight layout), followed by one of:
 //   kEpiSwiglu  -- h = SiLU(gate) * up: B interleaves gate and up columns in blocks of 16
 //                  packed rows, so each wave's accumulators hold matching gate/up columns and
-//                  h is formed in registers ("SwiGLU experts", routed-experts row of
+//                  h is formed in registers (SwiGLU experts, routed-experts row of
 //                  "Qwen3.5-397B-A17B vs Gemma 4 31B"); FP8 re-quantises h per 128 values;
 //   kEpiStore   -- rows stored as they are (y_perm, the shared experts' output, router logits).
 //

@@ -75,6 +75,7 @@ moe_status_t check_config(const moe_config_t* c) {
   if (c->score < MOE_SCORE_SOFTMAX || c->score > MOE_SCORE_SQRT_SOFTPLUS)
     return MOE_ERR_INVALID_ARGUMENT;
   if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->shared_gate != 0 && c->shared_gate != 1) return MOE_ERR_INVALID_ARGUMENT;
   if (!isfinite(c->routed_scale)) return MOE_ERR_INVALID_ARGUMENT;
   const int dts[3] = {c->act_dtype, c->expert_dtype, c->router_dtype};
   for (int v : dts)
@@ -153,6 +154,7 @@ moe_status_t check_weights(const moe_config_t* c, const moe_weights_t* w, bool r
     return MOE_ERR_INVALID_ARGUMENT;
   if (shared && c->num_shared > 0) {
     if (!w->ws_gate_up || !w->ws_down) return MOE_ERR_INVALID_ARGUMENT;
+    if (c->shared_gate && !w->ws_gate_vec) return MOE_ERR_INVALID_ARGUMENT;
     if (is_fp8(c) && (!w->ws_gate_up_scales || !w->ws_down_scales))
       return MOE_ERR_INVALID_ARGUMENT;
   }
@@ -327,9 +329,28 @@ hipError_t do_combine(const moe_config_t* c, const void* xa, const float* xs, co
   } else {
     e = mark(ev, MOE_STAGE_SHARED_GATE_UP, s);
   }
-  if (e == hipSuccess)
-    e = launch_combine(y, y_bytes(c) == 4, inv, tw, c->top_k, shared_out, out,
-                       act_bytes(c) == 4, static_cast<int>(T), static_cast<int>(d), s);
+  if (e == hipSuccess) {
+    CombineArgs ca{};
+    ca.y = y;
+    ca.y_f32 = y_bytes(c) == 4;
+    ca.inv = inv;
+    ca.w = tw;
+    ca.k = c->top_k;
+    ca.base = shared_out;
+    if (shared_out && c->shared_gate) {
+      // the gate reads what the shared experts read: x, or the block-scaled FP8 x~
+      ca.gate_vec = w->ws_gate_vec;
+      ca.gate_f32 = c->router_dtype == MOE_F32;
+      ca.x = xa;
+      ca.x_kind = is_fp8(c) ? 2 : act_bytes(c) == 4 ? 0 : 1;
+      ca.x_scales = xs;
+    }
+    ca.out = out;
+    ca.out_f32 = act_bytes(c) == 4;
+    ca.T = static_cast<int>(T);
+    ca.d = static_cast<int>(d);
+    e = launch_combine(ca, s);
+  }
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_COMBINE, s);
   return e;
 }

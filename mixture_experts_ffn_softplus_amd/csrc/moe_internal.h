@@ -72,11 +72,27 @@ hipError_t launch_grouped_gemm(int dtype, int epi, int bm, const GemmArgs& a, in
                                hipStream_t s);
 
 // ---- un-permute and weighted combine (combine.hip)
-// out[t] = base[t] + sum_j w[t*k+j] * y[inv[t*k+j]] over d columns; y rows fp32 (y_f32) or
-// bf16, base fp32 [T, d] or null, out fp32 (out_f32) or bf16.
-hipError_t launch_combine(const void* y, bool y_f32, const int32_t* inv, const float* w, int k,
-                          const float* base, void* out, bool out_f32, int T, int d,
-                          hipStream_t s);
+// out[t] = G[t] * base[t] + sum_j w[t*k+j] * y[inv[t*k+j]] over d columns; y rows fp32 (y_f32)
+// or bf16, base fp32 [T, d] or null, out fp32 (out_f32) or bf16.  G = 1, or with gate_vec
+// G[t] = sigmoid(x~[t] . gate_vec): x~ fp32 / bf16 (x_kind 0 / 1) or E4M3 codes times their
+// per-128 scales (x_kind 2); gate_vec fp32 or bf16 (gate_f32).
+struct CombineArgs {
+  const void* y;
+  bool y_f32;
+  const int32_t* inv;
+  const float* w;
+  int k;
+  const float* base;
+  const void* gate_vec;
+  bool gate_f32;
+  const void* x;
+  int x_kind;
+  const float* x_scales;
+  void* out;
+  bool out_f32;
+  int T, d;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
 // ---- packing (pack.hip)
 // Packed gate/up of one group: [2F, K] K-contiguous, rows in blocks of 16 alternating

@@ -1,6 +1,6 @@
 // permute.hip -- (token, slot) assignments into expert-contiguous order, stable in token order.
 //
-// The pages select routed experts per token ("keep the top 10", router row of
+// The pages select routed experts per token (the k largest, router row of
 // "Qwen3.5-397B-A17B vs DeepSeek-V4-Pro"), which the grouped expert GEMMs need as contiguous
 // per-expert row ranges.  A counting sort, deterministic by construction, over chunks of 256
 // consecutive assignments:

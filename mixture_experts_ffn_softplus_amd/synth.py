@@ -18,6 +18,8 @@ Recipe (all logical layouts row-major):
   torch.  The quantised weights are the inputs; how they were made is not part
   of the block.
 * Selection-only bias b_e ~ U(-r, r) (fp32) when the workload asks for one.
+* Shared-expert gate vector w_sg [d] ~ N(0, 1/d), stored in the router's dtype,
+  when the workload gates its shared experts.
 * Load skew: logit bias z_e = ln p_e - mean(ln p), p_e proportional to
   (e + 1)^-s, expert 0 hottest (fp32).
 
@@ -33,6 +35,7 @@ from .configs import BF16, F32, FP8_E4M3, MoEConfig
 TAG_X, TAG_ROUTER, TAG_SELECT_BIAS = 1, 2, 3
 TAG_GATE, TAG_UP, TAG_DOWN = 4, 5, 6
 TAG_SGATE, TAG_SUP, TAG_SDOWN = 7, 8, 9
+TAG_SHARED_GATE_VEC = 10
 
 _MASK64 = (1 << 64) - 1
 
@@ -159,8 +162,18 @@ def shared_experts(cfg: MoEConfig, device="cpu"):
     return _stack(cfg, True, cfg.num_shared, device)
 
 
+def shared_gate_vector(cfg: MoEConfig, device="cpu"):
+    """w_sg [d] in the router's dtype, or None when the shared experts are ungated."""
+    if not cfg.shared_gate or cfg.num_shared == 0:
+        return None
+    d = cfg.d_model
+    return _store(_normal((d,), 1.0 / math.sqrt(d), device, cfg.seed, TAG_SHARED_GATE_VEC),
+                  cfg.router_dtype)
+
+
 def inputs(cfg: MoEConfig, device="cpu"):
     """Every input of the block, logical layouts."""
     wr, z, b = router(cfg, device)
     return {"x": tokens(cfg, device), "w_router": wr, "logit_bias": z, "select_bias": b,
-            "routed": routed_experts(cfg, device), "shared": shared_experts(cfg, device)}
+            "routed": routed_experts(cfg, device), "shared": shared_experts(cfg, device),
+            "shared_gate": shared_gate_vector(cfg, device)}

@@ -13,13 +13,13 @@ What it computes, and the passages it follows (archdiff.com comparison pages):
 * ``route`` -- same row: softmax, top-k, renormalise, no selection bias
   (Qwen3.5 cell); sqrt-softplus affinities with a selection-only per-expert
   bias, selected scores normalised and scaled by 2.5 (DeepSeek-V4-Pro cell);
-  the blueprint router box "sigma / sqrt-softplus, bias balancing" for the
+  the blueprint router box (sigma or sqrt-softplus, balanced by a bias) for the
   sigmoid score.  Ties at the top-k boundary go to the lower expert index
   (the pages are silent; this is the reading taken).
 * ``permute`` -- expert-contiguous order of the (token, slot) assignments,
   stable in token order (a counting sort; the pages imply the grouping by
   selecting routed experts per token).
-* ``quant_rows`` / ``e4m3_*`` -- blueprint training box "block-scaled FP8":
+* ``quant_rows`` / ``e4m3_*`` -- blueprint training box (FP8 with block scales):
   E4M3FN, one fp32 scale (group max / 448) per 128-value group.
 * ``moe_tokens`` -- "Qwen3.5-397B-A17B vs Gemma 4 31B", component table,
   routed-experts row (SwiGLU experts) and shared-expert row (the shared

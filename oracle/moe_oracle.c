@@ -4,14 +4,14 @@
  * A plain, deliberately slow fp64 CPU implementation of the mixture-of-experts
  * FFN block, written from the archdiff.com architecture-comparison pages:
  *   - "Qwen3.5-397B-A17B vs DeepSeek-V4-Pro", component table, router row
- *     (Qwen3.5 cell: a linear router scores the experts, softmax, keep the
- *     top k, renormalise, no selection bias; DeepSeek-V4-Pro cell: sqrt-softplus
- *     affinities, a per-expert bias used only to pick the top k, the selected
- *     scores normalised and scaled by 2.5),
- *   - the same page's blueprint diagram, Mixture-of-experts group (router box
- *     "sigma / sqrt-softplus, bias balancing"; routed experts "top-6-22 of
- *     256-896, SwiGLU"; shared expert "1-2, always active"; training box
- *     "block-scaled FP8"),
+ *     (Qwen3.5 cell: one linear map gives a logit per expert, then softmax,
+ *     the k largest kept and renormalised, no selection bias; DeepSeek-V4-Pro
+ *     cell: sqrt-softplus scores, a per-expert bias that only affects which k
+ *     are picked, the picked scores normalised and multiplied by 2.5),
+ *   - the same page's blueprint diagram, Mixture-of-experts group (router box:
+ *     sigma or sqrt-softplus scores balanced by a bias; routed experts: 6 to 22
+ *     of 256 to 896 SwiGLU experts; shared experts: one or two, used by every
+ *     token; training box: FP8 with block scales),
  *   - "Qwen3.5-397B-A17B vs Gemma 4 31B", component table, routed-experts row
  *     (SwiGLU experts) and shared-expert row (shared output added to the
  *     routed sum).
@@ -96,7 +96,7 @@ uint8_t orc_e4m3_encode(double v) {
 }
 
 /* Block-scaled FP8 quantisation of one group of n values (the diagram's
- * "block-scaled FP8"): the scale is the group's largest magnitude over 448,
+ * training box): the scale is the group's largest magnitude over 448,
  * held in fp32 (1 when the group is all zero); each value divided by that
  * scale, held in fp32, is rounded to E4M3FN.  Writes the codes, the scale and
  * the dequantised values q*s.  The fp64 division followed by one rounding to
@@ -164,8 +164,8 @@ void orc_router_logits(int T, int d, int E, const double* x, int wr_dtype, const
   }
 }
 
-/* Scores of the sigma-family router (blueprint router box "sigma /
- * sqrt-softplus"; DeepSeek-V4-Pro cell "sqrt-softplus affinities"). */
+/* Scores of the sigma-family router (blueprint router box: sigma or
+ * sqrt-softplus; DeepSeek-V4-Pro router cell: sqrt-softplus). */
 double orc_score(int score, double l) {
   if (score == ORC_SIGMOID) return 1.0 / (1.0 + exp(-l));
   /* softplus(l) = log(1 + e^l) = max(l, 0) + log1p(e^-|l|) */
@@ -181,10 +181,10 @@ double orc_score(int score, double l) {
  * the bias added in fp32, so that the key is one fixed fp32 number.
  * Order: key descending, equal keys broken by the lower expert index.
  *
- * Weights.  Softmax, renormalised (Qwen3.5 cell "softmax, keep the top 10,
- * renormalize"): softmax over the selected logits; not renormalised: the full
- * softmax probability.  sigma / sqrt-softplus (DeepSeek-V4-Pro cell "the
- * selected scores are normalized and scaled by 2.5"): the selected unbiased
+ * Weights.  Softmax, renormalised (Qwen3.5 router cell, k = 10 there):
+ * softmax over the selected logits; not renormalised: the full
+ * softmax probability.  sigma / sqrt-softplus (DeepSeek-V4-Pro router cell:
+ * picked scores normalised, then multiplied by 2.5): the selected unbiased
  * scores divided by their sum; not renormalised: the score itself.  Either way
  * the result is multiplied by gamma (2.5 in that cell, 1 for softmax).
  *
@@ -312,7 +312,7 @@ static double orc_silu(double z) { return z / (1.0 + exp(-z)); }
 
 /* One SwiGLU expert on one (already dequantised) token row xr[d]:
  * g = xr W_gate, u = xr W_up, h = SiLU(g) * u, (FP8: h re-quantised per group
- * of `block`), y += wgt * (h W_down).  "SwiGLU experts" (routed-experts row,
+ * of `block`), y += wgt * (h W_down).  SwiGLU experts (routed-experts row,
  * Qwen3.5 cell).  Returns -1 if the expert was not supplied. */
 static int orc_swiglu(const orc_ffn_cfg* c, int f, const orc_expert_set* s, int e,
                       const double* xr, double wgt, double* y, double* h, double* g,

@@ -17,7 +17,8 @@ class Layer:
         print(f"[layer] {cfg.describe()}", flush=True)
         self.inp = synth.inputs(cfg, device)
         self.pw = api.pack(cfg, self.inp["w_router"], self.inp["routed"], self.inp["shared"],
-                           self.inp["logit_bias"], self.inp["select_bias"])
+                           self.inp["logit_bias"], self.inp["select_bias"],
+                           shared_gate=self.inp["shared_gate"])
         torch.cuda.synchronize()
         if not keep_logical:
             self.inp["routed"] = None
@@ -79,6 +80,7 @@ def oracle_block(cfg: MoEConfig, inp: dict, tokens, ids, w, max_experts=64):
     if sh is not None:
         S = sh["gate"].shape[0]
         shared = _expert_set([_expert_host(sh, s) for s in range(S)], S, list(range(S)))
+    gate = None if inp.get("shared_gate") is None else exact64(inp["shared_gate"])
     out = np.empty((len(tokens), cfg.d_model))
     i = 0
     while i < len(tokens):
@@ -92,7 +94,8 @@ def oracle_block(cfg: MoEConfig, inp: dict, tokens, ids, w, max_experts=64):
         routed = _expert_set(parts, cfg.num_experts, used)
         out[i:j] = oracle.moe_tokens(x[i:j], ids[i:j], w[i:j], routed, shared, cfg.d_model,
                                      cfg.d_ff, cfg.d_ff_shared,
-                                     quant=cfg.expert_dtype == FP8_E4M3, block=cfg.quant_block)
+                                     quant=cfg.expert_dtype == FP8_E4M3, block=cfg.quant_block,
+                                     shared_gate=gate)
         i = j
     return out
 

@@ -104,7 +104,7 @@ def test_null_pointers_and_small_workspace():
     cfg = api.config_struct(PRESETS["tiny_fp32"])
     ws_need = api.moe_workspace_size(cfg)
     assert ws_need > 0
-    w_ok = api.moe_weights_t(*([8] * 11))
+    w_ok = api.moe_weights_t(*([8] * 12))
     cp = ctypes.byref(cfg)
     # NULL x / out / weights / ws
     assert L.moe_forward(cp, None, ctypes.byref(w_ok), 8, None, 8, ws_need, None) == 1
@@ -112,12 +112,22 @@ def test_null_pointers_and_small_workspace():
     assert L.moe_forward(cp, 8, None, 8, None, 8, ws_need, None) == 1
     assert L.moe_forward(cp, 8, ctypes.byref(w_ok), 8, None, None, ws_need, None) == 1
     # missing router / expert weights
-    w_bad = api.moe_weights_t(*([8] * 11))
+    w_bad = api.moe_weights_t(*([8] * 12))
     w_bad.w_router = None
     assert L.moe_forward(cp, 8, ctypes.byref(w_bad), 8, None, 8, ws_need, None) == 1
-    w_bad = api.moe_weights_t(*([8] * 11))
+    w_bad = api.moe_weights_t(*([8] * 12))
     w_bad.ws_down = None
     assert L.moe_forward(cp, 8, ctypes.byref(w_bad), 8, None, 8, ws_need, None) == 1
+    # a gated shared expert needs its gate vector; the gate flag is 0 or 1
+    gated = api.config_struct(PRESETS["qwen_gated_bf16"])
+    w_bad = api.moe_weights_t(*([8] * 12))
+    w_bad.ws_gate_vec = None
+    n = api.moe_workspace_size(gated)
+    assert L.moe_forward(ctypes.byref(gated), 8, ctypes.byref(w_bad), 8, None, 8, n, None) == 1
+    assert L.moe_combine(ctypes.byref(gated), 8, None, 8, 8, 8, ctypes.byref(w_bad), 8, 8, n,
+                         None) == 1
+    assert api.moe_workspace_size(api.config_struct(PRESETS["qwen_gated_bf16"],
+                                                    shared_gate=2)) == 0
     # workspace one byte short
     assert L.moe_forward(cp, 8, ctypes.byref(w_ok), 8, None, 8, ws_need - 1, None) == 3
     assert L.moe_permute(cp, 8, 8, 8, 8, 8, ws_need - 1, None) == 3
@@ -133,7 +143,7 @@ def test_zero_tokens_is_a_valid_noop():
     cfg = api.config_struct(PRESETS["softmax_bf16"], num_tokens=0)
     n = api.moe_workspace_size(cfg)
     assert n > 0
-    w = api.moe_weights_t(*([8] * 11))
+    w = api.moe_weights_t(*([8] * 12))
     assert L.moe_forward(ctypes.byref(cfg), 8, ctypes.byref(w), 8, None, 8, n, None) == 0
     assert L.moe_route_from_logits(ctypes.byref(cfg), 8, None, 8, 8, None) == 0
 
