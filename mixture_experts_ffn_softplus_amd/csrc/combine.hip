@@ -3,8 +3,10 @@
 // out[t] = shared[t] + sum_j w[t, j] * y_perm[inv_perm[t * k + j]]: the routed experts' outputs
 // weighted by the router and added to the always-active shared experts' output (routed-experts
 // and shared-expert rows of "Qwen3.5-397B-A17B vs Gemma 4 31B"; the block's equation of the
-// DeepSeek-V4 blueprint).  Pure streaming: one workgroup per token, each thread owning
-// 8-column chunks and keeping up to eight row loads of y in flight.
+// DeepSeek-V4 blueprint).  Pure streaming: one workgroup per token.  The token's k row indices
+// and weights are staged in LDS once (padded to a multiple of eight with zero-weight copies of a
+// real row), so each thread, owning one 8-column chunk, issues its y loads eight at a time with
+// no dependent index load in between.
 //
 // Gated shared expert (shared-expert row, Qwen3.5 cell): the shared output is first scaled by
 // the token's sigmoid(x~ . w_sg), one dot product of length d per token reduced across the
@@ -14,8 +16,9 @@
 
 namespace moe {
 
-constexpr int kCombineThreads = 256;
+constexpr int kCombineMaxThreads = 1024;
 constexpr int kCombineBatch = 8;  // y rows loaded together
+constexpr int kCombineMaxK = 64;  // top_k limit of the library
 
 struct CombineGate {
   const uint8_t* vec;  // [d] fp32 or bf16, null: no gate
@@ -47,9 +50,9 @@ __device__ __forceinline__ void load8(const uint8_t* p, float* v) {
 
 // sigmoid(x~[t] . vec), reduced over the whole workgroup (every thread gets the value).
 __device__ float shared_gate(const CombineGate& g, int t, int d) {
-  __shared__ float part[kCombineThreads / kWave];
+  __shared__ float part[kCombineMaxThreads / kWave];
   float z = 0.0f;
-  for (int c = threadIdx.x; c < d / 8; c += kCombineThreads) {
+  for (int c = threadIdx.x; c < d / 8; c += blockDim.x) {
     float xv[8], gv[8];
     const int64_t i = static_cast<int64_t>(t) * d + c * 8;
     if (g.x_kind == 0) {
@@ -76,22 +79,29 @@ __device__ float shared_gate(const CombineGate& g, int t, int d) {
   if (lane_id() == 0) part[threadIdx.x / kWave] = z;
   __syncthreads();
   z = 0.0f;
-#pragma unroll
-  for (int q = 0; q < kCombineThreads / kWave; ++q) z += part[q];
+  for (int q = 0; q < static_cast<int>(blockDim.x) / kWave; ++q) z += part[q];
   return 1.0f / (1.0f + expf(-z));
 }
 
 template <bool Y_F32, bool OUT_F32>
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+__global__ __launch_bounds__(kCombineMaxThreads) void combine_kernel(
     const uint8_t* __restrict__ y, const int32_t* __restrict__ inv, const float* __restrict__ w,
     int k, const float* __restrict__ base, CombineGate gate, uint8_t* __restrict__ out, int d) {
   constexpr int ysz = Y_F32 ? 4 : 2, osz = OUT_F32 ? 4 : 2;
+  __shared__ int32_t s_row[kCombineMaxK];
+  __shared__ float s_w[kCombineMaxK];
   const int t = blockIdx.x;
-  const int64_t ldy = static_cast<int64_t>(d) * ysz;
-  const int32_t* rows = inv + static_cast<int64_t>(t) * k;
-  const float* wt = w + static_cast<int64_t>(t) * k;
+  const int kp = (k + kCombineBatch - 1) / kCombineBatch * kCombineBatch;
+  if (static_cast<int>(threadIdx.x) < kp) {
+    const int j = threadIdx.x;
+    const int64_t at = static_cast<int64_t>(t) * k + (j < k ? j : k - 1);
+    s_row[j] = inv[at];
+    s_w[j] = j < k ? w[at] : 0.0f;
+  }
   const float G = gate.vec ? shared_gate(gate, t, d) : 1.0f;  // uniform branch
-  for (int c = threadIdx.x; c < d / 8; c += kCombineThreads) {
+  __syncthreads();
+  const int64_t ldy = static_cast<int64_t>(d) * ysz;
+  for (int c = threadIdx.x; c < d / 8; c += blockDim.x) {
     float v[8];
     if (base) {
       const f32x4* b = reinterpret_cast<const f32x4*>(base + static_cast<int64_t>(t) * d + c * 8);
@@ -105,37 +115,17 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 #pragma unroll
       for (int q = 0; q < 8; ++q) v[q] = 0.0f;
     }
-    for (int j0 = 0; j0 < k; j0 += kCombineBatch) {
-      i32x4 raw[kCombineBatch][Y_F32 ? 2 : 1];
-      float wj[kCombineBatch];
+    const uint8_t* yc = y + c * 8 * ysz;
+    for (int j0 = 0; j0 < kp; j0 += kCombineBatch) {
+      float yv[kCombineBatch][8];
+#pragma unroll
+      for (int u = 0; u < kCombineBatch; ++u)
+        load8<Y_F32>(yc + s_row[j0 + u] * ldy, yv[u]);
 #pragma unroll
       for (int u = 0; u < kCombineBatch; ++u) {
-        wj[u] = 0.0f;
-        raw[u][0] = i32x4{0, 0, 0, 0};
-        if constexpr (Y_F32) raw[u][Y_F32 ? 1 : 0] = i32x4{0, 0, 0, 0};
-        if (j0 + u < k) {  // uniform: k is the same for the whole grid
-          wj[u] = wt[j0 + u];
-          const i32x4* src = reinterpret_cast<const i32x4*>(y + rows[j0 + u] * ldy + c * 8 * ysz);
-          raw[u][0] = src[0];
-          if constexpr (Y_F32) raw[u][Y_F32 ? 1 : 0] = src[1];
-        }
-      }
+        const float wj = s_w[j0 + u];
 #pragma unroll
-      for (int u = 0; u < kCombineBatch; ++u) {
-        if constexpr (Y_F32) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            v[q] = fmaf(wj[u], __int_as_float(raw[u][0][q]), v[q]);
-            v[4 + q] = fmaf(wj[u], __int_as_float(raw[u][Y_F32 ? 1 : 0][q]), v[4 + q]);
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t bits = static_cast<uint32_t>(raw[u][0][q]);
-            v[2 * q] = fmaf(wj[u], __uint_as_float(bits << 16), v[2 * q]);
-            v[2 * q + 1] = fmaf(wj[u], __uint_as_float(bits & 0xFFFF0000u), v[2 * q + 1]);
-          }
-        }
+        for (int q = 0; q < 8; ++q) v[q] = fmaf(wj, yv[u][q], v[q]);
       }
     }
     uint8_t* dst = out + (static_cast<int64_t>(t) * d + c * 8) * osz;
@@ -167,7 +157,10 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
     g.vec_f32 = a.gate_f32;
     g.x_kind = a.x_kind;
   }
-  const dim3 grid(a.T), block(kCombineThreads);
+  if (a.k < 1 || a.k > kCombineMaxK || a.d % 8) return hipErrorInvalidValue;
+  // one thread per 8-column chunk (whole waves), at most kCombineMaxThreads
+  const int chunks = (a.d / 8 + kWave - 1) / kWave * kWave;
+  const dim3 grid(a.T), block(chunks < kCombineMaxThreads ? chunks : kCombineMaxThreads);
   if (a.y_f32 && a.out_f32)
     hipLaunchKernelGGL((combine_kernel<true, true>), grid, block, 0, s, yb, a.inv, a.w, a.k,
                        a.base, g, ob, a.d);

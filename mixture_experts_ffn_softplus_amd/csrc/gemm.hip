@@ -370,9 +370,11 @@ void grouped_gemm_kernel(GemmArgs a) {
   };
   // FP8 step: one E4M3 MFMA covers exactly one 128-deep scale block; its fp32 partial is
   // promoted with the row's activation scale times the block's weight scale.  Written in
-  // issue order (sched_barrier pins it): MFMA n runs while partial n-1 is promoted, so only
-  // two partials are live, and f is refilled from slot `next` as soon as each fragment's last
-  // MFMA has issued (A row block i after its row of MFMAs, the B columns after the last row).
+  // issue order: MFMA n is issued before partial n-1 is promoted (sched_barrier fences each
+  // MFMA with the promotion of the previous one, and sched_group_barrier puts the MFMA first
+  // inside the fence, so the promotion waits on an MFMA that has long finished instead of the
+  // one just issued), and f is refilled from slot `next` as soon as each fragment's last MFMA
+  // has issued: A row block i after its row of MFMAs, B column j after MFMA (last row, j).
   auto mma_refill_fp8 = [&](F& f, int next) {
     if constexpr (S::kFp8) {
       const uint8_t* sa = smem + next * S::SLOT;
@@ -380,6 +382,7 @@ void grouped_gemm_kernel(GemmArgs a) {
       const float* ss = reinterpret_cast<const float*>(sa + STAGE_BYTES);
       f32x4 prev = f32x4{0.f, 0.f, 0.f, 0.f};
       f32x4 qs[2], qp[2];
+      float sb_next[2];
 #pragma unroll
       for (int i = 0; i < S::FM; ++i) {
 #pragma unroll
@@ -396,6 +399,16 @@ void grouped_gemm_kernel(GemmArgs a) {
             for (int e = 0; e < 4; ++e) acc[pi][pj][e] = fmaf(prev[e], qq[e], acc[pi][pj][e]);
           }
           prev = cur;
+          if (i == S::FM - 1) {  // B column j is done: refill it
+            const int r = wn * S::TN + j * 16 + lr;
+            const i32x4 lo4 = *reinterpret_cast<const i32x4*>(sb + swz(r, 2 * kq));
+            const i32x4 hi4 = *reinterpret_cast<const i32x4*>(sb + swz(r, 2 * kq + 1));
+            f.b[0][j] = i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+            if (j < 2) sb_next[j] = ss[BM + wn * S::TN / 16 + j];
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // the MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // then the VALU work
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // then the LDS reads
           __builtin_amdgcn_sched_barrier(0);
         }
         qp[0] = qs[0];
@@ -412,15 +425,8 @@ void grouped_gemm_kernel(GemmArgs a) {
       for (int e = 0; e < 4; ++e)
         acc[S::FM - 1][S::FN - 1][e] =
             fmaf(prev[e], qp[(S::FN - 1) & 1][e], acc[S::FM - 1][S::FN - 1][e]);
-#pragma unroll
-      for (int j = 0; j < S::FN; ++j) {
-        const int r = wn * S::TN + j * 16 + lr;
-        const i32x4 lo4 = *reinterpret_cast<const i32x4*>(sb + swz(r, 2 * kq));
-        const i32x4 hi4 = *reinterpret_cast<const i32x4*>(sb + swz(r, 2 * kq + 1));
-        f.b[0][j] = i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-      }
-      f.sb[0] = ss[BM + wn * S::TN / 16];
-      f.sb[1] = ss[BM + wn * S::TN / 16 + 1];
+      f.sb[0] = sb_next[0];
+      f.sb[1] = sb_next[1];
     }
   };
 
