@@ -16,6 +16,13 @@ What it computes, and the passages it follows (archdiff.com comparison pages):
   the blueprint router box (sigma or sqrt-softplus, balanced by a bias) for the
   sigmoid score.  Ties at the top-k boundary go to the lower expert index
   (the pages are silent; this is the reading taken).
+* ``route_hashed`` -- same row, DeepSeek-V4-Pro cell: the first three MoE
+  layers choose experts by a fixed token-id hash.  Read as a fixed table of k
+  expert ids per token id; the combine weights stay the router's (the same
+  formulas as ``route``, on the table's experts).
+* ``bias_update`` -- same cell: auxiliary-loss-free balancing with bias speed
+  0.001; each selection bias moves by the speed towards balance, by the sign of
+  (mean load - the expert's load) over the batch's assignments.
 * ``permute`` -- expert-contiguous order of the (token, slot) assignments,
   stable in token order (a counting sort; the pages imply the grouping by
   selecting routed experts per token).
@@ -25,7 +32,7 @@ What it computes, and the passages it follows (archdiff.com comparison pages):
   routed-experts row (SwiGLU experts) and shared-expert row (the shared
   expert's output is added to the routed sum; in the Qwen3.5 cell scaled
   first by a per-token sigmoid gate of a learned vector); blueprint
-  shared-expert box "1-2, always active".
+  shared-expert box (one or two shared experts used by every token).
 
 Parity status per function is listed in the module docstrings of the tests
 that pin it (``tests/test_oracle_*.py``).
@@ -90,6 +97,13 @@ def lib():
                                 ctypes.c_int, ctypes.c_double, _dp, _fp, _ip, _dp, _dp]
         L.orc_permute.restype = ctypes.c_int
         L.orc_permute.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _ip, _ip, _ip, _ip]
+        L.orc_route_hashed.restype = ctypes.c_int
+        L.orc_route_hashed.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_double, _dp, _ip, ctypes.c_int,
+                                       _ip, _ip, _dp]
+        L.orc_bias_update.restype = ctypes.c_int
+        L.orc_bias_update.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _ip,
+                                      ctypes.c_float, _fp]
         L.orc_moe_tokens.restype = ctypes.c_int
         L.orc_moe_tokens.argtypes = [ctypes.POINTER(_FfnCfg), ctypes.c_int, _dp, _ip, _dp,
                                      ctypes.POINTER(_ExpertSet), ctypes.POINTER(_ExpertSet), _dp]
@@ -199,6 +213,36 @@ def route(logits, k, score_kind=SOFTMAX, renormalize=True, gamma=1.0, select_bia
     if rc != 0:
         raise ValueError("oracle route: k out of range")
     return ids, w, s
+
+
+def route_hashed(logits, token_ids, table, score_kind=SOFTMAX, renormalize=True, gamma=1.0):
+    """Experts from a fixed token-id table (ids[t] = table[token_ids[t]]) and the router's
+    combine weights for them."""
+    logits = np.ascontiguousarray(logits, dtype=np.float64)
+    token_ids = np.ascontiguousarray(token_ids, dtype=np.int32)
+    table = np.ascontiguousarray(table, dtype=np.int32)
+    T, E = logits.shape
+    vocab, k = table.shape
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    rc = lib().orc_route_hashed(T, E, k, int(score_kind), int(bool(renormalize)), float(gamma),
+                                _ptr(logits, _dp), _ptr(token_ids, _ip), vocab,
+                                _ptr(table, _ip), _ptr(ids, _ip), _ptr(w, _dp))
+    if rc != 0:
+        raise ValueError("oracle route_hashed: token id or table entry out of range")
+    return ids, w
+
+
+def bias_update(bias, ids, num_experts, speed=0.001):
+    """One balancing step of the fp32 selection bias from the batch's expert ids [T, k]."""
+    b = np.array(bias, dtype=np.float32, copy=True)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T, k = ids.shape
+    rc = lib().orc_bias_update(T, k, num_experts, _ptr(ids, _ip), float(np.float32(speed)),
+                               _ptr(b, _fp))
+    if rc != 0:
+        raise ValueError("oracle bias_update: expert id out of range")
+    return b
 
 
 def permute(ids, num_experts):

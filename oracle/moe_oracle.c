@@ -172,6 +172,38 @@ double orc_score(int score, double l) {
   return sqrt(fmax(l, 0.0) + log1p(exp(-fabs(l))));
 }
 
+/* Combine weights of one token's selected experts sel[k] (slot order kept).
+ * Softmax, renormalised (Qwen3.5 router cell, k = 10 there): softmax over the
+ * selected logits; not renormalised: the full softmax probability.
+ * sigma / sqrt-softplus (DeepSeek-V4-Pro router cell: picked scores
+ * normalised, then multiplied by 2.5): the selected unbiased scores divided by
+ * their sum; not renormalised: the score itself.  Either way the result is
+ * multiplied by gamma (2.5 in that cell, 1 for softmax).  l: the token's E
+ * logits; s: their unbiased scores (softmax: the logits). */
+static void orc_weights(int E, int k, int score, int renorm, double gamma, const double* l,
+                        const double* s, const int32_t* sel, double* w) {
+  int j, e;
+  double denom = 0.0, mx;
+  if (score == ORC_SOFTMAX) {
+    if (renorm) {
+      mx = l[sel[0]];
+      for (j = 1; j < k; ++j) mx = fmax(mx, l[sel[j]]);
+      for (j = 0; j < k; ++j) denom += exp(l[sel[j]] - mx);
+    } else {
+      mx = l[0];
+      for (e = 1; e < E; ++e) mx = fmax(mx, l[e]);
+      for (e = 0; e < E; ++e) denom += exp(l[e] - mx);
+    }
+    for (j = 0; j < k; ++j) w[j] = gamma * exp(l[sel[j]] - mx) / denom;
+  } else {
+    if (renorm)
+      for (j = 0; j < k; ++j) denom += s[sel[j]];
+    else
+      denom = 1.0;
+    for (j = 0; j < k; ++j) w[j] = gamma * s[sel[j]] / denom;
+  }
+}
+
 /* Top-k selection and combine weights for each token.
  *
  * Keys.  Softmax router: the logit itself (softmax is monotone, so the top-k
@@ -180,13 +212,7 @@ double orc_score(int score, double l) {
  * to pick (DeepSeek-V4-Pro router cell); the score is rounded once to fp32 and
  * the bias added in fp32, so that the key is one fixed fp32 number.
  * Order: key descending, equal keys broken by the lower expert index.
- *
- * Weights.  Softmax, renormalised (Qwen3.5 router cell, k = 10 there):
- * softmax over the selected logits; not renormalised: the full
- * softmax probability.  sigma / sqrt-softplus (DeepSeek-V4-Pro router cell:
- * picked scores normalised, then multiplied by 2.5): the selected unbiased
- * scores divided by their sum; not renormalised: the score itself.  Either way
- * the result is multiplied by gamma (2.5 in that cell, 1 for softmax).
+ * Weights: orc_weights on the selection.
  *
  * scores_out, if non-NULL, receives the unbiased score (softmax: logit) of each
  * selected slot.  Returns 0, or -1 for invalid k. */
@@ -201,7 +227,6 @@ int orc_route(int T, int E, int k, int score, int renorm, double gamma, const do
     double* s = (double*)malloc(sizeof(double) * (size_t)E);
     char* taken = (char*)calloc((size_t)E, 1);
     int j, e;
-    double denom = 0.0, mx;
     for (e = 0; e < E; ++e) {
       if (score == ORC_SOFTMAX) {
         s[e] = l[e];
@@ -225,28 +250,75 @@ int orc_route(int T, int E, int k, int score, int renorm, double gamma, const do
     }
     if (scores_out)
       for (j = 0; j < k; ++j) scores_out[(size_t)t * k + j] = s[ids[(size_t)t * k + j]];
-    if (score == ORC_SOFTMAX) {
-      if (renorm) {
-        mx = l[ids[(size_t)t * k]];
-        for (j = 0; j < k; ++j) denom += exp(l[ids[(size_t)t * k + j]] - mx);
-      } else {
-        mx = l[0];
-        for (e = 1; e < E; ++e) mx = fmax(mx, l[e]);
-        for (e = 0; e < E; ++e) denom += exp(l[e] - mx);
-      }
-      for (j = 0; j < k; ++j)
-        w[(size_t)t * k + j] = gamma * exp(l[ids[(size_t)t * k + j]] - mx) / denom;
-    } else {
-      if (renorm)
-        for (j = 0; j < k; ++j) denom += s[ids[(size_t)t * k + j]];
-      else
-        denom = 1.0;
-      for (j = 0; j < k; ++j) w[(size_t)t * k + j] = gamma * s[ids[(size_t)t * k + j]] / denom;
-    }
+    orc_weights(E, k, score, renorm, gamma, l, s, ids + (size_t)t * k, w + (size_t)t * k);
     free(key);
     free(s);
     free(taken);
   }
+  return 0;
+}
+
+/* Routing by a fixed token-id hash (router row, DeepSeek-V4-Pro cell: the first
+ * three MoE layers choose their experts by a fixed hash of the token id).  The
+ * hash is a table of k expert ids per token id, applied as given: ids[t] =
+ * table[token_ids[t]].  Only the choice changes; the combine weights are the
+ * router's, orc_weights on the table's experts in the table's slot order.
+ * Returns -1 if a token id is outside [0, vocab) or a table row does not hold
+ * k distinct ids in [0, E). */
+int orc_route_hashed(int T, int E, int k, int score, int renorm, double gamma,
+                     const double* logits, const int32_t* token_ids, int vocab,
+                     const int32_t* table, int32_t* ids, double* w) {
+  int t;
+  if (k < 1 || k > E) return -1;
+  for (t = 0; t < T; ++t) {
+    int j, i;
+    const int32_t* row;
+    if (token_ids[t] < 0 || token_ids[t] >= vocab) return -1;
+    row = table + (size_t)token_ids[t] * k;
+    for (j = 0; j < k; ++j) {
+      if (row[j] < 0 || row[j] >= E) return -1;
+      for (i = 0; i < j; ++i)
+        if (row[i] == row[j]) return -1;
+    }
+  }
+#pragma omp parallel for schedule(static)
+  for (t = 0; t < T; ++t) {
+    const double* l = logits + (size_t)t * E;
+    double* s = (double*)malloc(sizeof(double) * (size_t)E);
+    int j, e;
+    for (e = 0; e < E; ++e) s[e] = score == ORC_SOFTMAX ? l[e] : orc_score(score, l[e]);
+    for (j = 0; j < k; ++j) ids[(size_t)t * k + j] = table[(size_t)token_ids[t] * k + j];
+    orc_weights(E, k, score, renorm, gamma, l, s, ids + (size_t)t * k, w + (size_t)t * k);
+    free(s);
+  }
+  return 0;
+}
+
+/* Auxiliary-loss-free balancing step (router row, DeepSeek-V4-Pro cell: bias
+ * balancing with speed 0.001; the update is the published sign rule of that
+ * method): every expert's selection bias moves by `speed` towards balance,
+ *   b_e <- b_e + speed * sign(mean load - load_e),
+ * load_e = number of the batch's T*k assignments routed to e, mean load =
+ * T*k / E.  The sign is decided exactly in integers, sign(T*k - E*load_e), and
+ * the step is one fp32 add (the bias is fp32).  Returns -1 for an id outside
+ * [0, E). */
+int orc_bias_update(int T, int k, int E, const int32_t* ids, float speed, float* bias) {
+  int64_t* load = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+  int64_t A = (int64_t)T * k, a;
+  int e;
+  for (a = 0; a < A; ++a) {
+    if (ids[a] < 0 || ids[a] >= E) {
+      free(load);
+      return -1;
+    }
+    load[ids[a]] += 1;
+  }
+  for (e = 0; e < E; ++e) {
+    int64_t diff = A - (int64_t)E * load[e];
+    float step = diff > 0 ? speed : diff < 0 ? -speed : 0.0f;
+    bias[e] = bias[e] + step; /* fp32 add */
+  }
+  free(load);
   return 0;
 }
 

@@ -1,11 +1,11 @@
 """Pins of the oracle's router (logits, scores, top-k, weights) and permutation.
 
 Passages (archdiff.com, "Qwen3.5-397B-A17B vs DeepSeek-V4-Pro", component table, router row):
-Qwen3.5 cell -- a linear router scores the experts, softmax, keep the top k, renormalise, no
-selection bias; DeepSeek-V4-Pro cell -- sqrt-softplus affinities, a per-expert bias used only
-to pick the top k, the selected scores normalised and scaled by 2.5.  Blueprint router box:
-"sigma / sqrt-softplus, bias balancing".  The tie-break (lower expert index wins) is a reading:
-the pages are silent on it.
+Qwen3.5 cell -- one linear map gives a logit per expert, then softmax, the k largest kept and
+renormalised, no selection bias; DeepSeek-V4-Pro cell -- sqrt-softplus scores, a per-expert
+bias that only affects which k are picked, the picked scores normalised and multiplied by 2.5.
+Blueprint router box: sigma or sqrt-softplus scores balanced by a bias.  The tie-break (lower
+expert index wins) is a reading: the pages are silent on it.
 """
 import itertools
 import math
