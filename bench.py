@@ -135,6 +135,86 @@ def cpu_baseline(cfg, inp, n_tokens, seed=0):
             "seconds": t_cpu}
 
 
+def _timed(fn, steps, warmup, marks=0):
+    """Mean ms of fn(i, events) over `steps` calls after `warmup` untimed ones, and the mean
+    ms between consecutive pairs of the events fn records (torch events on the current
+    stream, which is the stream the library is given)."""
+    import torch
+    for i in range(warmup):
+        fn(i, None)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(marks)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        fn(i, ev[i])
+    end.record()
+    torch.cuda.synchronize()
+    pairs = [sum(ev[i][2 * p].elapsed_time(ev[i][2 * p + 1]) for i in range(steps)) / steps
+             for p in range(marks // 2)]
+    return start.elapsed_time(end) / steps, pairs
+
+
+def time_hash_routing(cfg, x, w, ws, steps, warmup):
+    """The whole step with the experts chosen by a fixed token-id table."""
+    import torch
+    from mixture_experts_ffn_softplus_amd import api, synth
+    dev = x.device
+    tok, table = synth.hash_routing(cfg, dev)
+    T, E, k, d, A = cfg.num_tokens, cfg.num_experts, cfg.top_k, cfg.d_model, cfg.assignments
+    fp8 = cfg.expert_dtype == 2
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    tw = torch.empty(T, k, dtype=torch.float32, device=dev)
+    xq = torch.empty(T, d, dtype=torch.uint8, device=dev) if fp8 else None
+    xs = torch.empty(T, d // 128, dtype=torch.float32, device=dev) if fp8 else None
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(A, dtype=torch.int32, device=dev)
+    inv = torch.empty(A, dtype=torch.int32, device=dev)
+    y = torch.empty(A, d, dtype=api.y_dtype(cfg), device=dev)
+    out = torch.empty(T, d, dtype=api.out_dtype(cfg), device=dev)
+    xa = xq if fp8 else x
+
+    def step(i, ev):
+        if ev:
+            ev[0].record()
+        api.moe_route_hashed(cfg, x, w, tok, table, None, ids, tw, xq, xs, ws)
+        if ev:
+            ev[1].record()
+        api.moe_permute(cfg, ids, off, perm, inv, ws)
+        api.moe_expert_ffn(cfg, xa, xs, off, perm, w, y, ws)
+        api.moe_combine(cfg, xa, xs, y, inv, tw, w, out, ws)
+
+    ms, (route_ms,) = _timed(step, steps, warmup, marks=2)
+    counts = (off[1:] - off[:-1]).cpu()
+    log(f"hash routing: {ms:.4f} ms/step, route {route_ms:.4f} ms")
+    return {"ms_per_step": round(ms, 5), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "route_ms": round(route_ms, 5), "vocab": int(table.shape[0]),
+            "token_ids": "zipf s=1.0", "touched_experts": int((counts > 0).sum()),
+            "max_rows_per_expert": int(counts.max())}
+
+
+def time_bias_update(cfg, x, w, out, ws, steps, warmup):
+    """One balancing step of the selection bias from a forward's expert offsets (a scratch
+    copy of the bias is updated, so the timed forward's routing is not disturbed).  The kernel
+    is a few microseconds; the figure here is per call issued from Python, back to back, so
+    host launch latency bounds it (rocprofv3 gives the kernel's own duration)."""
+    import torch
+    from mixture_experts_ffn_softplus_amd import api
+    dev = x.device
+    E = cfg.num_experts
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    api.moe_forward(cfg, x, w, out, ws, {"expert_offsets": off})
+    bias = torch.zeros(E, dtype=torch.float32, device=dev)
+
+    def step(i, ev):
+        api.moe_update_bias(cfg, off, bias, 0.001)
+
+    ms, _ = _timed(step, steps, warmup, marks=0)
+    log(f"bias update: {ms * 1e3:.2f} us per call (host-launch bound)")
+    return {"us_per_call_host_bound": round(ms * 1e3, 3), "experts": E,
+            "bytes": (E + 1) * 4 + 2 * E * 4}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,6 +223,11 @@ def main():
     ap.add_argument("--workload", default="softmax_bf16")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hash-routing", action="store_true",
+                    help="also time the step with experts chosen by a fixed token-id table "
+                         "(moe_route_hashed, then permute / experts / combine)")
+    ap.add_argument("--bias-update", action="store_true",
+                    help="also time the bias-balancing step (moe_update_bias)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times): the reference for "
                          "scaling HBM byte counters")
@@ -250,6 +335,12 @@ def main():
             "mfma_frac": round(step_flops / (ms * 1e-3) / 1e12 / mfma_peak, 4),
             "touched_experts": touched, "max_rows_per_expert": int(counts.max())}
 
+    extra = {}
+    if args.hash_routing:
+        extra["hash_routing"] = time_hash_routing(cfg, x, w, ws, args.steps, args.warmup)
+    if args.bias_update:
+        extra["bias_update"] = time_bias_update(cfg, x, w, out, ws, args.steps, args.warmup)
+
     cpu = None
     if not args.no_cpu_baseline:
         inp["routed"] = None
@@ -269,6 +360,7 @@ def main():
                                                                    stage_ms.items()},
         "cpu_baseline": cpu,
     }
+    result.update(extra)
     print(json.dumps(result), flush=True)
 
 

@@ -211,6 +211,39 @@ MOE_API moe_status_t moe_route(const moe_config_t* cfg, const void* x, const moe
                        float* logits, int32_t* topk_ids, float* topk_w, void* xq,
                        float* xq_scales, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_route for the layers that choose their experts by a fixed token-id hash
+ * (router row, DeepSeek-V4-Pro cell: the first three MoE layers).  The hash is
+ * a caller-owned table [vocab, k] of expert ids: topk_ids[t] =
+ * hash_table[token_ids[t]] in the table's slot order, and topk_w[t] are the
+ * router's weights for those experts, computed from this call's logits as in
+ * moe_route (softmax renormalised over the table's experts, or the full softmax
+ * probability; sigma / sqrt-softplus: the experts' unbiased scores over their
+ * sum, or the scores; times routed_scale).  select_bias plays no part.
+ * token_ids [T] and hash_table are device int32; each token id must lie in
+ * [0, vocab) and each table row hold k distinct ids in [0, E): values outside
+ * those ranges are clamped into them (no out-of-bounds access, result
+ * unspecified).  Everything else (logits, xq, xq_scales, ws) as in moe_route.
+ * The ids then feed moe_permute, moe_expert_ffn and moe_combine unchanged. */
+MOE_API moe_status_t moe_route_hashed(const moe_config_t* cfg, const void* x,
+                                      const moe_weights_t* weights, const int32_t* token_ids,
+                                      const int32_t* hash_table, int32_t vocab, float* logits,
+                                      int32_t* topk_ids, float* topk_w, void* xq,
+                                      float* xq_scales, void* ws, size_t ws_bytes,
+                                      hipStream_t stream);
+
+/* One auxiliary-loss-free balancing step of the selection bias (router row,
+ * DeepSeek-V4-Pro cell: bias balancing with speed 0.001; the update is the
+ * published sign rule of that method).  With load_e = expert_offsets[e+1] -
+ * expert_offsets[e] (moe_permute's output for the batch) and A =
+ * expert_offsets[E] = T*k:
+ *   select_bias[e] += speed * sign(A - E * load_e)
+ * i.e. an expert above the mean load T*k/E moves down by speed, one below it
+ * moves up, one exactly at it keeps its bias bit for bit.  The comparison is
+ * exact in integers and the step is one fp32 add.  select_bias [E] fp32, updated in
+ * place on `stream`.  speed must be finite and >= 0 (0.001 on the pages). */
+MOE_API moe_status_t moe_update_bias(const moe_config_t* cfg, const int32_t* expert_offsets,
+                                     float speed, float* select_bias, hipStream_t stream);
+
 /* The scoring and top-k step of moe_route on caller-supplied fp32 logits
  * [T,E] (bias z already included); same keys, order and weights. */
 MOE_API moe_status_t moe_route_from_logits(const moe_config_t* cfg, const float* logits,

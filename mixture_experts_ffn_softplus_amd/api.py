@@ -22,8 +22,8 @@ MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = 3, 4
 PACK_COUNT = 9
 
 EXPORTED = ["moe_status_string", "moe_workspace_size", "moe_packed_size", "moe_pack_weights",
-            "moe_route", "moe_route_from_logits", "moe_permute", "moe_expert_ffn",
-            "moe_combine", "moe_forward"]
+            "moe_route", "moe_route_from_logits", "moe_route_hashed", "moe_update_bias",
+            "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward"]
 
 
 class moe_config_t(ctypes.Structure):
@@ -95,6 +95,11 @@ def lib():
         L.moe_route.argtypes = [cp, _vp, wp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.moe_route_from_logits.restype = ctypes.c_int
         L.moe_route_from_logits.argtypes = [cp, _vp, _vp, _vp, _vp, _vp]
+        L.moe_route_hashed.restype = ctypes.c_int
+        L.moe_route_hashed.argtypes = [cp, _vp, wp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp,
+                                       _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.moe_update_bias.restype = ctypes.c_int
+        L.moe_update_bias.argtypes = [cp, _vp, ctypes.c_float, _vp, _vp]
         L.moe_permute.restype = ctypes.c_int
         L.moe_permute.argtypes = [cp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.moe_expert_ffn.restype = ctypes.c_int
@@ -176,6 +181,22 @@ def moe_route(cfg, x, weights: moe_weights_t, logits, topk_ids, topk_w, xq=None,
 def moe_route_from_logits(cfg, logits, select_bias, topk_ids, topk_w, stream=None):
     _check(lib().moe_route_from_logits(_cfg(cfg), _p(logits), _p(select_bias), _p(topk_ids),
                                        _p(topk_w), _stream(stream)), "moe_route_from_logits")
+
+
+def moe_route_hashed(cfg, x, weights, token_ids, hash_table, logits, topk_ids, topk_w, xq=None,
+                     xq_scales=None, ws=None, stream=None):
+    """hash_table: int32 [vocab, k] on the device; token_ids: int32 [T]."""
+    _check(lib().moe_route_hashed(_cfg(cfg), _p(x), ctypes.byref(weights), _p(token_ids),
+                                  _p(hash_table), int(hash_table.shape[0]), _p(logits),
+                                  _p(topk_ids), _p(topk_w), _p(xq), _p(xq_scales), _p(ws),
+                                  ws.numel() * ws.element_size() if ws is not None else 0,
+                                  _stream(stream)), "moe_route_hashed")
+
+
+def moe_update_bias(cfg, expert_offsets, select_bias, speed=0.001, stream=None):
+    """One balancing step of the fp32 selection bias [E], in place."""
+    _check(lib().moe_update_bias(_cfg(cfg), _p(expert_offsets), float(speed), _p(select_bias),
+                                 _stream(stream)), "moe_update_bias")
 
 
 def moe_permute(cfg, topk_ids, expert_offsets, perm_token, inv_perm, ws, stream=None):

@@ -181,7 +181,8 @@ RouteArgs route_args(const moe_config_t* c, const float* select_bias, int32_t* i
 // then scoring and top-k; FP8 experts also get their block-scaled activations.
 hipError_t do_route(const moe_config_t* c, const void* x, const moe_weights_t* w, float* logits,
                     int32_t* ids, float* tw, void* xq, float* xq_scales, void* ws,
-                    hipStream_t s) {
+                    hipStream_t s, const int32_t* token_ids = nullptr,
+                    const int32_t* table = nullptr, int vocab = 0) {
   const WsLayout L = ws_layout(c);
   const int kind = router_kind(c);
   const int64_t d = c->d_model, Ep = e_pad(c);
@@ -205,6 +206,9 @@ hipError_t do_route(const moe_config_t* c, const void* x, const moe_weights_t* w
   if (e != hipSuccess) return e;
   RouteArgs ra = route_args(c, w->select_bias, ids, tw);
   ra.logit_bias = w->logit_bias;
+  ra.token_ids = token_ids;
+  ra.table = table;
+  ra.vocab = vocab;
   e = launch_topk(ra, lg, static_cast<int>(Ep), logits, s);
   if (e != hipSuccess) return e;
   if (is_fp8(c) && xq && xq_scales)
@@ -467,6 +471,29 @@ moe_status_t moe_route(const moe_config_t* c, const void* x, const moe_weights_t
   if ((st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
   if (c->num_tokens == 0) return MOE_OK;
   return hip_status(do_route(c, x, w, logits, ids, tw, xq, xq_scales, ws, s));
+}
+
+moe_status_t moe_route_hashed(const moe_config_t* c, const void* x, const moe_weights_t* w,
+                              const int32_t* token_ids, const int32_t* table, int32_t vocab,
+                              float* logits, int32_t* ids, float* tw, void* xq, float* xq_scales,
+                              void* ws, size_t ws_bytes, hipStream_t s) {
+  moe_status_t st = check_config(c);
+  if (st != MOE_OK) return st;
+  if (!x || !ids || !tw || !token_ids || !table || vocab < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if ((st = check_weights(c, w, true, false, false)) != MOE_OK) return st;
+  if ((st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
+  if (c->num_tokens == 0) return MOE_OK;
+  return hip_status(
+      do_route(c, x, w, logits, ids, tw, xq, xq_scales, ws, s, token_ids, table, vocab));
+}
+
+moe_status_t moe_update_bias(const moe_config_t* c, const int32_t* offsets, float speed,
+                             float* select_bias, hipStream_t s) {
+  moe_status_t st = check_config(c);
+  if (st != MOE_OK) return st;
+  if (!offsets || !select_bias || !isfinite(speed) || speed < 0.0f)
+    return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_bias_update(offsets, c->num_experts, speed, select_bias, s));
 }
 
 moe_status_t moe_route_from_logits(const moe_config_t* c, const float* logits,

@@ -17,6 +17,10 @@ struct RouteArgs {
   int T, E, k;
   int score, renorm;
   float gamma;
+  // choice by a fixed token-id table instead of the top k: ids[t] = table[token_ids[t]]
+  const int32_t* token_ids;  // [T], or null (top-k choice)
+  const int32_t* table;      // [vocab, k]
+  int vocab;
 };
 enum RouterKind { kRouterF32 = 0, kRouterBF16 = 1, kRouterBF16HiLo = 2 };
 // Scoring + top-k of fp32 logits rows `ld` apart (plus logit_bias); copy: optional [T, E]
@@ -24,6 +28,10 @@ enum RouterKind { kRouterF32 = 0, kRouterBF16 = 1, kRouterBF16HiLo = 2 };
 hipError_t launch_topk(const RouteArgs& a, const float* logits, int ld, float* copy,
                        hipStream_t s);
 hipError_t launch_quant_x_fp8(const uint16_t* x, uint8_t* xq, float* scales, int T, int d,
+                              hipStream_t s);
+// Balancing step of the fp32 selection bias from the permutation's expert offsets [E+1]:
+// bias[e] += speed * sign(A - E * load_e), A = offsets[E].
+hipError_t launch_bias_update(const int32_t* offsets, int E, float speed, float* bias,
                               hipStream_t s);
 
 // ---- permutation (permute.hip)

@@ -7,9 +7,11 @@
 // choosing the top k, the chosen unbiased scores normalised and scaled by 2.5 (DeepSeek-V4-Pro
 // cell).  Ties at equal keys go to the lower expert index.
 //
-// The logits come from the grouped MFMA GEMM (one group, fp32 out, logit bias added in its
-// epilogue).  Here one wave owns one token: each lane scores E/64 experts held in registers,
-// then k rounds of a 64-lane argmax pick the experts in key order.
+// The logits come from the grouped MFMA GEMM (one group, fp32 out); the logit bias is added
+// here as each logit is read.  One wave owns one token: each lane scores E/64 experts held in
+// registers, then k rounds of a 64-lane argmax pick the experts in key order.  In the layers
+// that choose by a fixed token-id hash (same row, DeepSeek-V4-Pro cell) a table gives the k
+// experts instead, and only the combine weights are computed.
 #include <math.h>
 
 #include "moe_common.h"
@@ -57,7 +59,19 @@ __device__ void topk_row(const float* row, int t, const RouteArgs& a) {
   uint32_t taken = 0;
   int my_id = 0;
   float my_val = 0.0f;
-  for (int j = 0; j < a.k; ++j) {
+  if (a.table) {
+    // fixed token-id table: lane j < k takes slot j's expert and its unbiased score.  Values
+    // outside their ranges (a precondition violation) are clamped, so nothing reads out of
+    // bounds.
+    if (l < a.k) {
+      const int tok = min(max(a.token_ids[t], 0), a.vocab - 1);
+      const int e = min(max(a.table[static_cast<size_t>(tok) * a.k + l], 0), a.E - 1);
+      const float lg = a.logit_bias ? __fadd_rn(row[e], a.logit_bias[e]) : row[e];
+      my_id = e;
+      my_val = a.score == MOE_SCORE_SOFTMAX ? lg : sigma_family_score(a.score, lg);
+    }
+  }
+  for (int j = 0; j < (a.table ? 0 : a.k); ++j) {
     float bk = -INFINITY, bv = 0.0f;
     int be = 0x7fffffff;
 #pragma unroll
@@ -89,11 +103,17 @@ __device__ void topk_row(const float* row, int t, const RouteArgs& a) {
   }
   float w;
   if (a.score == MOE_SCORE_SOFTMAX) {
-    float m = __shfl(my_val, 0, kWave);  // slot 0 holds the largest logit
-    float denom;
+    float m, denom;
     if (a.renorm) {
+      // the largest selected logit: slot 0's for the top-k choice
+      m = a.table ? wave_max(l < a.k ? my_val : -INFINITY) : __shfl(my_val, 0, kWave);
       denom = wave_sum(l < a.k ? expf(my_val - m) : 0.0f);
     } else {
+      float mm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < kMaxPerLane; ++i)
+        if (l + kWave * i < a.E) mm = fmaxf(mm, val[i]);
+      m = wave_max(mm);
       float part = 0.0f;
 #pragma unroll
       for (int i = 0; i < kMaxPerLane; ++i)
@@ -170,6 +190,27 @@ hipError_t launch_topk(const RouteArgs& a, const float* logits, int ld, float* c
                        hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   hipLaunchKernelGGL(topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a, logits, ld, copy);
+  return hipGetLastError();
+}
+
+// Auxiliary-loss-free balancing step (router row, DeepSeek-V4-Pro cell: bias balancing with
+// speed 0.001): the selection bias of an expert that took more than the mean load T*k/E moves
+// down by `speed`, of one that took less moves up, of one exactly at it stays as it is.  The
+// comparison is exact in integers; the step is one fp32 add.  One thread per expert.
+__global__ __launch_bounds__(256) void bias_update_kernel(const int32_t* __restrict__ offsets,
+                                                          int E, float speed,
+                                                          float* __restrict__ bias) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  const int64_t A = offsets[E];
+  const int64_t diff = A - static_cast<int64_t>(E) * (offsets[e + 1] - offsets[e]);
+  if (diff != 0) bias[e] = __fadd_rn(bias[e], diff > 0 ? speed : -speed);  // at the mean: kept
+}
+
+hipError_t launch_bias_update(const int32_t* offsets, int E, float speed, float* bias,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(bias_update_kernel, dim3((E + 255) / 256), dim3(256), 0, s, offsets, E,
+                     speed, bias);
   return hipGetLastError();
 }
 

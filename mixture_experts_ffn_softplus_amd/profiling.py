@@ -102,6 +102,28 @@ def summarize(a):
     print("\n".join(lines))
 
 
+def durations(a):
+    """Kernel-trace durations of each kernel pattern (no counters): small kernels whose time,
+    not their traffic, is the figure of interest."""
+    lines = [
+        f"# rocprofv3 kernel durations on workload {a.workload}",
+        f"# commands (from the repository root):",
+        *[f"#   {c}" for c in a.command],
+        f"# summarised by: python -m mixture_experts_ffn_softplus_amd.profiling durations ...",
+        f"workload: {a.workload}",
+    ]
+    for name, pattern in (kv.split("=", 1) for kv in a.kernel):
+        dur = kernel_durations(a.trace, pattern)
+        lines += [f"{name}_regex: {pattern}", f"{name}_dispatches: {len(dur)}",
+                  f"{name}_avg_us: {statistics.mean(dur):.2f}",
+                  f"{name}_median_us: {statistics.median(dur):.2f}",
+                  f"{name}_min_us: {min(dur):.2f}"]
+    lines += ["top kernels by total time (kernel-trace --stats):", *stats_table(a.trace)]
+    with open(a.out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def read_summary(path: str) -> dict:
     """key: value lines of a summary file (comments and tables skipped)."""
     out = {}
@@ -133,10 +155,17 @@ def main():
         p.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
     p.add_argument("--copy-mib", dest="copy_mib", type=int, default=1024)
     p.add_argument("--command", action="append", default=[])
+    d = sub.add_parser("durations")
+    for k in ("trace", "workload", "out"):
+        d.add_argument("--" + k, dest=k, required=True)
+    d.add_argument("--kernel", action="append", default=[], metavar="NAME=REGEX")
+    d.add_argument("--command", action="append", default=[])
     sub.add_parser("hash")
     a = ap.parse_args()
     if a.cmd == "hash":
         print(source_hash())
+    elif a.cmd == "durations":
+        durations(a)
     else:
         summarize(a)
 

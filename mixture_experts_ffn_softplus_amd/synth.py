@@ -22,6 +22,11 @@ Recipe (all logical layouts row-major):
   when the workload gates its shared experts.
 * Load skew: logit bias z_e = ln p_e - mean(ln p), p_e proportional to
   (e + 1)^-s, expert 0 hottest (fp32).
+* Routing by a fixed token-id hash: a table [vocab, k] of k distinct expert ids
+  per token id (the first k of a seeded random permutation of the experts for
+  each row), vocab 131072 (the low end of the pages' 128K-262K tokenizers), and
+  token ids drawn with Zipf frequencies p(rank r) proportional to 1/r, as word
+  frequencies in text fall off, the id of rank r being a seeded random id.
 
 Generators on a CUDA device and on the CPU produce different streams for the
 same seed; a test always hands the very same tensors to both sides.
@@ -36,6 +41,7 @@ TAG_X, TAG_ROUTER, TAG_SELECT_BIAS = 1, 2, 3
 TAG_GATE, TAG_UP, TAG_DOWN = 4, 5, 6
 TAG_SGATE, TAG_SUP, TAG_SDOWN = 7, 8, 9
 TAG_SHARED_GATE_VEC = 10
+TAG_HASH_TABLE, TAG_TOKEN_IDS = 11, 12
 
 _MASK64 = (1 << 64) - 1
 
@@ -177,3 +183,20 @@ def inputs(cfg: MoEConfig, device="cpu"):
     return {"x": tokens(cfg, device), "w_router": wr, "logit_bias": z, "select_bias": b,
             "routed": routed_experts(cfg, device), "shared": shared_experts(cfg, device),
             "shared_gate": shared_gate_vector(cfg, device)}
+
+
+HASH_VOCAB = 131072
+
+
+def hash_routing(cfg: MoEConfig, device="cpu", vocab: int = HASH_VOCAB, zipf_s: float = 1.0):
+    """(token_ids int32 [T], table int32 [vocab, k]) for routing by a fixed token-id hash."""
+    g = _gen(device, cfg.seed, TAG_HASH_TABLE)
+    keys = torch.rand((vocab, cfg.num_experts), generator=g, device=device)
+    table = keys.argsort(dim=1)[:, :cfg.top_k].to(torch.int32).contiguous()
+    del keys
+    g = _gen(device, cfg.seed, TAG_TOKEN_IDS)
+    p = torch.arange(1, vocab + 1, dtype=torch.float64, device=device) ** -zipf_s
+    rank = torch.multinomial(p / p.sum(), cfg.num_tokens, replacement=True, generator=g)
+    ids_of_rank = torch.randperm(vocab, generator=g, device=device)
+    token_ids = ids_of_rank[rank].to(torch.int32).contiguous()
+    return token_ids, table

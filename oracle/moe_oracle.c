@@ -300,8 +300,9 @@ int orc_route_hashed(int T, int E, int k, int score, int renorm, double gamma,
  *   b_e <- b_e + speed * sign(mean load - load_e),
  * load_e = number of the batch's T*k assignments routed to e, mean load =
  * T*k / E.  The sign is decided exactly in integers, sign(T*k - E*load_e), and
- * the step is one fp32 add (the bias is fp32).  Returns -1 for an id outside
- * [0, E). */
+ * the step is one fp32 add (the bias is fp32); an expert exactly at the mean
+ * load keeps its bias bit for bit (no add, so a -0 stays -0).  Returns -1 for
+ * an id outside [0, E). */
 int orc_bias_update(int T, int k, int E, const int32_t* ids, float speed, float* bias) {
   int64_t* load = (int64_t*)calloc((size_t)E, sizeof(int64_t));
   int64_t A = (int64_t)T * k, a;
@@ -315,8 +316,7 @@ int orc_bias_update(int T, int k, int E, const int32_t* ids, float speed, float*
   }
   for (e = 0; e < E; ++e) {
     int64_t diff = A - (int64_t)E * load[e];
-    float step = diff > 0 ? speed : diff < 0 ? -speed : 0.0f;
-    bias[e] = bias[e] + step; /* fp32 add */
+    if (diff != 0) bias[e] = bias[e] + (diff > 0 ? speed : -speed); /* fp32 add */
   }
   free(load);
   return 0;

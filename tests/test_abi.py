@@ -163,3 +163,27 @@ def test_packed_sizes():
     assert api.moe_packed_size(t, api.PACK_SHARED_DOWN) == 256 * 256 * 4
     assert api.moe_packed_size(t, 42) == 0
     assert FP8_E4M3 == 2 and F32 == 0
+
+
+def test_hashed_route_and_bias_update_argument_checks():
+    L = api.lib()
+    cfg = api.config_struct(PRESETS["tiny_fp32"])
+    cp = ctypes.byref(cfg)
+    n = api.moe_workspace_size(cfg)
+    w = api.moe_weights_t(*([8] * 12))
+    wp = ctypes.byref(w)
+    # moe_route_hashed: token ids, table and a positive vocab are required
+    assert L.moe_route_hashed(cp, 8, wp, None, 8, 4, None, 8, 8, None, None, 8, n, None) == 1
+    assert L.moe_route_hashed(cp, 8, wp, 8, None, 4, None, 8, 8, None, None, 8, n, None) == 1
+    assert L.moe_route_hashed(cp, 8, wp, 8, 8, 0, None, 8, 8, None, None, 8, n, None) == 1
+    assert L.moe_route_hashed(cp, 8, wp, 8, 8, 4, None, 8, 8, None, None, 8, n - 1, None) == 3
+    c0 = api.config_struct(PRESETS["tiny_fp32"], num_tokens=0)
+    assert L.moe_route_hashed(ctypes.byref(c0), 8, wp, 8, 8, 4, None, 8, 8, None, None, 8, n,
+                              None) == 0
+    # moe_update_bias: offsets and bias required; speed finite and >= 0
+    assert L.moe_update_bias(cp, None, 0.001, 8, None) == 1
+    assert L.moe_update_bias(cp, 8, 0.001, None, None) == 1
+    assert L.moe_update_bias(cp, 8, float("nan"), 8, None) == 1
+    assert L.moe_update_bias(cp, 8, -0.001, 8, None) == 1
+    bad = api.config_struct(PRESETS["tiny_fp32"], top_k=0)
+    assert L.moe_update_bias(ctypes.byref(bad), 8, 0.001, 8, None) == 1
