@@ -28,6 +28,9 @@ What it computes, and the passages it follows (archdiff.com comparison pages):
   selecting routed experts per token).
 * ``quant_rows`` / ``e4m3_*`` -- blueprint training box (FP8 with block scales):
   E4M3FN, one fp32 scale (group max / 448) per 128-value group.
+* ``e2m1_value`` / ``e8m0_value`` and ``ExpertSet(fmt="mxfp4")`` -- the same box names
+  MXFP4: OCP MX E2M1 elements with one E8M0 (power-of-two) scale per 32 values along
+  the reduction axis.
 * ``moe_tokens`` -- "Qwen3.5-397B-A17B vs Gemma 4 31B", component table,
   routed-experts row (SwiGLU experts) and shared-expert row (the shared
   expert's output is added to the routed sum; in the Qwen3.5 cell scaled
@@ -44,7 +47,7 @@ import numpy as np
 
 from . import build as _build
 
-F32, BF16, E4M3 = 0, 1, 2
+F32, BF16, E4M3, MXFP4 = 0, 1, 2, 3
 SOFTMAX, SIGMOID, SQRT_SOFTPLUS = 0, 1, 2
 
 _LIB = None
@@ -85,6 +88,10 @@ def lib():
         L.orc_e4m3_round.argtypes = [ctypes.c_double]
         L.orc_e4m3_encode.restype = ctypes.c_uint8
         L.orc_e4m3_encode.argtypes = [ctypes.c_double]
+        L.orc_e2m1_value.restype = ctypes.c_double
+        L.orc_e2m1_value.argtypes = [ctypes.c_uint8]
+        L.orc_e8m0_value.restype = ctypes.c_double
+        L.orc_e8m0_value.argtypes = [ctypes.c_uint8]
         L.orc_quant_rows.restype = None
         L.orc_quant_rows.argtypes = [_dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _up, _fp, _dp]
         L.orc_router_logits.restype = None
@@ -144,6 +151,16 @@ def e4m3_encode(values):
     values = np.asarray(values, dtype=np.float64)
     return np.array([lib().orc_e4m3_encode(float(v)) for v in values.ravel()],
                     dtype=np.uint8).reshape(values.shape)
+
+
+def e2m1_value(codes):
+    """fp64 values of 4-bit E2M1 codes (MXFP4 elements)."""
+    return np.array([lib().orc_e2m1_value(int(c)) for c in np.ravel(codes)]).reshape(np.shape(codes))
+
+
+def e8m0_value(codes):
+    """fp64 values of E8M0 scale codes (2^(code - 127))."""
+    return np.array([lib().orc_e8m0_value(int(c)) for c in np.ravel(codes)]).reshape(np.shape(codes))
 
 
 def quant_rows(x, group=128):
@@ -266,10 +283,15 @@ class ExpertSet:
 
     ``gate[e]``, ``up[e]``: [d, f]; ``down[e]``: [f, d] -- float32, bf16 bits
     (uint16) or E4M3 codes (uint8) with ``*_scales[e]`` float32
-    [rows/128, cols/128].  Entries may be ``None`` for experts no token uses."""
+    [rows/128, cols/128].  ``fmt="mxfp4"``: stored transposed, ``gate[e]``/``up[e]``
+    uint8 [f, d/2] and ``down[e]`` [d, f/2], two E2M1 codes per byte (lower K index in the
+    low nibble), with E8M0 scale bytes ``*_scales[e]`` [f, d/32] / [d, f/32].  Entries may be
+    ``None`` for experts no token uses."""
 
-    def __init__(self, n, gate, up, down, gate_scales=None, up_scales=None, down_scales=None):
+    def __init__(self, n, gate, up, down, gate_scales=None, up_scales=None, down_scales=None,
+                 fmt=None):
         self.n = n
+        self.fmt = fmt
         self.gate, self.up, self.down = gate, up, down
         self.gate_scales, self.up_scales, self.down_scales = gate_scales, up_scales, down_scales
 
@@ -287,8 +309,8 @@ class ExpertSet:
             keep.append(ptrs)
             return ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p))
 
-        dtype = None
-        for lst in (self.gate, self.up, self.down):
+        dtype = MXFP4 if self.fmt == "mxfp4" else None
+        for lst in (() if dtype is not None else (self.gate, self.up, self.down)):
             for a in lst:
                 if a is not None:
                     dtype = storage_dtype(np.asarray(a))

@@ -30,6 +30,7 @@
 #define ORC_F32 0
 #define ORC_BF16 1
 #define ORC_E4M3 2
+#define ORC_MXFP4 3
 
 #define ORC_SOFTMAX 0
 #define ORC_SIGMOID 1
@@ -95,6 +96,20 @@ uint8_t orc_e4m3_encode(double v) {
   return (uint8_t)(sign | ((e + 7) << 3) | m);
 }
 
+/* OCP MX E2M1 element (MXFP4's 4-bit element: 1 sign, 2 exponent bits with
+ * bias 1, 1 mantissa bit; exponent field 0 is subnormal, 0.5 * mantissa).
+ * The training box of the blueprint names MXFP4. */
+double orc_e2m1_value(uint8_t code) {
+  int e = (code >> 1) & 3, m = code & 1;
+  double mag = e == 0 ? 0.5 * m : (1.0 + 0.5 * m) * ldexp(1.0, e - 1);
+  return (code & 8) ? -mag : mag;
+}
+
+/* OCP MX E8M0 shared scale: 2^(code - 127); code 255 is NaN. */
+double orc_e8m0_value(uint8_t code) {
+  return code == 255 ? NAN : ldexp(1.0, (int)code - 127);
+}
+
 /* Block-scaled FP8 quantisation of one group of n values (the diagram's
  * training box): the scale is the group's largest magnitude over 448,
  * held in fp32 (1 when the group is all zero); each value divided by that
@@ -129,16 +144,25 @@ void orc_quant_rows(const double* x, int rows, int cols, int g, uint8_t* codes, 
                       xdq ? xdq + (size_t)r * cols + (size_t)b * g : NULL);
 }
 
-/* One element of a stored matrix [rows, cols] (row-major) as fp64.  For E4M3
- * the matrix carries one fp32 scale per 128 x 128 block, laid out
- * [rows/128, cols/128]. */
-static double orc_elem(int dtype, const void* w, const float* scales, int cols, int block, size_t r,
-                       size_t c) {
+/* One element (r, c) of a stored matrix of logical shape [rows, cols] as fp64.
+ * F32 / BF16 / E4M3: row-major [rows, cols]; E4M3 carries one fp32 scale per
+ * 128 x 128 block, laid out [rows/128, cols/128].  MXFP4: stored transposed,
+ * [cols, rows/2] bytes with two E2M1 codes per byte (the lower row index in
+ * the low nibble), and one E8M0 byte per 32 consecutive rows of a column,
+ * [cols, rows/32] -- the MX blocks run along the reduction axis (rows). */
+static double orc_elem(int dtype, const void* w, const void* scales, int rows, int cols,
+                       int block, size_t r, size_t c) {
   size_t i = r * (size_t)cols + c;
   if (dtype == ORC_F32) return (double)((const float*)w)[i];
   if (dtype == ORC_BF16) return orc_bf16_value(((const uint16_t*)w)[i]);
+  if (dtype == ORC_MXFP4) {
+    uint8_t byte = ((const uint8_t*)w)[c * (size_t)(rows / 2) + r / 2];
+    uint8_t code = (r & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+    return orc_e2m1_value(code) *
+           orc_e8m0_value(((const uint8_t*)scales)[c * (size_t)(rows / 32) + r / 32]);
+  }
   return orc_e4m3_value(((const uint8_t*)w)[i]) *
-         (double)scales[(r / block) * (size_t)(cols / block) + c / block];
+         (double)((const float*)scales)[(r / block) * (size_t)(cols / block) + c / block];
 }
 
 /* ------------------------------------------------------------------------- */
@@ -157,7 +181,7 @@ void orc_router_logits(int T, int d, int E, const double* x, int wr_dtype, const
     for (e = 0; e < E; ++e) {
       double acc = 0.0;
       for (i = 0; i < d; ++i)
-        acc += x[(size_t)t * d + i] * orc_elem(wr_dtype, wr, NULL, E, 1, (size_t)i, (size_t)e);
+        acc += x[(size_t)t * d + i] * orc_elem(wr_dtype, wr, NULL, d, E, 1, (size_t)i, (size_t)e);
       if (logit_bias) acc += (double)logit_bias[e];
       logits[(size_t)t * E + e] = acc;
     }
@@ -360,14 +384,14 @@ int orc_permute(int T, int k, int E, const int32_t* ids, int32_t* off, int32_t* 
 /* ------------------------------------------------------------------------- */
 
 typedef struct {
-  int dtype;                        /* ORC_F32, ORC_BF16 or ORC_E4M3 */
+  int dtype;                        /* ORC_F32, ORC_BF16, ORC_E4M3 or ORC_MXFP4 */
   int n;                            /* number of experts in the set */
-  const void* const* gate;          /* n pointers to [d, f] (NULL: not supplied) */
-  const void* const* up;            /* n pointers to [d, f] */
-  const void* const* down;          /* n pointers to [f, d] */
-  const float* const* gate_scales;  /* E4M3: n pointers to [d/128, f/128] */
-  const float* const* up_scales;    /* E4M3: n pointers to [d/128, f/128] */
-  const float* const* down_scales;  /* E4M3: n pointers to [f/128, d/128] */
+  const void* const* gate;          /* n pointers to logical [d, f] (NULL: not supplied) */
+  const void* const* up;            /* n pointers to logical [d, f] */
+  const void* const* down;          /* n pointers to logical [f, d] */
+  const void* const* gate_scales;   /* E4M3: fp32 [d/128, f/128]; MXFP4: E8M0 [f, d/32] */
+  const void* const* up_scales;     /* likewise */
+  const void* const* down_scales;   /* E4M3: fp32 [f/128, d/128]; MXFP4: E8M0 [d, f/32] */
 } orc_expert_set;
 
 typedef struct {
@@ -393,17 +417,18 @@ static int orc_swiglu(const orc_ffn_cfg* c, int f, const orc_expert_set* s, int 
   const void* wg = s->gate[e];
   const void* wu = s->up[e];
   const void* wd = s->down[e];
-  const float* sg = s->dtype == ORC_E4M3 ? s->gate_scales[e] : NULL;
-  const float* su = s->dtype == ORC_E4M3 ? s->up_scales[e] : NULL;
-  const float* sd = s->dtype == ORC_E4M3 ? s->down_scales[e] : NULL;
+  const int scaled = s->dtype == ORC_E4M3 || s->dtype == ORC_MXFP4;
+  const void* sg = scaled ? s->gate_scales[e] : NULL;
+  const void* su = scaled ? s->up_scales[e] : NULL;
+  const void* sd = scaled ? s->down_scales[e] : NULL;
   if (!wg || !wu || !wd) return -1;
-  if (s->dtype == ORC_E4M3 && (!sg || !su || !sd)) return -1;
+  if (scaled && (!sg || !su || !sd)) return -1;
   for (j = 0; j < f; ++j) g[j] = u[j] = 0.0;
   for (i = 0; i < c->d; ++i) {
     double xi = xr[i];
     for (j = 0; j < f; ++j) {
-      g[j] += xi * orc_elem(s->dtype, wg, sg, f, c->block, (size_t)i, (size_t)j);
-      u[j] += xi * orc_elem(s->dtype, wu, su, f, c->block, (size_t)i, (size_t)j);
+      g[j] += xi * orc_elem(s->dtype, wg, sg, c->d, f, c->block, (size_t)i, (size_t)j);
+      u[j] += xi * orc_elem(s->dtype, wu, su, c->d, f, c->block, (size_t)i, (size_t)j);
     }
   }
   for (j = 0; j < f; ++j) h[j] = orc_silu(g[j]) * u[j];
@@ -411,7 +436,7 @@ static int orc_swiglu(const orc_ffn_cfg* c, int f, const orc_expert_set* s, int 
   for (j = 0; j < f; ++j) {
     double hj = h[j] * wgt;
     for (i = 0; i < c->d; ++i)
-      y[i] += hj * orc_elem(s->dtype, wd, sd, c->d, c->block, (size_t)j, (size_t)i);
+      y[i] += hj * orc_elem(s->dtype, wd, sd, f, c->d, c->block, (size_t)j, (size_t)i);
   }
   return 0;
 }

@@ -270,3 +270,65 @@ def test_missing_expert_is_an_error():
     with pytest.raises(ValueError):
         oracle.moe_tokens(np.zeros((1, d)), np.array([[1]], np.int32), np.ones((1, 1)), routed,
                           None, d, f, 1)
+
+
+# ------------------------------------------------------------------ MXFP4 experts
+
+def _mxfp4_dense(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Logical [K, N] fp64 values of an N-major MXFP4 matrix (codes [N, K/2], two per byte with
+    the lower K index in the low nibble; E8M0 scales [N, K/32]), decoded with the OCP E2M1
+    table and torch's E8M0 type."""
+    table = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    table = np.concatenate([table, -table])
+    nib = np.stack([codes & 15, codes >> 4], axis=-1).reshape(codes.shape[0], -1)   # [N, K]
+    sc = torch.from_numpy(scales).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    return (table[nib] * np.repeat(sc, 32, axis=1)).T
+
+
+def _rand_mxfp4(rng, n, k):
+    codes = rng.integers(0, 256, (n, k // 2)).astype(np.uint8)
+    scales = rng.integers(118, 126, (n, k // 32)).astype(np.uint8)
+    return codes, scales
+
+
+def test_mxfp4_one_hot_fixes_layout_and_nibble_order():
+    # one nonzero weight: W_gate[k=5, n=3] = 1.5 * 2^1 (odd k: the high nibble of byte 2 of
+    # row 3); W_up = 1 everywhere; W_down row 3 = e_7 (scale 2^0)
+    d, f = 256, 128
+    g = np.zeros((f, d // 2), np.uint8)
+    g[3, 2] = 3 << 4
+    gs = np.full((f, d // 32), 127, np.uint8)
+    gs[3, 0] = 128
+    u = np.full((f, d // 2), 0x22, np.uint8)
+    us = np.full((f, d // 32), 127, np.uint8)
+    dn = np.zeros((d, f // 2), np.uint8)
+    dn[7, 1] = 2 << 4                                  # W_down[k=3, n=7] = 1.0
+    ds = np.full((d, f // 32), 127, np.uint8)
+    x = np.zeros((1, d))
+    x[0, 5] = 1.0
+    routed = oracle.ExpertSet(1, [g], [u], [dn], gate_scales=[gs], up_scales=[us],
+                              down_scales=[ds], fmt="mxfp4")
+    out = oracle.moe_tokens(x, np.zeros((1, 1), np.int32), np.ones((1, 1)), routed, None, d, f,
+                            128, quant=False)
+    want = np.zeros(d)
+    want[7] = silu(3.0) * 1.0     # g[3] = x[5] * 3, u[3] = sum(x) = 1, h[3] -> y[7]
+    assert np.max(np.abs(out[0] - want)) < 1e-15
+
+
+def test_mxfp4_expert_equals_dense_swiglu_with_fp8_activations():
+    # E = k = 1 reduces to a plain SwiGLU MLP on the dequantised weights; activations (x and
+    # h) block-scaled FP8 as for E4M3 experts, checked with torch's float8 cast
+    rng = np.random.default_rng(4)
+    d, f, n = 256, 256, 5
+    gq, gs = _rand_mxfp4(rng, f, d)
+    uq, us = _rand_mxfp4(rng, f, d)
+    dq, ds = _rand_mxfp4(rng, d, f)
+    routed = oracle.ExpertSet(1, [gq], [uq], [dq], gate_scales=[gs], up_scales=[us],
+                              down_scales=[ds], fmt="mxfp4")
+    x = rng.standard_normal((n, d))
+    out = oracle.moe_tokens(x, np.zeros((n, 1), np.int32), np.ones((n, 1)), routed, None, d, f,
+                            128, quant=True)
+    xq = _torch_qdq_rows(x)
+    h = silu(xq @ _mxfp4_dense(gq, gs)) * (xq @ _mxfp4_dense(uq, us))
+    ref = _torch_qdq_rows(h) @ _mxfp4_dense(dq, ds)
+    assert np.max(np.abs(out - ref)) <= 1e-12 * np.max(np.abs(ref))

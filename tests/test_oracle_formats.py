@@ -118,3 +118,23 @@ def test_bf16_value(bits):
     u = np.array([bits << 16], dtype=np.uint32).view(np.float32)[0]
     assert oracle.bf16_value(np.array([bits], dtype=np.uint16))[0] == float(u)
     assert math.isfinite(float(u))
+
+
+# ------------------------------------------------------------------ MXFP4 (E2M1 + E8M0)
+# OCP Microscaling Formats (MX) v1.0: the FP4 E2M1 element values of the 16 codes (sign in
+# bit 3), and the E8M0 scale 2^(code - 127).  The blueprint's training box names MXFP4.
+OCP_E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_decode_matches_the_ocp_table():
+    got = oracle.e2m1_value(np.arange(16))
+    assert got[:8].tolist() == OCP_E2M1
+    assert got[8:].tolist() == [-v for v in OCP_E2M1]
+    assert math.copysign(1.0, got[8]) == -1.0      # code 8 is -0
+
+
+def test_e8m0_decode_matches_torch_on_every_finite_code():
+    codes = np.arange(255, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    assert np.array_equal(oracle.e8m0_value(codes), ref)
+    assert math.isnan(oracle.e8m0_value(np.array([255]))[0])
