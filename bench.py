@@ -19,8 +19,12 @@ if ROOT not in sys.path:
 
 METRIC = "MoE-layer tokens/sec + % MFMA peak (T=4096) and % HBM BW (decode)"
 HBM_PEAK_GBS = 8000.0                 # MI355X HBM3E
-MFMA_PEAK_TFLOPS = {0: 157.3, 1: 2500.0, 2: 5000.0}   # fp32, bf16, fp8 dense
-DTYPE_NAME = {0: "f32", 1: "bf16", 2: "fp8_e4m3"}
+# dense MFMA peaks by expert dtype: fp32, bf16, fp8; MXFP4 experts multiply E4M3 activations by
+# E2M1 weights, which runs at the fp8 rate
+MFMA_PEAK_TFLOPS = {0: 157.3, 1: 2500.0, 2: 5000.0, 3: 5000.0}
+DTYPE_NAME = {0: "f32", 1: "bf16", 2: "fp8_e4m3", 3: "mxfp4_e2m1"}
+# stored bytes per weight element: MXFP4 half a byte plus one E8M0 byte per 32 elements
+WEIGHT_BYTES = {0: 4, 1: 2, 2: 1, 3: 0.5 + 1 / 32}
 
 
 def log(msg):
@@ -59,12 +63,12 @@ def algorithmic(cfg, touched):
     """Algorithmic bytes and flops of one step (what the block must read, write and compute)."""
     d, f, fs, S, E, T, k = (cfg.d_model, cfg.d_ff, cfg.d_ff_shared, cfg.num_shared,
                             cfg.num_experts, cfg.num_tokens, cfg.top_k)
-    wb = {0: 4, 1: 2, 2: 1}[cfg.expert_dtype]
+    wb = WEIGHT_BYTES[cfg.expert_dtype]
     rb = 4 if cfg.router_dtype == 0 else 2
     xb = 4 if cfg.act_dtype == 0 else 2
-    step_bytes = (touched * 3 * d * f * wb + S * 3 * d * fs * wb + d * E * rb + 2 * T * d * xb)
+    step_bytes = int(touched * 3 * d * f * wb + S * 3 * d * fs * wb + d * E * rb + 2 * T * d * xb)
     step_flops = 2 * T * d * E + 6 * T * k * d * f + 6 * T * d * S * fs
-    gate_up_bytes = touched * 2 * d * f * wb + T * d * xb
+    gate_up_bytes = int(touched * 2 * d * f * wb + T * d * xb)
     gate_up_flops = 4 * T * k * d * f
     return step_bytes, step_flops, gate_up_bytes, gate_up_flops
 
@@ -92,7 +96,8 @@ def cpu_baseline(cfg, inp, n_tokens, seed=0):
         col = lambda key: [None if p is None else p.get(key) for p in parts]  # noqa: E731
         return oracle.ExpertSet(n, col("gate"), col("up"), col("down"),
                                 gate_scales=col("gate_scales"), up_scales=col("up_scales"),
-                                down_scales=col("down_scales"))
+                                down_scales=col("down_scales"),
+                                fmt="mxfp4" if cfg.expert_dtype == 3 else None)
 
     rng = np.random.default_rng(seed)
     tok = np.sort(rng.choice(cfg.num_tokens, min(n_tokens, cfg.num_tokens), replace=False))
@@ -100,7 +105,7 @@ def cpu_baseline(cfg, inp, n_tokens, seed=0):
     wr = np_storage(inp["w_router"])
     z = None if inp["logit_bias"] is None else inp["logit_bias"].cpu().numpy()
     sb = None if inp["select_bias"] is None else inp["select_bias"].cpu().numpy()
-    quant = cfg.expert_dtype == 2
+    quant = cfg.expert_dtype in (2, 3)   # E4M3 activations
 
     def host(d):
         return {k: (v.cpu().numpy() if k.endswith("scales") else np_storage(v))
@@ -162,7 +167,7 @@ def time_hash_routing(cfg, x, w, ws, steps, warmup):
     dev = x.device
     tok, table = synth.hash_routing(cfg, dev)
     T, E, k, d, A = cfg.num_tokens, cfg.num_experts, cfg.top_k, cfg.d_model, cfg.assignments
-    fp8 = cfg.expert_dtype == 2
+    fp8 = cfg.expert_dtype in (2, 3)   # E4M3 activations
     ids = torch.empty(T, k, dtype=torch.int32, device=dev)
     tw = torch.empty(T, k, dtype=torch.float32, device=dev)
     xq = torch.empty(T, d, dtype=torch.uint8, device=dev) if fp8 else None

@@ -56,8 +56,11 @@ typedef enum {
   MOE_ERR_HIP = 4                 /* a HIP launch error */
 } moe_status_t;
 
-/* Number formats (moe_config_t.*_dtype). */
-enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 };
+/* Number formats (moe_config_t.*_dtype).  MOE_MXFP4 is for expert weights only:
+ * OCP MX E2M1 elements with one E8M0 (power-of-two) scale per 32 values along
+ * the reduction axis (the blueprint's training box names MXFP4); the
+ * activations x and h are then block-scaled E4M3 as with MOE_FP8_E4M3. */
+enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 };
 
 /* Router score (moe_config_t.score). */
 enum {
@@ -78,7 +81,8 @@ typedef struct {
   int32_t renormalize;   /* 1: normalise the weights over the selected experts */
   float routed_scale;    /* gamma: routed weights are multiplied by it (2.5 / 1) */
   int32_t act_dtype;     /* storage of x and of the output: MOE_F32 or MOE_BF16 */
-  int32_t expert_dtype;  /* expert weights; MOE_FP8_E4M3 also quantises x and h */
+  int32_t expert_dtype;  /* expert weights (routed and shared); MOE_FP8_E4M3 and
+                            MOE_MXFP4 also quantise x and h to block-scaled E4M3 */
   int32_t router_dtype;  /* storage of W_r: MOE_F32 or MOE_BF16 */
   int32_t quant_block;   /* FP8 block edge; must be 128 */
   int32_t shared_gate;   /* 1: the shared experts' output is multiplied per token by
@@ -91,22 +95,26 @@ typedef struct {
 
 /* Weights in the caller's logical layout, for moe_pack_weights (device pointers).
  * FP8 weights are E4M3FN codes with one fp32 scale per 128 x 128 block, the
- * scale grid laid out [rows/128, cols/128] per expert; scales are NULL otherwise.
- * Shared pointers may be NULL when num_shared == 0. */
+ * scale grid laid out [rows/128, cols/128] per expert.  MXFP4 weights are
+ * stored N-major, the MX blocks running along the reduction axis: gate and up
+ * [E, f, d/2] bytes and down [E, d, f/2] (two E2M1 codes a byte, the lower K
+ * index in the low nibble), each with E8M0 scale bytes [E, f, d/32] /
+ * [E, d, f/32] (the shared experts likewise with S and f_s).  Scales are NULL
+ * for fp32 / bf16 weights.  Shared pointers may be NULL when num_shared == 0. */
 typedef struct {
   const void* w_router;          /* [d, E] router_dtype */
   const void* w_gate;            /* [E, d, f] */
   const void* w_up;              /* [E, d, f] */
   const void* w_down;            /* [E, f, d] */
-  const float* w_gate_scales;    /* [E, d/128, f/128] */
-  const float* w_up_scales;      /* [E, d/128, f/128] */
-  const float* w_down_scales;    /* [E, f/128, d/128] */
+  const void* w_gate_scales;     /* FP8 fp32 [E, d/128, f/128]; MXFP4 E8M0 [E, f, d/32] */
+  const void* w_up_scales;       /* as w_gate_scales */
+  const void* w_down_scales;     /* FP8 fp32 [E, f/128, d/128]; MXFP4 E8M0 [E, d, f/32] */
   const void* ws_gate;           /* [S, d, f_s] */
   const void* ws_up;             /* [S, d, f_s] */
   const void* ws_down;           /* [S, f_s, d] */
-  const float* ws_gate_scales;   /* [S, d/128, f_s/128] */
-  const float* ws_up_scales;     /* [S, d/128, f_s/128] */
-  const float* ws_down_scales;   /* [S, f_s/128, d/128] */
+  const void* ws_gate_scales;    /* as w_gate_scales with S and f_s */
+  const void* ws_up_scales;      /* as w_up_scales with S and f_s */
+  const void* ws_down_scales;    /* as w_down_scales with S and f_s */
 } moe_logical_weights_t;
 
 /* Packed buffers, indexes for moe_packed_size / moe_pack_weights. */
@@ -134,13 +142,13 @@ typedef struct {
   const float* logit_bias;
   const float* select_bias;
   const void* w_gate_up;
-  const float* w_gate_up_scales;
+  const void* w_gate_up_scales;  /* FP8: fp32; MXFP4: E8M0 bytes; NULL otherwise */
   const void* w_down;
-  const float* w_down_scales;
+  const void* w_down_scales;
   const void* ws_gate_up;
-  const float* ws_gate_up_scales;
+  const void* ws_gate_up_scales;
   const void* ws_down;
-  const float* ws_down_scales;
+  const void* ws_down_scales;
   const void* ws_gate_vec;       /* [d] router_dtype gate vector w_sg; required when
                                     shared_gate = 1 and num_shared > 0, else ignored */
 } moe_weights_t;

@@ -9,7 +9,7 @@ import os
 
 import torch
 
-from .configs import BF16, F32, FP8_E4M3, MoEConfig
+from .configs import BF16, F32, FP8_E4M3, MXFP4, MoEConfig
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 
@@ -235,7 +235,7 @@ _TORCH_ACT = {F32: torch.float32, BF16: torch.bfloat16}
 
 
 def y_dtype(cfg: MoEConfig):
-    return torch.bfloat16 if cfg.expert_dtype == FP8_E4M3 else torch.float32
+    return torch.bfloat16 if cfg.expert_dtype in (FP8_E4M3, MXFP4) else torch.float32
 
 
 def out_dtype(cfg: MoEConfig):

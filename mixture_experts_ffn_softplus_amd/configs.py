@@ -17,6 +17,10 @@ Sources for the shapes (archdiff.com comparison pages):
   blueprint's training box (FP8 with block scales) for the number format.
 * ``tiny_fp32`` -- a small fp32 layer that the oracle finishes in well under a
   second, used for parity at every step.
+* ``mxfp4_decode`` / ``mxfp4_block`` -- ``decode_bf16`` / ``fp8_block`` with the
+  experts' weights in MXFP4 (E2M1 with an E8M0 scale per 32 values along K), the
+  other format the blueprint's training box names; activations stay block-scaled
+  E4M3.
 * ``qwen_gated_bf16`` -- ``softmax_bf16`` with the Qwen3.5 shared expert as the
   shared-expert row of "Qwen3.5-397B-A17B vs Gemma 4 31B" states it: its output
   scaled by a per-token sigmoid gate of a learned d-vector before the routed sum
@@ -24,10 +28,10 @@ Sources for the shapes (archdiff.com comparison pages):
 """
 from dataclasses import dataclass, replace
 
-F32, BF16, FP8_E4M3 = 0, 1, 2
+F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
 SOFTMAX, SIGMOID, SQRT_SOFTPLUS = 0, 1, 2
 
-_DT_NAMES = {F32: "f32", BF16: "bf16", FP8_E4M3: "fp8_e4m3"}
+_DT_NAMES = {F32: "f32", BF16: "bf16", FP8_E4M3: "fp8_e4m3", MXFP4: "mxfp4"}
 
 
 @dataclass(frozen=True)
@@ -44,7 +48,7 @@ class MoEConfig:
     renormalize: int = 1
     routed_scale: float = 1.0
     act_dtype: int = BF16      # storage of x and of the block output
-    expert_dtype: int = BF16   # arithmetic of the expert GEMMs (FP8: x and h quantised)
+    expert_dtype: int = BF16   # expert weights (FP8 / MXFP4: x and h quantised to E4M3)
     router_dtype: int = BF16   # storage of W_r
     quant_block: int = 128
     seed: int = 0
@@ -89,4 +93,6 @@ PRESETS = {
         act_dtype=BF16, expert_dtype=FP8_E4M3, router_dtype=F32, seed=4),
 }
 PRESETS["qwen_gated_bf16"] = PRESETS["softmax_bf16"].with_(name="qwen_gated_bf16", shared_gate=1)
+PRESETS["mxfp4_decode"] = PRESETS["decode_bf16"].with_(name="mxfp4_decode", expert_dtype=MXFP4)
+PRESETS["mxfp4_block"] = PRESETS["fp8_block"].with_(name="mxfp4_block", expert_dtype=MXFP4)
 

@@ -38,8 +38,14 @@ template <>
 struct DT_<MOE_BF16> { static constexpr int esize = 2; };
 template <>
 struct DT_<MOE_FP8_E4M3> { static constexpr int esize = 1; };
+template <>
+struct DT_<MOE_MXFP4> { static constexpr int esize = 1; };  // A: E4M3 activations
 
 __device__ __forceinline__ int swz(int row, int ch) { return row * kBlockK + ((ch ^ (row & 7)) << 4); }
+// E2M1 weight rows hold 64 bytes per step (four 16-byte chunks).  Chunk c of row r sits at
+// slot c ^ ((r >> 2) & 3): the 16 lanes of a fragment read (16 rows, one chunk) then hit 16
+// different 16-byte bank groups.
+__device__ __forceinline__ int swz4(int row, int ch) { return row * 64 + ((ch ^ ((row >> 2) & 3)) << 4); }
 
 // Row pitch (floats) of the per-wave epilogue staging block: 16 + 4, so that the four row groups
 // a wave writes at once (rows 4q + e) fall on different banks.
@@ -57,17 +63,26 @@ struct GemmShape {
   static constexpr int WN = NW / WM;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 16, FN = TN / 16;
-  static constexpr bool kFp8 = DT == MOE_FP8_E4M3;
-  static constexpr int A_CHUNKS = BM * 8, B_CHUNKS = BN * 8;  // 16-byte chunks per step
+  // E4M3 activations with one fp32 scale per row and 128 K values (FP8 and MXFP4 experts)
+  static constexpr bool kFp8 = DT == MOE_FP8_E4M3 || DT == MOE_MXFP4;
+  // E2M1 weights with one E8M0 scale per column and 32 K values, applied inside the MFMA
+  static constexpr bool kMx = DT == MOE_MXFP4;
+  static constexpr int B_ROW = kMx ? 64 : kBlockK;    // bytes of one B row per step
+  static constexpr int A_CHUNKS = BM * 8, B_CHUNKS = BN * (B_ROW / 16);  // 16-byte chunks
   static constexpr int A_PER = (A_CHUNKS + NT - 1) / NT, B_PER = (B_CHUNKS + NT - 1) / NT;
   // LDS ring: step s multiplies out of slot s % 3 while steps s+1 and s+2 land in the others
   static constexpr int NSLOT = 3;
-  static constexpr int STAGE = (BM + BN) * kBlockK;
-  // FP8 scales per slot: BM row scales, 64 weight-block scales, 64 floats for idle waves
-  static constexpr int SCALES = kFp8 ? (BM + 128) * 4 : 0;
+  static constexpr int STAGE = BM * kBlockK + BN * B_ROW;
+  // Scale loads of a step, one 4-byte load per lane of a wave (256 bytes of LDS each): ASW
+  // waves the activation row scales (64 rows a wave), BSW waves the weight scales (FP8: one
+  // wave, a float per 16 packed rows; MXFP4: a dword of four E8M0 scales per column, 64
+  // columns a wave); any other wave loads into a spare 256 bytes
+  static constexpr int ASW = kFp8 ? (BM + 63) / 64 : 0;
+  static constexpr int BSW = kMx ? BN / 64 : kFp8 ? 1 : 0;
+  static constexpr int SCALES = kFp8 ? (ASW + BSW + 1) * 256 : 0;
   static constexpr int SLOT = STAGE + SCALES;
   // destination of the A/B loads a wave issues for nothing (when the chunks do not divide evenly
-  // over the waves; FP8 scale loads of idle waves land in the slot's own spare words)
+  // over the waves)
   static constexpr int DUMMY = (A_CHUNKS % NT || B_CHUNKS % NT) ? NW * 1024 : 0;
   static constexpr int MAIN = NSLOT * SLOT + DUMMY;
   // FP8 h quantisation: per-row maxima of each wave column, exchanged between waves
@@ -79,10 +94,11 @@ struct GemmShape {
   static constexpr int LPS = A_PER + B_PER + (kFp8 ? 1 : 0);
   // stores every wave issues in a tile's epilogue (at least; FP8 h scales come on top)
   static constexpr int EPI_STORES = EPI == kEpiStore ? FM * FN : FM * (FN / 2);
-  static_assert(FM >= 1 && FN >= 1, "tile too small for 4 waves");
-  static_assert(!kFp8 || NW >= BM / 64 + 1, "FP8 scale loads need BM / 64 + 1 waves");
+  static_assert(FM >= 1 && FN >= 1, "tile too small for its waves");
+  static_assert(!kFp8 || NW >= ASW + BSW, "scale loads need ASW + BSW waves");
   static_assert(2 * LPS < 64 && LPS + EPI_STORES < 64, "vmcnt holds at most 63");
-  static_assert(!kFp8 || (TN <= 128 && 128 % TN == 0), "FP8: two weight scales per wave");
+  static_assert(!kFp8 || kMx || (TN <= 128 && 128 % TN == 0), "FP8: two weight scales per wave");
+  static_assert(!kMx || BN % 64 == 0, "MXFP4: whole waves of weight scales");
   static_assert(EPI != kEpiSwiglu || FN % 2 == 0, "gate/up pairs must stay within one wave");
   static_assert(!(kFp8 && EPI == kEpiSwiglu) || BN == 256, "FP8 h groups need 128 h columns");
 };
@@ -99,6 +115,15 @@ struct Frags<MOE_FP8_E4M3, FM, FN> {
   i32x8 a[1][FM], b[1][FN];
   f32x4 sa[FM];
   float sb[2];
+};
+// E4M3 activations against E2M1 weights: 32 B of A and 16 B of B per lane, the lane's E8M0
+// weight scale (its column, its 32-value block) in the low byte of sbx
+template <int FM, int FN>
+struct Frags<MOE_MXFP4, FM, FN> {
+  i32x8 a[1][FM];
+  i32x4 b[1][FN];
+  f32x4 sa[FM];
+  int sbx[FN];
 };
 
 // Waves per SIMD the register allocation aims for: what the LDS footprint lets run (160 KiB
@@ -232,19 +257,29 @@ void grouped_gemm_kernel(GemmArgs a) {
     b_rs = rsrc_words(bg, static_cast<uint32_t>(static_cast<int64_t>(a.N) * ldb));
 #pragma unroll
     for (int i = 0; i < S::B_PER; ++i) {
-      const int c = tid + S::NT * i, r = c >> 3;
-      b_off[i] = c < S::B_CHUNKS ? static_cast<uint32_t>(static_cast<int64_t>(g.n0 + r) * ldb +
-                                                         (((c & 7) ^ (r & 7)) << 4))
-                                 : kOob;
+      const int c = tid + S::NT * i;
+      if constexpr (S::kMx) {  // 64-byte rows, see swz4
+        const int r = c >> 2;
+        b_off[i] = c < S::B_CHUNKS
+                       ? static_cast<uint32_t>(static_cast<int64_t>(g.n0 + r) * ldb +
+                                               (((c & 3) ^ ((r >> 2) & 3)) << 4))
+                       : kOob;
+      } else {
+        const int r = c >> 3;
+        b_off[i] = c < S::B_CHUNKS
+                       ? static_cast<uint32_t>(static_cast<int64_t>(g.n0 + r) * ldb +
+                                               (((c & 7) ^ (r & 7)) << 4))
+                       : kOob;
+      }
     }
     // an expert with one row tile is the only reader of its weights
     stream_b = GROUPED && a.b_stream && g.count == 1;
-    // FP8: wave w < BM/64 loads the row scales of rows [64w, 64w+64), wave BM/64 the weight
-    // block scales, any other wave a dummy slice
+    // E4M3 activations: wave w < ASW loads the row scales of rows [64w, 64w+64), the next BSW
+    // waves the weight scales, any other wave a dummy word
     if constexpr (S::kFp8) {
       const int kb_bytes = KB * 4;
       s_off = kOob;
-      if (wv < BM / 64) {
+      if (wv < S::ASW) {
         const uint32_t a_rows = static_cast<uint32_t>(a.a_bytes / a.lda);
         s_rs = rsrc_words(a.a_scales, a_rows * kb_bytes);
         const int r = wv * 64 + l;
@@ -256,16 +291,26 @@ void grouped_gemm_kernel(GemmArgs a) {
             if ((l >> 3) == qd) arow = select8(v, l & 7);
           }
         }
-        if (r < g.rows) s_off = static_cast<uint32_t>(arow) * kb_bytes;
+        if (r < g.rows && r < BM) s_off = static_cast<uint32_t>(arow) * kb_bytes;
         s_dst = STAGE_BYTES + wv * 256;
-      } else if (wv == BM / 64) {
-        s_rs = rsrc_words(a.b_scales + g.group * a.bs_group_stride,
-                          static_cast<uint32_t>((a.N / 16) * kb_bytes));
-        if (l < BN / 16) s_off = static_cast<uint32_t>(g.n0 / 16 + l) * kb_bytes;
-        s_dst = STAGE_BYTES + BM * 4;
+      } else if (wv < S::ASW + S::BSW) {
+        const int bw = wv - S::ASW;
+        if constexpr (S::kMx) {
+          // E8M0 scales [N, K/32] bytes per group: column n's four scales of a step are one
+          // dword at n * K/32 + 4 * step
+          const int kb32 = a.K / 32;
+          s_rs = rsrc_words(a.b_e8m0 + g.group * a.be_group_stride,
+                            static_cast<uint32_t>(a.N) * kb32);
+          s_off = static_cast<uint32_t>(g.n0 + bw * 64 + l) * kb32;
+        } else {
+          s_rs = rsrc_words(a.b_scales + g.group * a.bs_group_stride,
+                            static_cast<uint32_t>((a.N / 16) * kb_bytes));
+          if (l < BN / 16) s_off = static_cast<uint32_t>(g.n0 / 16 + l) * kb_bytes;
+        }
+        s_dst = STAGE_BYTES + wv * 256;
       } else {
-        s_rs = rsrc_words(a.b_scales, 4);
-        s_dst = STAGE_BYTES + BM * 4 + 256;  // the slot's spare 256 bytes
+        s_rs = rsrc_words(a.a_scales, 4);
+        s_dst = STAGE_BYTES + (S::ASW + S::BSW) * 256;  // the slot's spare 256 bytes
       }
     }
   };
@@ -286,7 +331,7 @@ void grouped_gemm_kernel(GemmArgs a) {
     iss_slot = iss_slot + 1 == S::NSLOT ? 0 : iss_slot + 1;
     ++iss_s;
     const uint32_t as = static_cast<uint32_t>(step < a_steps ? step : step - a_steps) * kBlockK;
-    const uint32_t bs = static_cast<uint32_t>(step) * kBlockK;
+    const uint32_t bs = static_cast<uint32_t>(step) * S::B_ROW;
 #pragma unroll
     for (int i = 0; i < S::A_PER; ++i) lds_dma<16, false>(a_rs, lds_ptr(slot, a_dst[i]), a_off[i], as);
     if (stream_b) {  // weights read by one tile only: do not keep them in the caches
@@ -314,7 +359,26 @@ void grouped_gemm_kernel(GemmArgs a) {
   auto load = [&](F& f, int slot) {
     const uint8_t* sa = smem + slot * S::SLOT;
     const uint8_t* sb = sa + BM * kBlockK;
-    if constexpr (DT == MOE_FP8_E4M3) {
+    if constexpr (S::kMx) {
+      const float* ss = reinterpret_cast<const float*>(sa + STAGE_BYTES);
+      const uint32_t* bsc = reinterpret_cast<const uint32_t*>(sa + STAGE_BYTES + S::ASW * 256);
+#pragma unroll
+      for (int i = 0; i < S::FM; ++i) {
+        // A in the MFMA's K order for an E2M1 partner: bytes 0-15 of the lane hold K
+        // 16*kq.., bytes 16-31 K 64+16*kq..
+        const int r = wm * S::TM + i * 16 + lr;
+        const i32x4 lo4 = *reinterpret_cast<const i32x4*>(sa + swz(r, kq));
+        const i32x4 hi4 = *reinterpret_cast<const i32x4*>(sa + swz(r, 4 + kq));
+        f.a[0][i] = i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        f.sa[i] = *reinterpret_cast<const f32x4*>(ss + wm * S::TM + i * 16 + 4 * kq);
+      }
+#pragma unroll
+      for (int j = 0; j < S::FN; ++j) {
+        const int r = wn * S::TN + j * 16 + lr;  // E2M1: K 32*kq.. of column r
+        f.b[0][j] = *reinterpret_cast<const i32x4*>(sb + swz4(r, kq));
+        f.sbx[j] = static_cast<int>((bsc[r] >> (8 * kq)) & 0xFFu);
+      }
+    } else if constexpr (DT == MOE_FP8_E4M3) {
       const float* ss = reinterpret_cast<const float*>(sa + STAGE_BYTES);
 #pragma unroll
       for (int i = 0; i < S::FM; ++i) {
@@ -333,8 +397,8 @@ void grouped_gemm_kernel(GemmArgs a) {
       }
       // a wave's columns lie in one 128-wide weight block per gate/up half (even/odd
       // 16-row blocks of the packed rows), so two weight scales cover all its fragments
-      f.sb[0] = ss[BM + wn * S::TN / 16];
-      f.sb[1] = ss[BM + wn * S::TN / 16 + 1];
+      f.sb[0] = ss[S::ASW * 64 + wn * S::TN / 16];
+      f.sb[1] = ss[S::ASW * 64 + wn * S::TN / 16 + 1];
     } else {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -376,7 +440,7 @@ void grouped_gemm_kernel(GemmArgs a) {
   // one just issued), and f is refilled from slot `next` as soon as each fragment's last MFMA
   // has issued: A row block i after its row of MFMAs, B column j after MFMA (last row, j).
   auto mma_refill_fp8 = [&](F& f, int next) {
-    if constexpr (S::kFp8) {
+    if constexpr (S::kFp8 && !S::kMx) {
       const uint8_t* sa = smem + next * S::SLOT;
       const uint8_t* sb = sa + BM * kBlockK;
       const float* ss = reinterpret_cast<const float*>(sa + STAGE_BYTES);
@@ -404,7 +468,7 @@ void grouped_gemm_kernel(GemmArgs a) {
             const i32x4 lo4 = *reinterpret_cast<const i32x4*>(sb + swz(r, 2 * kq));
             const i32x4 hi4 = *reinterpret_cast<const i32x4*>(sb + swz(r, 2 * kq + 1));
             f.b[0][j] = i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-            if (j < 2) sb_next[j] = ss[BM + wn * S::TN / 16 + j];
+            if (j < 2) sb_next[j] = ss[S::ASW * 64 + wn * S::TN / 16 + j];
           }
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // the MFMA
           __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // then the VALU work
@@ -427,6 +491,54 @@ void grouped_gemm_kernel(GemmArgs a) {
             fmaf(prev[e], qp[(S::FN - 1) & 1][e], acc[S::FM - 1][S::FN - 1][e]);
       f.sb[0] = sb_next[0];
       f.sb[1] = sb_next[1];
+    }
+  };
+
+  // MXFP4 step: one scaled MFMA per (row block, column block) takes E4M3 activations and E2M1
+  // weights with the lane's E8M0 weight scale applied inside; its fp32 partial is promoted
+  // with the row's activation scale.  Same issue order and refill points as the FP8 step.
+  auto mma_refill_mx = [&](F& f, int next) {
+    if constexpr (S::kMx) {
+      const uint8_t* sa = smem + next * S::SLOT;
+      const uint8_t* sb = sa + BM * kBlockK;
+      const float* ss = reinterpret_cast<const float*>(sa + STAGE_BYTES);
+      const uint32_t* bsc = reinterpret_cast<const uint32_t*>(sa + STAGE_BYTES + S::ASW * 256);
+      f32x4 prev = f32x4{0.f, 0.f, 0.f, 0.f}, qp = prev;
+#pragma unroll
+      for (int i = 0; i < S::FM; ++i) {
+        const f32x4 qs = f.sa[i];
+#pragma unroll
+        for (int j = 0; j < S::FN; ++j) {
+          const f32x4 cur = mfma_mx(f.a[0][i], f.b[0][j], f.sbx[j]);
+          if (i + j > 0) {
+            const int pi = j > 0 ? i : i - 1, pj = j > 0 ? j - 1 : S::FN - 1;
+            const f32x4& qq = j > 0 ? qs : qp;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[pi][pj][e] = fmaf(prev[e], qq[e], acc[pi][pj][e]);
+          }
+          prev = cur;
+          if (i == S::FM - 1) {  // B column j is done: refill it and its scale
+            const int r = wn * S::TN + j * 16 + lr;
+            f.b[0][j] = *reinterpret_cast<const i32x4*>(sb + swz4(r, kq));
+            f.sbx[j] = static_cast<int>((bsc[r] >> (8 * kq)) & 0xFFu);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // the MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // then the VALU work
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // then the LDS reads
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        qp = qs;
+        // row block i is done with its A fragment and row scales
+        const int r = wm * S::TM + i * 16 + lr;
+        const i32x4 lo4 = *reinterpret_cast<const i32x4*>(sa + swz(r, kq));
+        const i32x4 hi4 = *reinterpret_cast<const i32x4*>(sa + swz(r, 4 + kq));
+        f.a[0][i] = i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        f.sa[i] = *reinterpret_cast<const f32x4*>(ss + wm * S::TM + i * 16 + 4 * kq);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc[S::FM - 1][S::FN - 1][e] = fmaf(prev[e], qp[e], acc[S::FM - 1][S::FN - 1][e]);
     }
   };
 
@@ -579,6 +691,8 @@ void grouped_gemm_kernel(GemmArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // MFMA
       }
       __builtin_amdgcn_sched_group_barrier(0x008, NM - PER * NR, 0);
+    } else if constexpr (S::kMx) {
+      mma_refill_mx(cur, next);
     } else {
       mma_refill_fp8(cur, next);
     }
@@ -609,7 +723,6 @@ void grouped_gemm_kernel(GemmArgs a) {
 
 int gemm_bm(int dtype, int epi, int avg_rows) {
   if (dtype == MOE_F32) return 32;
-  if (dtype == MOE_FP8_E4M3) return 128;
   if (avg_rows <= 16) return 16;
   if (avg_rows <= 32) return 32;
   if (avg_rows <= 48) return 64;
@@ -652,13 +765,24 @@ template <int DT, int EPI, bool G>
 static hipError_t launch_dt(int bm, const GemmArgs& a, int max_tiles, hipStream_t s) {
   if constexpr (DT == MOE_F32) {
     return launch_one<DT, 32, 128, EPI, G>(a, max_tiles, s);
-  } else if constexpr (DT == MOE_FP8_E4M3) {
-    // 8 waves, two per SIMD: one wave's promotion and loads overlap the other's MFMAs.  The
-    // SwiGLU output (N = 2 d_ff, d_ff a multiple of 128) always takes the wide tile.
-    if constexpr (EPI == kEpiSwiglu) return launch_one<DT, 128, 256, EPI, G>(a, max_tiles, s);
-    else
-      return a.N % 256 == 0 ? launch_one<DT, 128, 256, EPI, G>(a, max_tiles, s)
-                            : launch_one<DT, 128, 128, EPI, G>(a, max_tiles, s);
+  } else if constexpr (DT == MOE_FP8_E4M3 || DT == MOE_MXFP4) {
+    // E4M3 activations.  The SwiGLU output (N = 2 d_ff, d_ff a multiple of 128) always takes
+    // the 256-wide tile so each tile quantises whole 128-value groups of h; 8 waves there, two
+    // per SIMD, one wave's promotion and loads overlapping the other's MFMAs.  Rows per tile
+    // follow the rows per expert (decode shapes take 16).
+    auto wide = [&](auto bm_tag) {
+      constexpr int BMv = decltype(bm_tag)::value;
+      if constexpr (EPI == kEpiSwiglu) return launch_one<DT, BMv, 256, EPI, G>(a, max_tiles, s);
+      else
+        return a.N % 256 == 0 ? launch_one<DT, BMv, 256, EPI, G>(a, max_tiles, s)
+                              : launch_one<DT, BMv, 128, EPI, G>(a, max_tiles, s);
+    };
+    switch (bm) {
+      case 16: return wide(std::integral_constant<int, 16>{});
+      case 32: return wide(std::integral_constant<int, 32>{});
+      case 64: return wide(std::integral_constant<int, 64>{});
+      default: return wide(std::integral_constant<int, 128>{});
+    }
   } else {
     switch (bm) {
       case 16: return launch_one<DT, 16, 128, EPI, G>(a, max_tiles, s);
@@ -686,6 +810,7 @@ hipError_t launch_grouped_gemm(int dtype, int epi, int bm, const GemmArgs& a, in
   switch (dtype) {
     case MOE_F32: return launch_epi<MOE_F32>(epi, bm, a, max_tiles, s);
     case MOE_BF16: return launch_epi<MOE_BF16>(epi, bm, a, max_tiles, s);
+    case MOE_MXFP4: return launch_epi<MOE_MXFP4>(epi, bm, a, max_tiles, s);
     default: return launch_epi<MOE_FP8_E4M3>(epi, bm, a, max_tiles, s);
   }
 }

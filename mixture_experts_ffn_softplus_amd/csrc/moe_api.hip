@@ -13,16 +13,22 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-bool is_fp8(const moe_config_t* c) { return c->expert_dtype == MOE_FP8_E4M3; }
+// E4M3 activations (x and h block-scaled per 128 values): FP8 and MXFP4 experts
+bool is_fp8(const moe_config_t* c) {
+  return c->expert_dtype == MOE_FP8_E4M3 || c->expert_dtype == MOE_MXFP4;
+}
+bool is_mx(const moe_config_t* c) { return c->expert_dtype == MOE_MXFP4; }
 
-// Bytes of one element of an expert operand (weights and h), of x / out, and of y_perm.
-int weight_bytes(const moe_config_t* c) {
+// Bytes of one h element (the expert activations), of x / out, and of y_perm.
+int h_bytes(const moe_config_t* c) {
   return c->expert_dtype == MOE_F32 ? 4 : c->expert_dtype == MOE_BF16 ? 2 : 1;
 }
+// Bytes of one packed weight row of K elements (E2M1: two a byte).
+int64_t wrow(const moe_config_t* c, int64_t K) { return is_mx(c) ? K / 2 : K * h_bytes(c); }
 int act_bytes(const moe_config_t* c) { return c->act_dtype == MOE_F32 ? 4 : 2; }
-// y_perm: fp32 unless the experts are FP8.  A bf16 y_perm would add a third bf16 rounding
+// y_perm: fp32 unless the activations are E4M3.  A bf16 y_perm would add a third bf16 rounding
 // (after h and the output) to a budget the output rounding alone half fills.
-int y_bytes(const moe_config_t* c) { return c->expert_dtype == MOE_FP8_E4M3 ? 2 : 4; }
+int y_bytes(const moe_config_t* c) { return is_fp8(c) ? 2 : 4; }
 
 // Router columns padded to the GEMM's N tiles: 128 for small E, else 256 (the wide 8-wave tile).
 int e_pad(const moe_config_t* c) {
@@ -56,10 +62,10 @@ int routed_bm(const moe_config_t* c) {
   int64_t avg = c->num_experts > 0 ? assignments(c) / c->num_experts : 0;
   return gemm_bm(c->expert_dtype, kEpiSwiglu, static_cast<int>(avg < 1 << 20 ? avg : 1 << 20));
 }
+// The shared experts see every token: their rows per tile follow T.
 int shared_bm(const moe_config_t* c) {
-  if (c->expert_dtype != MOE_BF16) return gemm_bm(c->expert_dtype, kEpiSwiglu, 0);
-  int T = c->num_tokens;
-  return T <= 16 ? 16 : T <= 32 ? 32 : T <= 64 ? 64 : 128;
+  if (c->expert_dtype == MOE_F32) return gemm_bm(MOE_F32, kEpiSwiglu, 0);
+  return gemm_bm(c->expert_dtype, kEpiSwiglu, c->num_tokens);
 }
 int64_t routed_max_tiles(const moe_config_t* c) {
   int bm = routed_bm(c);
@@ -79,12 +85,12 @@ moe_status_t check_config(const moe_config_t* c) {
   if (!isfinite(c->routed_scale)) return MOE_ERR_INVALID_ARGUMENT;
   const int dts[3] = {c->act_dtype, c->expert_dtype, c->router_dtype};
   for (int v : dts)
-    if (v < MOE_F32 || v > MOE_FP8_E4M3) return MOE_ERR_INVALID_ARGUMENT;
+    if (v < MOE_F32 || v > MOE_MXFP4) return MOE_ERR_INVALID_ARGUMENT;
   const bool ok_types =
       (c->act_dtype == MOE_F32 && c->expert_dtype == MOE_F32 && c->router_dtype == MOE_F32) ||
       (c->act_dtype == MOE_BF16 && c->expert_dtype == MOE_BF16 && c->router_dtype == MOE_BF16) ||
-      (c->act_dtype == MOE_BF16 && c->expert_dtype == MOE_FP8_E4M3 &&
-       c->router_dtype != MOE_FP8_E4M3);
+      (c->act_dtype == MOE_BF16 && is_fp8(c) &&
+       (c->router_dtype == MOE_F32 || c->router_dtype == MOE_BF16));
   if (!ok_types) return MOE_ERR_UNSUPPORTED;
   if (is_fp8(c) && c->quant_block != 128) return MOE_ERR_UNSUPPORTED;
   if (c->d_model % 128 || c->d_ff % 128 || (c->num_shared > 0 && c->d_ff_shared % 128))
@@ -103,7 +109,7 @@ WsLayout ws_layout(const moe_config_t* c) {
   WsLayout L{};
   const int64_t A = assignments(c), T = c->num_tokens, d = c->d_model, f = c->d_ff;
   const int64_t fs = shared_width(c);
-  const int hb = weight_bytes(c);
+  const int hb = h_bytes(c);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -150,7 +156,7 @@ moe_status_t check_weights(const moe_config_t* c, const moe_weights_t* w, bool r
   if (!w) return MOE_ERR_INVALID_ARGUMENT;
   if (router && !w->w_router) return MOE_ERR_INVALID_ARGUMENT;
   if (routed && (!w->w_gate_up || !w->w_down)) return MOE_ERR_INVALID_ARGUMENT;
-  if (routed && is_fp8(c) && (!w->w_gate_up_scales || !w->w_down_scales))
+  if (routed && is_fp8(c) && (!w->w_gate_up_scales || !w->w_down_scales))  // both formats
     return MOE_ERR_INVALID_ARGUMENT;
   if (shared && c->num_shared > 0) {
     if (!w->ws_gate_up || !w->ws_down) return MOE_ERR_INVALID_ARGUMENT;
@@ -222,12 +228,25 @@ hipError_t mark(hipEvent_t* ev, int i, hipStream_t s) {
   return ev ? hipEventRecord(ev[i], s) : hipSuccess;
 }
 
+// The weight scales of one packed operand [N, K] per group: FP8 one fp32 per 16 packed rows
+// and 128 K values; MXFP4 one E8M0 byte per row and 32 K values.
+void set_weight_scales(const moe_config_t* c, GemmArgs& g, const void* scales, int64_t N,
+                       int64_t K) {
+  if (is_mx(c)) {
+    g.b_e8m0 = static_cast<const uint8_t*>(scales);
+    g.be_group_stride = N * (K / 32);
+  } else {
+    g.b_scales = static_cast<const float*>(scales);
+    g.bs_group_stride = (N / 16) * (K / 128);
+  }
+}
+
 hipError_t do_expert_ffn(const moe_config_t* c, const void* xa, const float* xs,
                          const int32_t* offsets, const int32_t* perm, const moe_weights_t* w,
                          void* y, void* ws, hipStream_t s, hipEvent_t* ev = nullptr) {
   const WsLayout L = ws_layout(c);
   const int64_t A = assignments(c), d = c->d_model, f = c->d_ff;
-  const int wb = weight_bytes(c);
+  const int hb = h_bytes(c);
   const int bm = routed_bm(c);
   int4* tiles = at<int4>(ws, L.tiles);
   int32_t* tcount = at<int32_t>(ws, L.tiles_count);
@@ -243,17 +262,16 @@ hipError_t do_expert_ffn(const moe_config_t* c, const void* xa, const float* xs,
   g.a_map = perm;
   g.a_scales = xs;
   g.B = w->w_gate_up;
-  g.ldb = d * wb;
+  g.ldb = wrow(c, d);
   g.b_group_stride = 2 * f * g.ldb;
-  g.b_scales = w->w_gate_up_scales;
-  g.bs_group_stride = (2 * f / 16) * (d / 128);
+  set_weight_scales(c, g, w->w_gate_up_scales, 2 * f, d);
   g.K = static_cast<int>(d);
   g.N = static_cast<int>(2 * f);
   g.tiles = tiles;
   g.tiles_count = tcount;
   g.M = static_cast<int>(A);
   g.out = at<uint8_t>(ws, L.h);
-  g.ldo = f * wb;
+  g.ldo = f * hb;
   g.out_scales = is_fp8(c) ? at<float>(ws, L.h_scales) : nullptr;
   // an expert whose rows fit one tile streams its weights past the caches
   g.b_stream = 1;
@@ -263,15 +281,14 @@ hipError_t do_expert_ffn(const moe_config_t* c, const void* xa, const float* xs,
 
   GemmArgs h{};
   h.A = at<uint8_t>(ws, L.h);
-  h.lda = f * wb;
+  h.lda = f * hb;
   h.a_bytes = A * h.lda;
   h.a_map = nullptr;
   h.a_scales = is_fp8(c) ? at<float>(ws, L.h_scales) : nullptr;
   h.B = w->w_down;
-  h.ldb = f * wb;
+  h.ldb = wrow(c, f);
   h.b_group_stride = d * h.ldb;
-  h.b_scales = w->w_down_scales;
-  h.bs_group_stride = (d / 16) * (f / 128);
+  set_weight_scales(c, h, w->w_down_scales, d, f);
   h.K = static_cast<int>(f);
   h.N = static_cast<int>(d);
   h.tiles = tiles;
@@ -286,12 +303,43 @@ hipError_t do_expert_ffn(const moe_config_t* c, const void* xa, const float* xs,
   return e;
 }
 
+// MXFP4 experts, logical N-major rows (see moe_logical_weights_t): gate/up rows [f, d/2] and
+// scale rows [f, d/32] interleaved 16 at a time; down rows [d, f/2] and [d, f/32], the shared
+// experts' rows concatenated along K.
+hipError_t pack_mx(const moe_config_t* c, const moe_logical_weights_t* lw, void* const* packed,
+                   hipStream_t s) {
+  const int d = c->d_model, f = c->d_ff, E = c->num_experts;
+  hipError_t e = launch_pack_rows_gate_up(lw->w_gate, lw->w_up, packed[MOE_PACK_GATE_UP], f, 1,
+                                          E, d / 2, s);
+  if (e == hipSuccess)
+    e = launch_pack_rows_gate_up(lw->w_gate_scales, lw->w_up_scales,
+                                 packed[MOE_PACK_GATE_UP_SCALES], f, 1, E, d / 32, s);
+  if (e == hipSuccess)
+    e = launch_pack_rows_concat(lw->w_down, packed[MOE_PACK_DOWN], d, 1, E, f / 2, s);
+  if (e == hipSuccess)
+    e = launch_pack_rows_concat(lw->w_down_scales, packed[MOE_PACK_DOWN_SCALES], d, 1, E,
+                                f / 32, s);
+  if (e != hipSuccess || c->num_shared == 0) return e;
+  const int S = c->num_shared, fs = c->d_ff_shared;
+  e = launch_pack_rows_gate_up(lw->ws_gate, lw->ws_up, packed[MOE_PACK_SHARED_GATE_UP], fs, S, 1,
+                               d / 2, s);
+  if (e == hipSuccess)
+    e = launch_pack_rows_gate_up(lw->ws_gate_scales, lw->ws_up_scales,
+                                 packed[MOE_PACK_SHARED_GATE_UP_SCALES], fs, S, 1, d / 32, s);
+  if (e == hipSuccess)
+    e = launch_pack_rows_concat(lw->ws_down, packed[MOE_PACK_SHARED_DOWN], d, S, 1, fs / 2, s);
+  if (e == hipSuccess)
+    e = launch_pack_rows_concat(lw->ws_down_scales, packed[MOE_PACK_SHARED_DOWN_SCALES], d, S, 1,
+                                fs / 32, s);
+  return e;
+}
+
 hipError_t do_combine(const moe_config_t* c, const void* xa, const float* xs, const void* y,
                       const int32_t* inv, const float* tw, const moe_weights_t* w, void* out,
                       void* ws, hipStream_t s, hipEvent_t* ev = nullptr) {
   const WsLayout L = ws_layout(c);
   const int64_t T = c->num_tokens, d = c->d_model, F = shared_width(c);
-  const int wb = weight_bytes(c);
+  const int hb = h_bytes(c);
   const int bm = shared_bm(c);
   const int max_tiles = static_cast<int>((T + bm - 1) / bm);
   hipError_t e = hipSuccess;
@@ -303,13 +351,13 @@ hipError_t do_combine(const moe_config_t* c, const void* xa, const float* xs, co
     g.a_bytes = T * g.lda;
     g.a_scales = xs;
     g.B = w->ws_gate_up;
-    g.ldb = d * wb;
-    g.b_scales = w->ws_gate_up_scales;
+    g.ldb = wrow(c, d);
+    set_weight_scales(c, g, w->ws_gate_up_scales, 2 * F, d);
     g.K = static_cast<int>(d);
     g.N = static_cast<int>(2 * F);
     g.M = static_cast<int>(T);
     g.out = at<uint8_t>(ws, L.hs);
-    g.ldo = F * wb;
+    g.ldo = F * hb;
     g.out_scales = is_fp8(c) ? at<float>(ws, L.hs_scales) : nullptr;
     e = launch_grouped_gemm(c->expert_dtype, kEpiSwiglu, bm, g, max_tiles, s);
     if (e == hipSuccess) e = mark(ev, MOE_STAGE_SHARED_GATE_UP, s);
@@ -317,12 +365,12 @@ hipError_t do_combine(const moe_config_t* c, const void* xa, const float* xs, co
     shared_out = at<float>(ws, L.so);
     GemmArgs h{};
     h.A = at<uint8_t>(ws, L.hs);
-    h.lda = F * wb;
+    h.lda = F * hb;
     h.a_bytes = T * h.lda;
     h.a_scales = is_fp8(c) ? at<float>(ws, L.hs_scales) : nullptr;
     h.B = w->ws_down;
-    h.ldb = F * wb;
-    h.b_scales = w->ws_down_scales;
+    h.ldb = wrow(c, F);
+    set_weight_scales(c, h, w->ws_down_scales, d, F);
     h.K = static_cast<int>(F);
     h.N = static_cast<int>(d);
     h.M = static_cast<int>(T);
@@ -385,22 +433,25 @@ size_t moe_workspace_size(const moe_config_t* cfg) {
 size_t moe_packed_size(const moe_config_t* c, int which) {
   if (check_config(c) != MOE_OK) return 0;
   const size_t d = c->d_model, f = c->d_ff, E = c->num_experts, F = shared_width(c);
-  const size_t wb = weight_bytes(c);
-  const bool q = is_fp8(c);
+  const bool q = c->expert_dtype == MOE_FP8_E4M3, mx = is_mx(c);
+  // FP8: fp32 per 16 packed rows and 128 K; MXFP4: an E8M0 byte per row and 32 K
+  auto sc = [&](size_t N, size_t K) -> size_t {
+    return q ? (N / 16) * (K / 128) * 4 : mx ? N * (K / 32) : 0;
+  };
   switch (which) {
     case MOE_PACK_ROUTER: {
       int k = router_kind(c);
       size_t eb = k == kRouterF32 ? 4 : k == kRouterBF16 ? 2 : 4;  // hi/lo: two bf16 planes
       return static_cast<size_t>(e_pad(c)) * d * eb;
     }
-    case MOE_PACK_GATE_UP: return E * 2 * f * d * wb;
-    case MOE_PACK_GATE_UP_SCALES: return q ? E * (2 * f / 16) * (d / 128) * 4 : 0;
-    case MOE_PACK_DOWN: return E * d * f * wb;
-    case MOE_PACK_DOWN_SCALES: return q ? E * (d / 16) * (f / 128) * 4 : 0;
-    case MOE_PACK_SHARED_GATE_UP: return 2 * F * d * wb;
-    case MOE_PACK_SHARED_GATE_UP_SCALES: return q ? (2 * F / 16) * (d / 128) * 4 : 0;
-    case MOE_PACK_SHARED_DOWN: return d * F * wb;
-    case MOE_PACK_SHARED_DOWN_SCALES: return q ? (d / 16) * (F / 128) * 4 : 0;
+    case MOE_PACK_GATE_UP: return E * 2 * f * wrow(c, d);
+    case MOE_PACK_GATE_UP_SCALES: return E * sc(2 * f, d);
+    case MOE_PACK_DOWN: return E * d * wrow(c, f);
+    case MOE_PACK_DOWN_SCALES: return E * sc(d, f);
+    case MOE_PACK_SHARED_GATE_UP: return 2 * F * wrow(c, d);
+    case MOE_PACK_SHARED_GATE_UP_SCALES: return sc(2 * F, d);
+    case MOE_PACK_SHARED_DOWN: return d * wrow(c, F);
+    case MOE_PACK_SHARED_DOWN_SCALES: return sc(d, F);
     default: return 0;
   }
 }
@@ -413,7 +464,7 @@ moe_status_t moe_pack_weights(const moe_config_t* c, const moe_logical_weights_t
   for (int i = 0; i < MOE_PACK_COUNT; ++i)
     if (moe_packed_size(c, i) > 0 && !packed[i]) return MOE_ERR_INVALID_ARGUMENT;
   if (!lw->w_router || !lw->w_gate || !lw->w_up || !lw->w_down) return MOE_ERR_INVALID_ARGUMENT;
-  const bool q = is_fp8(c);
+  const bool q = is_fp8(c);  // FP8 and MXFP4 weights both carry scales
   if (q && (!lw->w_gate_scales || !lw->w_up_scales || !lw->w_down_scales))
     return MOE_ERR_INVALID_ARGUMENT;
   if (c->num_shared > 0) {
@@ -421,22 +472,24 @@ moe_status_t moe_pack_weights(const moe_config_t* c, const moe_logical_weights_t
     if (q && (!lw->ws_gate_scales || !lw->ws_up_scales || !lw->ws_down_scales))
       return MOE_ERR_INVALID_ARGUMENT;
   }
-  const int d = c->d_model, f = c->d_ff, E = c->num_experts, wb = weight_bytes(c);
+  const int d = c->d_model, f = c->d_ff, E = c->num_experts, wb = h_bytes(c);
   hipError_t e;
   const int rk = router_kind(c);
   e = launch_pack_router(lw->w_router, c->router_dtype == MOE_F32 ? 4 : 2,
                          rk == kRouterBF16HiLo, packed[MOE_PACK_ROUTER], d, E, e_pad(c), s);
   if (e != hipSuccess) return MOE_ERR_HIP;
+  if (is_mx(c)) return hip_status(pack_mx(c, lw, packed, s));
   e = launch_pack_gate_up(lw->w_gate, lw->w_up, packed[MOE_PACK_GATE_UP], d, f, 1, E, wb, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = launch_pack_down(lw->w_down, packed[MOE_PACK_DOWN], d, f, 1, E, wb, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (q) {
-    e = launch_pack_scales_gate_up(lw->w_gate_scales, lw->w_up_scales,
+    e = launch_pack_scales_gate_up(static_cast<const float*>(lw->w_gate_scales),
+                                   static_cast<const float*>(lw->w_up_scales),
                                    static_cast<float*>(packed[MOE_PACK_GATE_UP_SCALES]), d, f, 1,
                                    E, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
-    e = launch_pack_scales_down(lw->w_down_scales,
+    e = launch_pack_scales_down(static_cast<const float*>(lw->w_down_scales),
                                 static_cast<float*>(packed[MOE_PACK_DOWN_SCALES]), d, f, 1, E, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
@@ -448,11 +501,12 @@ moe_status_t moe_pack_weights(const moe_config_t* c, const moe_logical_weights_t
     e = launch_pack_down(lw->ws_down, packed[MOE_PACK_SHARED_DOWN], d, fs, S, 1, wb, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
     if (q) {
-      e = launch_pack_scales_gate_up(lw->ws_gate_scales, lw->ws_up_scales,
+      e = launch_pack_scales_gate_up(static_cast<const float*>(lw->ws_gate_scales),
+                                     static_cast<const float*>(lw->ws_up_scales),
                                      static_cast<float*>(packed[MOE_PACK_SHARED_GATE_UP_SCALES]),
                                      d, fs, S, 1, s);
       if (e != hipSuccess) return MOE_ERR_HIP;
-      e = launch_pack_scales_down(lw->ws_down_scales,
+      e = launch_pack_scales_down(static_cast<const float*>(lw->ws_down_scales),
                                   static_cast<float*>(packed[MOE_PACK_SHARED_DOWN_SCALES]), d, fs,
                                   S, 1, s);
       if (e != hipSuccess) return MOE_ERR_HIP;

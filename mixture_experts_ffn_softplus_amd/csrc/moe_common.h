@@ -81,6 +81,15 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma_fp8(i32x8 a, i32x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
+// E4M3 x E2M1 (format selectors 0 and 4), K = 128, from zero.  A: 32 bytes per lane, bytes
+// 0-15 holding K 16*(l/16).. and bytes 16-31 K 64+16*(l/16).. of row l%16; B: 16 bytes per
+// lane, K 32*(l/16)..+31 of column l%16, two codes a byte, the lower K in the low nibble.  The
+// lane's E8M0 byte `sb` scales B's 32 values (A's scale field is 127 = 2^0).
+__device__ __forceinline__ f32x4 mfma_mx(i32x8 a, i32x4 b, int sb) {
+  const i32x8 b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b8, f32x4{0.f, 0.f, 0.f, 0.f}, 0,
+                                                          4, 0, 127, 0, sb);
+}
 
 // ----------------------------------------------------------------------------- buffer loads
 // A buffer resource covers [base, base + bytes); a load past `bytes` returns zeros instead of

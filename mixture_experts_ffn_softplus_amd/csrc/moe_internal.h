@@ -57,8 +57,10 @@ struct GemmArgs {
   int64_t b_group_stride;     // bytes per group
   int64_t ldb;                // bytes between rows of B
   int b_stream;               // B of a group with one row tile: load it non-temporally
-  const float* b_scales;      // FP8: [N/128, K/128] per group
+  const float* b_scales;      // FP8: [N/16, K/128] per group (one per 16 packed rows)
   int64_t bs_group_stride;    // floats per group
+  const uint8_t* b_e8m0;      // MXFP4: E8M0 scales [N, K/32] per group
+  int64_t be_group_stride;    // bytes per group
   int K, N;
   // tiles of rows: a device list {group, first row, rows} (grouped), or one group of M rows
   const int4* tiles;          // null: one group, rows [0, M)
@@ -73,7 +75,8 @@ struct GemmArgs {
   int a_steps;
 };
 
-// dtype: MOE_F32 / MOE_BF16 / MOE_FP8_E4M3 (operands).  max_tiles: upper bound of the device
+// dtype: MOE_F32 / MOE_BF16 / MOE_FP8_E4M3 / MOE_MXFP4 (E4M3 activations, E2M1 weights).
+// max_tiles: upper bound of the device
 // tile count (grouped) for sizing the persistent grid.
 int gemm_bm(int dtype, int epi, int avg_rows);
 hipError_t launch_grouped_gemm(int dtype, int epi, int bm, const GemmArgs& a, int max_tiles,
@@ -114,6 +117,13 @@ hipError_t launch_pack_gate_up(const void* gate, const void* up, void* dst, int 
 // sources logical [C, N].
 hipError_t launch_pack_down(const void* down, void* dst, int N, int C, int sub, int groups,
                             int esize, hipStream_t s);
+// MXFP4 (N-major rows of `row_bytes`, a multiple of 4): gate/up rows [C] per source expert
+// interleaved 16 at a time into [2F, row] per group (F = sub * C, `sub` sources a group), and
+// down rows [N] per source concatenated along K into [N, sub * row] per group.
+hipError_t launch_pack_rows_gate_up(const void* gate, const void* up, void* dst, int C, int sub,
+                                    int groups, int row_bytes, hipStream_t s);
+hipError_t launch_pack_rows_concat(const void* src, void* dst, int N, int sub, int groups,
+                                   int row_bytes, hipStream_t s);
 // Router [d, E] -> [E_pad, d] (rows >= E zero).  hilo: fp32 source split into bf16 hi and
 // lo = bf16(w - hi), one [E_pad, 2d] bf16 matrix; otherwise the element type is kept.
 hipError_t launch_pack_router(const void* wr, int esize, int hilo, void* dst, int d, int E,

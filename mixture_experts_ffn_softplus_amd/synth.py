@@ -17,6 +17,10 @@ Recipe (all logical layouts row-major):
   the block is zero) and codes = the draw over the scale, cast to E4M3FN by
   torch.  The quantised weights are the inputs; how they were made is not part
   of the block.
+* MXFP4 weights: the fp32 draw stored N-major; each 32 consecutive values
+  along K get the E8M0 scale 2^(floor(log2 amax) - 2) (2 = the largest E2M1
+  exponent; amax = 0 gives 2^-127), and each value over its scale is rounded
+  to the nearest E2M1 value (ties to the smaller magnitude, saturating at 6).
 * Selection-only bias b_e ~ U(-r, r) (fp32) when the workload asks for one.
 * Shared-expert gate vector w_sg [d] ~ N(0, 1/d), stored in the router's dtype,
   when the workload gates its shared experts.
@@ -35,7 +39,7 @@ import math
 
 import torch
 
-from .configs import BF16, F32, FP8_E4M3, MoEConfig
+from .configs import BF16, F32, FP8_E4M3, MXFP4, MoEConfig
 
 TAG_X, TAG_ROUTER, TAG_SELECT_BIAS = 1, 2, 3
 TAG_GATE, TAG_UP, TAG_DOWN = 4, 5, 6
@@ -91,6 +95,26 @@ def _store_fp8(t: torch.Tensor, block: int):
     return q.reshape(*lead, R, C).contiguous(), scale.contiguous()
 
 
+_E2M1 = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def _store_mxfp4(t: torch.Tensor):
+    """fp32 [K, N] -> (codes uint8 [N, K/2], two E2M1 codes a byte with the lower K index in
+    the low nibble; E8M0 scales uint8 [N, K/32])."""
+    w = t.t().contiguous()                                   # [N, K]
+    N, K = w.shape
+    b = w.reshape(N, K // 32, 32)
+    amax = b.abs().amax(-1)
+    e = torch.where(amax > 0, torch.floor(torch.log2(amax.clamp_min(1e-38))) - 2,
+                    torch.full_like(amax, -127.0)).clamp(-127, 127)
+    v = b / torch.exp2(e)[..., None]
+    grid = torch.tensor(_E2M1, device=t.device)
+    mag = (v.abs()[..., None] - grid).abs().argmin(-1)       # nearest, lower index on ties
+    codes = (mag | torch.where(v < 0, 8, 0)).to(torch.uint8).reshape(N, K)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).contiguous()
+    return packed, (e + 127).to(torch.uint8).contiguous()
+
+
 def tokens(cfg: MoEConfig, device="cpu") -> torch.Tensor:
     x = _normal((cfg.num_tokens, cfg.d_model), 1.0, device, cfg.seed, TAG_X)
     return _store(x, F32 if cfg.act_dtype == F32 else BF16)
@@ -122,6 +146,10 @@ def _expert(cfg: MoEConfig, shared: bool, e: int, device):
     g = _normal((d, f), 1.0 / math.sqrt(d), device, cfg.seed, tg, e)
     u = _normal((d, f), 1.0 / math.sqrt(d), device, cfg.seed, tu, e)
     dn = _normal((f, d), 1.0 / math.sqrt(f), device, cfg.seed, td, e)
+    if cfg.expert_dtype == MXFP4:
+        (gq, gs), (uq, us), (dq, ds) = (_store_mxfp4(t) for t in (g, u, dn))
+        return {"gate": gq, "up": uq, "down": dq, "gate_scales": gs, "up_scales": us,
+                "down_scales": ds}
     if cfg.expert_dtype == FP8_E4M3:
         (gq, gs), (uq, us), (dq, ds) = (_store_fp8(t, cfg.quant_block) for t in (g, u, dn))
         return {"gate": gq, "up": uq, "down": dq, "gate_scales": gs, "up_scales": us,
@@ -131,7 +159,8 @@ def _expert(cfg: MoEConfig, shared: bool, e: int, device):
 
 
 def routed_expert(cfg: MoEConfig, e: int, device="cpu"):
-    """Weights of routed expert e: gate/up [d,f], down [f,d] (+ FP8 block scales)."""
+    """Weights of routed expert e: gate/up [d,f], down [f,d] (+ FP8 block scales); MXFP4:
+    gate/up [f, d/2] and down [d, f/2] codes with E8M0 scales [f, d/32] / [d, f/32]."""
     return _expert(cfg, False, e, device)
 
 

@@ -4,9 +4,10 @@ import torch
 
 
 def np_storage(t: torch.Tensor) -> np.ndarray:
-    """A stored tensor as the oracle reads it: float32, bf16 bits (uint16) or E4M3 codes (uint8)."""
+    """A stored tensor as the oracle reads it: float32, bf16 bits (uint16), E4M3 codes or packed
+    E2M1 codes (uint8)."""
     t = t.detach().contiguous().cpu()
-    if t.dtype == torch.float32:
+    if t.dtype in (torch.float32, torch.uint8):
         return t.numpy()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)

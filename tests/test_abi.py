@@ -77,6 +77,9 @@ def test_status_strings():
     ("d_model", 200, api.MOE_ERR_UNSUPPORTED),           # not a multiple of 128
     ("d_ff", 96, api.MOE_ERR_UNSUPPORTED),
     ("expert_dtype", BF16, api.MOE_ERR_UNSUPPORTED),     # f32 activations with bf16 experts
+    ("expert_dtype", 3, api.MOE_ERR_UNSUPPORTED),        # MXFP4 experts need bf16 activations
+    ("expert_dtype", 4, api.MOE_ERR_INVALID_ARGUMENT),   # no such format
+    ("router_dtype", 3, api.MOE_ERR_UNSUPPORTED),        # MXFP4 is for expert weights only
     ("act_dtype", 5, api.MOE_ERR_INVALID_ARGUMENT),
 ])
 def test_config_errors_return_status_without_launch(field, value, status):

@@ -20,7 +20,7 @@ import torch
 
 import oracle
 from mixture_experts_ffn_softplus_amd import PRESETS, api, synth
-from mixture_experts_ffn_softplus_amd.configs import BF16, F32, FP8_E4M3, SIGMOID, SOFTMAX, \
+from mixture_experts_ffn_softplus_amd.configs import BF16, F32, FP8_E4M3, MXFP4, SIGMOID, SOFTMAX, \
     SQRT_SOFTPLUS
 from tests._common import exact64, np_storage, rel_err
 from tests._gpu import Layer, check_layer, oracle_block, oracle_route_on
@@ -68,6 +68,24 @@ SMALL = {
         d_ff=512, num_shared=1, d_ff_shared=512, router_dtype=BF16, shared_gate=1, seed=20),
     "f32_gated_shared": PRESETS["tiny_fp32"].with_(name="f32_gated_shared", num_tokens=90,
                                                    num_shared=1, shared_gate=1, seed=21),
+    # decode-like rows per expert: the E4M3-activation GEMMs take 16-row tiles
+    "fp8_decode_rows": PRESETS["fp8_block"].with_(name="fp8_decode_rows", num_tokens=24,
+                                                  d_model=384, num_experts=32, top_k=4,
+                                                  d_ff=512, num_shared=1, d_ff_shared=512,
+                                                  seed=22),
+    # MXFP4 experts (E2M1 weights, E8M0 scales per 32 along K; E4M3 activations)
+    "mxfp4_f32_router": PRESETS["mxfp4_block"].with_(name="mxfp4_f32_router", num_tokens=150,
+                                                     d_model=256, num_experts=10, top_k=3,
+                                                     d_ff=512, num_shared=1, d_ff_shared=512,
+                                                     seed=23),
+    "mxfp4_decode_rows": PRESETS["mxfp4_decode"].with_(name="mxfp4_decode_rows", num_tokens=40,
+                                                       d_model=384, num_experts=24, top_k=4,
+                                                       d_ff=512, num_shared=2, d_ff_shared=256,
+                                                       seed=24),
+    "mxfp4_many_rows": PRESETS["mxfp4_block"].with_(name="mxfp4_many_rows", num_tokens=600,
+                                                    d_model=512, num_experts=4, top_k=2,
+                                                    d_ff=768, num_shared=1, d_ff_shared=512,
+                                                    router_dtype=BF16, seed=25),
 }
 
 
@@ -80,7 +98,7 @@ def test_small_layers(name):
     check_layer(Layer(SMALL[name]))
 
 
-@pytest.mark.parametrize("name", ["fp8_f32_router", "fp8_bf16_router"])
+@pytest.mark.parametrize("name", ["fp8_f32_router", "fp8_bf16_router", "mxfp4_f32_router"])
 def test_fp8_activation_codes_bit_exact(name):
     cfg = SMALL[name]
     layer = Layer(cfg)
@@ -276,7 +294,8 @@ def test_identity_like_experts_reproduce_input():
 
 @pytest.mark.parametrize("name,sample", [("decode_bf16", 64), ("softmax_bf16", 24),
                                          ("softplus_bf16", 12), ("fp8_block", 16),
-                                         ("qwen_gated_bf16", 16)])
+                                         ("qwen_gated_bf16", 16), ("mxfp4_decode", 64),
+                                         ("mxfp4_block", 16)])
 def test_full_size_workloads(name, sample):
     cfg = PRESETS[name]
     layer = Layer(cfg)
