@@ -43,9 +43,10 @@ struct DT_<MOE_MXFP4> { static constexpr int esize = 1; };  // A: E4M3 activatio
 
 __device__ __forceinline__ int swz(int row, int ch) { return row * kBlockK + ((ch ^ (row & 7)) << 4); }
 // E2M1 weight rows hold 64 bytes per step (four 16-byte chunks).  Chunk c of row r sits at
-// slot c ^ ((r >> 2) & 3): the 16 lanes of a fragment read (16 rows, one chunk) then hit 16
-// different 16-byte bank groups.
-__device__ __forceinline__ int swz4(int row, int ch) { return row * 64 + ((ch ^ ((row >> 2) & 3)) << 4); }
+// slot c ^ ((r >> 1) & 2).  A 128-bit LDS read is served for lanes 0-7 and 16-23 together (and
+// likewise for the other half-groups) -- eight rows read at chunk c and at chunk c+1 -- and this
+// puts those 16 accesses on 16 different 16-byte bank groups.
+__device__ __forceinline__ int swz4(int row, int ch) { return row * 64 + ((ch ^ ((row >> 1) & 2)) << 4); }
 
 // Row pitch (floats) of the per-wave epilogue staging block: 16 + 4, so that the four row groups
 // a wave writes at once (rows 4q + e) fall on different banks.
@@ -262,7 +263,7 @@ void grouped_gemm_kernel(GemmArgs a) {
         const int r = c >> 2;
         b_off[i] = c < S::B_CHUNKS
                        ? static_cast<uint32_t>(static_cast<int64_t>(g.n0 + r) * ldb +
-                                               (((c & 3) ^ ((r >> 2) & 3)) << 4))
+                                               (((c & 3) ^ ((r >> 1) & 2)) << 4))
                        : kOob;
       } else {
         const int r = c >> 3;
@@ -379,20 +380,23 @@ void grouped_gemm_kernel(GemmArgs a) {
         f.sbx[j] = static_cast<int>((bsc[r] >> (8 * kq)) & 0xFFu);
       }
     } else if constexpr (DT == MOE_FP8_E4M3) {
+      // chunks kq and 4 + kq, the MFMA's own K order (A and B agree, so any order within the
+      // 128-value block would do; this one keeps the lanes kq and kq + 1 that one 128-bit LDS
+      // read serves together on different bank groups)
       const float* ss = reinterpret_cast<const float*>(sa + STAGE_BYTES);
 #pragma unroll
       for (int i = 0; i < S::FM; ++i) {
         const int r = wm * S::TM + i * 16 + lr;
-        const i32x4 lo4 = *reinterpret_cast<const i32x4*>(sa + swz(r, 2 * kq));
-        const i32x4 hi4 = *reinterpret_cast<const i32x4*>(sa + swz(r, 2 * kq + 1));
+        const i32x4 lo4 = *reinterpret_cast<const i32x4*>(sa + swz(r, kq));
+        const i32x4 hi4 = *reinterpret_cast<const i32x4*>(sa + swz(r, 4 + kq));
         f.a[0][i] = i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
         f.sa[i] = *reinterpret_cast<const f32x4*>(ss + wm * S::TM + i * 16 + 4 * kq);
       }
 #pragma unroll
       for (int j = 0; j < S::FN; ++j) {
         const int r = wn * S::TN + j * 16 + lr;
-        const i32x4 lo4 = *reinterpret_cast<const i32x4*>(sb + swz(r, 2 * kq));
-        const i32x4 hi4 = *reinterpret_cast<const i32x4*>(sb + swz(r, 2 * kq + 1));
+        const i32x4 lo4 = *reinterpret_cast<const i32x4*>(sb + swz(r, kq));
+        const i32x4 hi4 = *reinterpret_cast<const i32x4*>(sb + swz(r, 4 + kq));
         f.b[0][j] = i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
       }
       // a wave's columns lie in one 128-wide weight block per gate/up half (even/odd
@@ -465,8 +469,8 @@ void grouped_gemm_kernel(GemmArgs a) {
           prev = cur;
           if (i == S::FM - 1) {  // B column j is done: refill it
             const int r = wn * S::TN + j * 16 + lr;
-            const i32x4 lo4 = *reinterpret_cast<const i32x4*>(sb + swz(r, 2 * kq));
-            const i32x4 hi4 = *reinterpret_cast<const i32x4*>(sb + swz(r, 2 * kq + 1));
+            const i32x4 lo4 = *reinterpret_cast<const i32x4*>(sb + swz(r, kq));
+            const i32x4 hi4 = *reinterpret_cast<const i32x4*>(sb + swz(r, 4 + kq));
             f.b[0][j] = i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
             if (j < 2) sb_next[j] = ss[S::ASW * 64 + wn * S::TN / 16 + j];
           }
@@ -479,8 +483,8 @@ void grouped_gemm_kernel(GemmArgs a) {
         qp[1] = qs[1];
         // row block i is done with its A fragment and row scales
         const int r = wm * S::TM + i * 16 + lr;
-        const i32x4 lo4 = *reinterpret_cast<const i32x4*>(sa + swz(r, 2 * kq));
-        const i32x4 hi4 = *reinterpret_cast<const i32x4*>(sa + swz(r, 2 * kq + 1));
+        const i32x4 lo4 = *reinterpret_cast<const i32x4*>(sa + swz(r, kq));
+        const i32x4 hi4 = *reinterpret_cast<const i32x4*>(sa + swz(r, 4 + kq));
         f.a[0][i] = i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
         f.sa[i] = *reinterpret_cast<const f32x4*>(ss + wm * S::TM + i * 16 + 4 * kq);
         __builtin_amdgcn_sched_barrier(0);
