@@ -27,18 +27,24 @@ struct CombineGate {
   int vec_f32, x_kind;
 };
 
-// Eight consecutive values of a row of bf16 (16 B) or fp32 (32 B) elements.
-template <bool F32>
+// Eight consecutive values of a row of bf16 (16 B) or fp32 (32 B) elements; NT: non-temporal
+// loads.  The expert rows are read once; measured on MI355X, non-temporal loads speed up the
+// bf16 rows (FP8 experts: 2.95 GB, 668 -> 585 us) but slow down the fp32 rows of the bf16
+// experts (0.67 GB, 183 -> 216 us), so only the former use them.
+template <bool F32, bool NT = false>
 __device__ __forceinline__ void load8(const uint8_t* p, float* v) {
   if constexpr (F32) {
-    const f32x4 a = reinterpret_cast<const f32x4*>(p)[0], b = reinterpret_cast<const f32x4*>(p)[1];
+    const f32x4* q = reinterpret_cast<const f32x4*>(p);
+    const f32x4 a = NT ? __builtin_nontemporal_load(q) : q[0];
+    const f32x4 b = NT ? __builtin_nontemporal_load(q + 1) : q[1];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       v[q] = a[q];
       v[4 + q] = b[q];
     }
   } else {
-    const i32x4 r = *reinterpret_cast<const i32x4*>(p);
+    const i32x4* q = reinterpret_cast<const i32x4*>(p);
+    const i32x4 r = NT ? __builtin_nontemporal_load(q) : q[0];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t bits = static_cast<uint32_t>(r[q]);
@@ -105,7 +111,9 @@ __global__ __launch_bounds__(kCombineMaxThreads) void combine_kernel(
     float v[8];
     if (base) {
       const f32x4* b = reinterpret_cast<const f32x4*>(base + static_cast<int64_t>(t) * d + c * 8);
-      const f32x4 b0 = b[0], b1 = b[1];
+      // read once as well: non-temporal with the bf16 rows (FP8 experts), as measured above
+      const f32x4 b0 = Y_F32 ? b[0] : __builtin_nontemporal_load(b);
+      const f32x4 b1 = Y_F32 ? b[1] : __builtin_nontemporal_load(b + 1);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         v[q] = G * b0[q];
@@ -120,7 +128,7 @@ __global__ __launch_bounds__(kCombineMaxThreads) void combine_kernel(
       float yv[kCombineBatch][8];
 #pragma unroll
       for (int u = 0; u < kCombineBatch; ++u)
-        load8<Y_F32>(yc + s_row[j0 + u] * ldy, yv[u]);
+        load8<Y_F32, !Y_F32>(yc + s_row[j0 + u] * ldy, yv[u]);
 #pragma unroll
       for (int u = 0; u < kCombineBatch; ++u) {
         const float wj = s_w[j0 + u];
