@@ -34,29 +34,65 @@ __device__ __forceinline__ float sigma_family_score(int score, float l) {
   return static_cast<float>(s);
 }
 
+// Order-preserving 64-bit selection key of one expert: the fp32 key's bits mapped so that
+// unsigned order is numeric order (-0 folded into +0 first, so equal keys stay equal), above
+// the bitwise complement of the expert id, so that the unsigned maximum is the largest key
+// and, among equal keys, the lower expert id.  0 marks "not a candidate".
+__device__ __forceinline__ uint64_t select_key(float key, int e) {
+  const uint32_t b = __float_as_uint(key + 0.0f);
+  const uint32_t u = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return (static_cast<uint64_t>(u) << 32) | static_cast<uint32_t>(~e);
+}
+
+// max(v, v moved by one DPP lane pattern) over the 64-bit key; lanes outside ROW_MASK, or
+// whose source lane is out of range, see 0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint64_t dpp_max(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(v), CTRL, ROW_MASK,
+                                                  0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(v >> 32), CTRL,
+                                                  ROW_MASK, 0xF, false);
+  const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+  return o > v ? o : v;
+}
+
+// The wave's largest key, wave-uniform: within each row of 16 lanes by quad swaps and the
+// half-row and row mirrors, across rows by the row broadcasts into lane 63.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+  v = dpp_max<0xB1>(v);         // quad_perm [1,0,3,2]
+  v = dpp_max<0x4E>(v);         // quad_perm [2,3,0,1]
+  v = dpp_max<0x141>(v);        // row_half_mirror
+  v = dpp_max<0x140>(v);        // row_mirror
+  v = dpp_max<0x142, 0xA>(v);   // row_bcast15 into rows 1 and 3
+  v = dpp_max<0x143, 0xC>(v);   // row_bcast31 into rows 2 and 3
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), 63);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), 63);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 // Top-k of one token over `row[0..E)` (LDS or global), executed by one full wave.
 __device__ void topk_row(const float* row, int t, const RouteArgs& a) {
   const int l = lane_id();
-  float key[kMaxPerLane], val[kMaxPerLane];
+  uint64_t key[kMaxPerLane];
+  float val[kMaxPerLane];
 #pragma unroll
   for (int i = 0; i < kMaxPerLane; ++i) {
     int e = l + kWave * i;
-    key[i] = -INFINITY;
+    key[i] = 0;
     val[i] = 0.0f;
     if (e < a.E) {
       const float lg = a.logit_bias ? __fadd_rn(row[e], a.logit_bias[e]) : row[e];
       if (a.score == MOE_SCORE_SOFTMAX) {
-        key[i] = lg;
+        key[i] = select_key(lg, e);
         val[i] = lg;
       } else {
         float s = sigma_family_score(a.score, lg);
         float b = a.select_bias ? a.select_bias[e] : 0.0f;
         val[i] = s;
-        key[i] = __fadd_rn(s, b);
+        key[i] = select_key(__fadd_rn(s, b), e);
       }
     }
   }
-  uint32_t taken = 0;
   int my_id = 0;
   float my_val = 0.0f;
   if (a.table) {
@@ -71,34 +107,29 @@ __device__ void topk_row(const float* row, int t, const RouteArgs& a) {
       my_val = a.score == MOE_SCORE_SOFTMAX ? lg : sigma_family_score(a.score, lg);
     }
   }
+  // k rounds: each lane's largest remaining key, the wave's largest of those; its owner lane
+  // drops it and lane j keeps the winner of round j
   for (int j = 0; j < (a.table ? 0 : a.k); ++j) {
-    float bk = -INFINITY, bv = 0.0f;
-    int be = 0x7fffffff;
+    uint64_t best = 0;
+    float bv = 0.0f;
 #pragma unroll
     for (int i = 0; i < kMaxPerLane; ++i) {
-      int e = l + kWave * i;
-      bool ok = e < a.E && !((taken >> i) & 1u);
-      if (ok && (key[i] > bk || (key[i] == bk && e < be))) {
-        bk = key[i];
-        be = e;
-        bv = val[i];
-      }
+      const bool gt = key[i] > best;
+      best = gt ? key[i] : best;
+      bv = gt ? val[i] : bv;
     }
+    const uint64_t win = wave_max_key(best);
+    const int we = static_cast<int>(~static_cast<uint32_t>(win));
+    const int owner = we & (kWave - 1);
+    const float wv = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(bv), owner));
+    if (l == owner) {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      float ok_ = __shfl_xor(bk, o, kWave);
-      int oe = __shfl_xor(be, o, kWave);
-      float ov = __shfl_xor(bv, o, kWave);
-      if (ok_ > bk || (ok_ == bk && oe < be)) {
-        bk = ok_;
-        be = oe;
-        bv = ov;
-      }
+      for (int i = 0; i < kMaxPerLane; ++i)
+        if (i == (we >> 6)) key[i] = 0;
     }
-    if ((be & (kWave - 1)) == l) taken |= 1u << (be >> 6);
     if (l == j) {
-      my_id = be;
-      my_val = bv;
+      my_id = we;
+      my_val = wv;
     }
   }
   float w;
