@@ -111,11 +111,16 @@ struct Frags {
   using V = typename std::conditional<DT == MOE_BF16, bf16x8, f32x4>::type;
   V a[2][FM], b[2][FN];
 };
+// E4M3: index [p] is the set of steps of parity p.  Row blocks 0 .. FM-2 of A (and their row
+// scales) live in set 0 only and are refilled in place once their row of MFMAs has issued; the
+// last row block, the B fragments and the two weight scales alternate between the sets, the
+// next step's set read at the start of the step (so no fragment read is left to wait for at
+// the step's end).  Elements never touched are dropped by the compiler.
 template <int FM, int FN>
 struct Frags<MOE_FP8_E4M3, FM, FN> {
-  i32x8 a[1][FM], b[1][FN];
-  f32x4 sa[FM];
-  float sb[2];
+  i32x8 a[2][FM], b[2][FN];
+  f32x4 sa[2][FM];
+  float sb[2][2];
 };
 // E4M3 activations against E2M1 weights: 32 B of A and 16 B of B per lane, the lane's E8M0
 // weight scale (its column, its 32-value block) in the low byte of sbx
@@ -322,28 +327,48 @@ void grouped_gemm_kernel(GemmArgs a) {
   };
   // Issue one step.  Past the last tile the loads repeat the last tile's bytes (or zeros) into
   // slots no one reads, so every wave keeps the same count of loads in flight for the waits.
+  // issue_begin advances to the next step (and tile); issue_load(n) issues its n-th of the LPS
+  // loads, so that a caller can spread them between MFMAs.
   int iss_t = 0, iss_s = 0, iss_slot = 0;
-  auto issue = [&]() {
+  int q_slot = 0;
+  uint32_t q_as = 0, q_bs = 0, q_ss = 0;
+  auto issue_begin = [&]() __attribute__((always_inline)) {
     if (iss_s == KB) {
       iss_s = 0;
       if (++iss_t < n_my) setup(iss_t);
     }
-    const int slot = iss_slot, step = iss_s;
+    const int step = iss_s;
+    q_slot = iss_slot;
     iss_slot = iss_slot + 1 == S::NSLOT ? 0 : iss_slot + 1;
     ++iss_s;
-    const uint32_t as = static_cast<uint32_t>(step < a_steps ? step : step - a_steps) * kBlockK;
-    const uint32_t bs = static_cast<uint32_t>(step) * S::B_ROW;
+    q_as = static_cast<uint32_t>(step < a_steps ? step : step - a_steps) * kBlockK;
+    q_bs = static_cast<uint32_t>(step) * S::B_ROW;
+    q_ss = static_cast<uint32_t>(step) * 4;
+  };
+  // nt: the weights' loads are non-temporal (stream_b of the step being issued)
+  auto issue_load = [&](int n, auto nt) __attribute__((always_inline)) {
+    if (n < S::A_PER) {
+      lds_dma<16, false>(a_rs, lds_ptr(q_slot, a_dst[n]), a_off[n], q_as);
+    } else if (n < S::A_PER + S::B_PER) {
+      const int i = n - S::A_PER;
+      lds_dma<16, decltype(nt)::value>(b_rs, lds_ptr(q_slot, b_dst[i]), b_off[i], q_bs);
+    } else if constexpr (S::kFp8) {
+      lds_dma<4, false>(s_rs, lds_ptr(q_slot, s_dst), s_off, q_ss);
+    }
+  };
+  // (issue and epilogue are called from both parities of the step: forced inline, so the
+  // accumulators and fragments stay in registers)
+  constexpr std::true_type kStream{};  // weights read by one tile only: not kept in the caches
+  constexpr std::false_type kKeep{};
+  auto issue = [&]() __attribute__((always_inline)) {
+    issue_begin();
+    if (stream_b) {
 #pragma unroll
-    for (int i = 0; i < S::A_PER; ++i) lds_dma<16, false>(a_rs, lds_ptr(slot, a_dst[i]), a_off[i], as);
-    if (stream_b) {  // weights read by one tile only: do not keep them in the caches
-#pragma unroll
-      for (int i = 0; i < S::B_PER; ++i) lds_dma<16, true>(b_rs, lds_ptr(slot, b_dst[i]), b_off[i], bs);
+      for (int n = 0; n < S::LPS; ++n) issue_load(n, kStream);
     } else {
 #pragma unroll
-      for (int i = 0; i < S::B_PER; ++i) lds_dma<16, false>(b_rs, lds_ptr(slot, b_dst[i]), b_off[i], bs);
+      for (int n = 0; n < S::LPS; ++n) issue_load(n, kKeep);
     }
-    if constexpr (S::kFp8)
-      lds_dma<4, false>(s_rs, lds_ptr(slot, s_dst), s_off, static_cast<uint32_t>(step) * 4);
   };
 
   // ---------------------------------------------------------------- fragments and MFMAs
@@ -355,6 +380,14 @@ void grouped_gemm_kernel(GemmArgs a) {
       for (int j = 0; j < S::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
   zero_acc();
+  // One E4M3 fragment of row r of an LDS tile: chunks kq and 4 + kq, the MFMA's own K order (A
+  // and B agree, so any order within the 128-value block would do; this one keeps the lanes kq
+  // and kq + 1 that one 128-bit LDS read serves together on different bank groups).
+  auto frag_e4m3 = [&](const uint8_t* tile, int r) {
+    const i32x4 lo4 = *reinterpret_cast<const i32x4*>(tile + swz(r, kq));
+    const i32x4 hi4 = *reinterpret_cast<const i32x4*>(tile + swz(r, 4 + kq));
+    return i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+  };
   // Operand fragments of one step, read from its LDS slot into registers one step ahead of
   // the MFMAs that use them.
   auto load = [&](F& f, int slot) {
@@ -379,30 +412,19 @@ void grouped_gemm_kernel(GemmArgs a) {
         f.b[0][j] = *reinterpret_cast<const i32x4*>(sb + swz4(r, kq));
         f.sbx[j] = static_cast<int>((bsc[r] >> (8 * kq)) & 0xFFu);
       }
-    } else if constexpr (DT == MOE_FP8_E4M3) {
-      // chunks kq and 4 + kq, the MFMA's own K order (A and B agree, so any order within the
-      // 128-value block would do; this one keeps the lanes kq and kq + 1 that one 128-bit LDS
-      // read serves together on different bank groups)
+    } else if constexpr (DT == MOE_FP8_E4M3) {  // set 0 of every fragment
       const float* ss = reinterpret_cast<const float*>(sa + STAGE_BYTES);
 #pragma unroll
       for (int i = 0; i < S::FM; ++i) {
-        const int r = wm * S::TM + i * 16 + lr;
-        const i32x4 lo4 = *reinterpret_cast<const i32x4*>(sa + swz(r, kq));
-        const i32x4 hi4 = *reinterpret_cast<const i32x4*>(sa + swz(r, 4 + kq));
-        f.a[0][i] = i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-        f.sa[i] = *reinterpret_cast<const f32x4*>(ss + wm * S::TM + i * 16 + 4 * kq);
+        f.a[0][i] = frag_e4m3(sa, wm * S::TM + i * 16 + lr);
+        f.sa[0][i] = *reinterpret_cast<const f32x4*>(ss + wm * S::TM + i * 16 + 4 * kq);
       }
 #pragma unroll
-      for (int j = 0; j < S::FN; ++j) {
-        const int r = wn * S::TN + j * 16 + lr;
-        const i32x4 lo4 = *reinterpret_cast<const i32x4*>(sb + swz(r, kq));
-        const i32x4 hi4 = *reinterpret_cast<const i32x4*>(sb + swz(r, 4 + kq));
-        f.b[0][j] = i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-      }
+      for (int j = 0; j < S::FN; ++j) f.b[0][j] = frag_e4m3(sb, wn * S::TN + j * 16 + lr);
       // a wave's columns lie in one 128-wide weight block per gate/up half (even/odd
       // 16-row blocks of the packed rows), so two weight scales cover all its fragments
-      f.sb[0] = ss[S::ASW * 64 + wn * S::TN / 16];
-      f.sb[1] = ss[S::ASW * 64 + wn * S::TN / 16 + 1];
+      f.sb[0][0] = ss[S::ASW * 64 + wn * S::TN / 16];
+      f.sb[0][1] = ss[S::ASW * 64 + wn * S::TN / 16 + 1];
     } else {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -436,30 +458,37 @@ void grouped_gemm_kernel(GemmArgs a) {
               acc[i][j] = mfma_f32(f.a[s][i][e], f.b[s][j][e], acc[i][j]);
     }  // FP8: mma_refill_fp8
   };
-  // FP8 step: one E4M3 MFMA covers exactly one 128-deep scale block; its fp32 partial is
-  // promoted with the row's activation scale times the block's weight scale.  Written in
-  // issue order: MFMA n is issued before partial n-1 is promoted (sched_barrier fences each
-  // MFMA with the promotion of the previous one, and sched_group_barrier puts the MFMA first
-  // inside the fence, so the promotion waits on an MFMA that has long finished instead of the
-  // one just issued), and f is refilled from slot `next` as soon as each fragment's last MFMA
-  // has issued: A row block i after its row of MFMAs, B column j after MFMA (last row, j).
-  auto mma_refill_fp8 = [&](F& f, int next) {
+  // FP8 step (steps of parity P use fragment set P, see Frags): one E4M3 MFMA covers exactly one
+  // 128-deep scale block; its fp32 partial is promoted with the row's activation scale times the
+  // block's weight scale.  Written in issue order: MFMA n is issued before partial n-1 is
+  // promoted (sched_barrier fences each MFMA with the promotion of the previous one, and
+  // sched_group_barrier puts the MFMA first inside the fence, so the promotion waits on an MFMA
+  // that has long finished instead of the one just issued).  The next step's reads from slot
+  // `next` ride along: its B fragments (set 1-P) one per MFMA of the first row block, its last
+  // row block and weight scales in the second, and row block i-1 in place (set 0) once row
+  // block i has started.
+  auto mma_refill_fp8 = [&](F& f, int next, auto parity) {
     if constexpr (S::kFp8 && !S::kMx) {
+      constexpr int P = decltype(parity)::value, Q = 1 - P, L = S::FM - 1;
+      // where the next step's last row block and weight scales are read
+      constexpr int XI = S::FM > 1 ? 1 : 0;
+      constexpr int XJ_A = S::FM > 1 ? (S::FN > 1 ? 1 : 0) : S::FN - 1;
+      constexpr int XJ_S = S::FM > 1 ? (S::FN > 2 ? 2 : S::FN - 1) : S::FN - 1;
       const uint8_t* sa = smem + next * S::SLOT;
       const uint8_t* sb = sa + BM * kBlockK;
       const float* ss = reinterpret_cast<const float*>(sa + STAGE_BYTES);
       f32x4 prev = f32x4{0.f, 0.f, 0.f, 0.f};
       f32x4 qs[2], qp[2];
-      float sb_next[2];
 #pragma unroll
       for (int i = 0; i < S::FM; ++i) {
+        const int ai = i == L ? P : 0;  // constant after unrolling
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) qs[h][e] = f.sa[i][e] * f.sb[h];
+          for (int e = 0; e < 4; ++e) qs[h][e] = f.sa[ai][i][e] * f.sb[P][h];
 #pragma unroll
         for (int j = 0; j < S::FN; ++j) {
-          const f32x4 cur = mfma_fp8(f.a[0][i], f.b[0][j], f32x4{0.f, 0.f, 0.f, 0.f});
+          const f32x4 cur = mfma_fp8(f.a[ai][i], f.b[P][j], f32x4{0.f, 0.f, 0.f, 0.f});
           if (i + j > 0) {
             const int pi = j > 0 ? i : i - 1, pj = j > 0 ? j - 1 : S::FN - 1;
             const f32x4& qq = j > 0 ? qs[pj & 1] : qp[pj & 1];
@@ -467,12 +496,19 @@ void grouped_gemm_kernel(GemmArgs a) {
             for (int e = 0; e < 4; ++e) acc[pi][pj][e] = fmaf(prev[e], qq[e], acc[pi][pj][e]);
           }
           prev = cur;
-          if (i == S::FM - 1) {  // B column j is done: refill it
-            const int r = wn * S::TN + j * 16 + lr;
-            const i32x4 lo4 = *reinterpret_cast<const i32x4*>(sb + swz(r, kq));
-            const i32x4 hi4 = *reinterpret_cast<const i32x4*>(sb + swz(r, 4 + kq));
-            f.b[0][j] = i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-            if (j < 2) sb_next[j] = ss[S::ASW * 64 + wn * S::TN / 16 + j];
+          if (i * S::FN + j < S::LPS) issue_load(i * S::FN + j, kKeep);  // step g+3's loads
+          if (i == 0) f.b[Q][j] = frag_e4m3(sb, wn * S::TN + j * 16 + lr);
+          if (i == XI && j == XJ_A) {
+            f.a[Q][L] = frag_e4m3(sa, wm * S::TM + L * 16 + lr);
+            f.sa[Q][L] = *reinterpret_cast<const f32x4*>(ss + wm * S::TM + L * 16 + 4 * kq);
+          }
+          if (i == XI && j == XJ_S) {
+            f.sb[Q][0] = ss[S::ASW * 64 + wn * S::TN / 16];
+            f.sb[Q][1] = ss[S::ASW * 64 + wn * S::TN / 16 + 1];
+          }
+          if (j == 0 && i > 0 && i - 1 < L) {  // row block i-1 is done with its fragment
+            f.a[0][i - 1] = frag_e4m3(sa, wm * S::TM + (i - 1) * 16 + lr);
+            f.sa[0][i - 1] = *reinterpret_cast<const f32x4*>(ss + wm * S::TM + (i - 1) * 16 + 4 * kq);
           }
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // the MFMA
           __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // then the VALU work
@@ -481,20 +517,13 @@ void grouped_gemm_kernel(GemmArgs a) {
         }
         qp[0] = qs[0];
         qp[1] = qs[1];
-        // row block i is done with its A fragment and row scales
-        const int r = wm * S::TM + i * 16 + lr;
-        const i32x4 lo4 = *reinterpret_cast<const i32x4*>(sa + swz(r, kq));
-        const i32x4 hi4 = *reinterpret_cast<const i32x4*>(sa + swz(r, 4 + kq));
-        f.a[0][i] = i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-        f.sa[i] = *reinterpret_cast<const f32x4*>(ss + wm * S::TM + i * 16 + 4 * kq);
-        __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int n = S::FM * S::FN; n < S::LPS; ++n) issue_load(n, kKeep);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         acc[S::FM - 1][S::FN - 1][e] =
             fmaf(prev[e], qp[(S::FN - 1) & 1][e], acc[S::FM - 1][S::FN - 1][e]);
-      f.sb[0] = sb_next[0];
-      f.sb[1] = sb_next[1];
     }
   };
 
@@ -560,7 +589,7 @@ void grouped_gemm_kernel(GemmArgs a) {
     // LDS operations of one wave complete in order: the read sees the writes above
     return *reinterpret_cast<const f32x4*>(stage + srow * kEpiPitch + scol);
   };
-  auto epilogue = [&](int t) {
+  auto epilogue = [&](int t) __attribute__((always_inline)) {
     const TileGeo g = geo(t);
     const __amdgpu_buffer_rsrc_t orsrc =
         buffer_rsrc(static_cast<uint8_t*>(a.out) + static_cast<int64_t>(g.m0) * a.ldo,
@@ -651,9 +680,11 @@ void grouped_gemm_kernel(GemmArgs a) {
   // this wave's loads of step g+1 (those of g+2 stay in flight) and for its own fragment reads
   // of step g; barrier (every wave's step-(g+1) data is in LDS and nobody reads slot g any
   // more); issue step g+3 into slot g; read the fragments of step g+1 while the MFMAs of step g
-  // run; after a tile's last step, store it.  FP8 keeps one fragment set (two do not fit beside
-  // the accumulators at two waves per SIMD) and refills it in place.
+  // run; after a tile's last step, store it.  bf16 and fp32 alternate two whole fragment sets;
+  // E4M3 alternates part of one (see Frags), MXFP4 refills one set in place.
   constexpr bool kTwoSets = !S::kFp8;
+  constexpr std::integral_constant<int, 0> kEven{};
+  constexpr std::integral_constant<int, 1> kOdd{};
   F f0, f1;
   setup(0);
   issue();
@@ -670,7 +701,7 @@ void grouped_gemm_kernel(GemmArgs a) {
   // normally the next step's LPS loads; in the two iterations after an epilogue also that
   // epilogue's stores, which sit between the two steps' loads.  (Counting fewer than were
   // issued only waits longer.)
-  auto iter = [&](F& cur, F& nxt) {
+  auto iter = [&](F& cur, F& nxt, auto parity) {
     if (after_epi > 0) {
       lds_dma_wait<S::LPS + S::EPI_STORES>();
       --after_epi;
@@ -678,7 +709,10 @@ void grouped_gemm_kernel(GemmArgs a) {
       lds_dma_wait<S::LPS>();
     }
     __syncthreads();
-    issue();
+    if constexpr (S::kFp8 && !S::kMx)
+      issue_begin();  // the loads go out between the MFMAs
+    else
+      issue();
     const int next = c_slot + 1 == S::NSLOT ? 0 : c_slot + 1;
     if constexpr (kTwoSets) {
       // one fragment read, then its share of the MFMAs, repeated: the reads of step g+1
@@ -698,7 +732,7 @@ void grouped_gemm_kernel(GemmArgs a) {
     } else if constexpr (S::kMx) {
       mma_refill_mx(cur, next);
     } else {
-      mma_refill_fp8(cur, next);
+      mma_refill_fp8(cur, next, parity);
     }
     c_slot = next;
     if (++c_step == KB) {
@@ -711,14 +745,16 @@ void grouped_gemm_kernel(GemmArgs a) {
   };
   const int total = n_my * KB;
   int gs = 0;
-  if constexpr (kTwoSets) {
-    for (; gs + 1 < total; gs += 2) {
-      iter(f0, f1);
-      iter(f1, f0);
-    }
-    if (gs < total) iter(f0, f1);
+  if constexpr (S::kMx) {
+    for (; gs < total; ++gs) iter(f0, f0, kEven);
   } else {
-    for (; gs < total; ++gs) iter(f0, f0);
+    // steps in pairs, one call site per parity: bf16 and fp32 trade f0 and f1, E4M3 alternates
+    // the sets inside f0
+    for (; gs < total; gs += 2) {
+      if constexpr (kTwoSets) iter(f0, f1, kEven); else iter(f0, f0, kEven);
+      if (gs + 1 == total) break;
+      if constexpr (kTwoSets) iter(f1, f0, kOdd); else iter(f0, f0, kOdd);
+    }
   }
   lds_dma_wait<0>();  // no load may still write this workgroup's LDS when it ends
 }
