@@ -19,8 +19,10 @@
 // already arriving while the current tile's epilogue stores its results from registers.  The
 // 16-byte chunks land XOR-swizzled by row so that fragment reads of 16 consecutive rows hit
 // distinct banks; fragments of step s+1 are read from LDS while the MFMAs of step s run, one
-// barrier per step.  Weights of an expert whose rows fit one tile are loaded non-temporally
-// (read once); others keep the default policy so the expert's other row tiles find them in L2.
+// barrier per step.  bf16 and fp32 weights of an expert whose rows fit one tile are loaded
+// non-temporally (read once); others keep the default policy so the expert's other row tiles
+// find them in L2.  (With E4M3 activations the loads go out between the MFMAs and keep the
+// default policy: measured on MI355X, the non-temporal hint gains nothing there.)
 #include <math.h>
 
 #include <type_traits>
@@ -123,13 +125,13 @@ struct Frags<MOE_FP8_E4M3, FM, FN> {
   float sb[2][2];
 };
 // E4M3 activations against E2M1 weights: 32 B of A and 16 B of B per lane, the lane's E8M0
-// weight scale (its column, its 32-value block) in the low byte of sbx
+// weight scale (its column, its 32-value block) in the low byte of sbx; sets as for E4M3.
 template <int FM, int FN>
 struct Frags<MOE_MXFP4, FM, FN> {
-  i32x8 a[1][FM];
-  i32x4 b[1][FN];
-  f32x4 sa[FM];
-  int sbx[FN];
+  i32x8 a[2][FM];
+  i32x4 b[2][FN];
+  f32x4 sa[2][FM];
+  int sbx[2][FN];
 };
 
 // Waves per SIMD the register allocation aims for: what the LDS footprint lets run (160 KiB
@@ -393,24 +395,21 @@ void grouped_gemm_kernel(GemmArgs a) {
   auto load = [&](F& f, int slot) {
     const uint8_t* sa = smem + slot * S::SLOT;
     const uint8_t* sb = sa + BM * kBlockK;
-    if constexpr (S::kMx) {
+    if constexpr (S::kMx) {  // set 0 of every fragment
       const float* ss = reinterpret_cast<const float*>(sa + STAGE_BYTES);
       const uint32_t* bsc = reinterpret_cast<const uint32_t*>(sa + STAGE_BYTES + S::ASW * 256);
 #pragma unroll
       for (int i = 0; i < S::FM; ++i) {
         // A in the MFMA's K order for an E2M1 partner: bytes 0-15 of the lane hold K
-        // 16*kq.., bytes 16-31 K 64+16*kq..
-        const int r = wm * S::TM + i * 16 + lr;
-        const i32x4 lo4 = *reinterpret_cast<const i32x4*>(sa + swz(r, kq));
-        const i32x4 hi4 = *reinterpret_cast<const i32x4*>(sa + swz(r, 4 + kq));
-        f.a[0][i] = i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-        f.sa[i] = *reinterpret_cast<const f32x4*>(ss + wm * S::TM + i * 16 + 4 * kq);
+        // 16*kq.., bytes 16-31 K 64+16*kq.. (the E4M3 fragment layout)
+        f.a[0][i] = frag_e4m3(sa, wm * S::TM + i * 16 + lr);
+        f.sa[0][i] = *reinterpret_cast<const f32x4*>(ss + wm * S::TM + i * 16 + 4 * kq);
       }
 #pragma unroll
       for (int j = 0; j < S::FN; ++j) {
         const int r = wn * S::TN + j * 16 + lr;  // E2M1: K 32*kq.. of column r
         f.b[0][j] = *reinterpret_cast<const i32x4*>(sb + swz4(r, kq));
-        f.sbx[j] = static_cast<int>((bsc[r] >> (8 * kq)) & 0xFFu);
+        f.sbx[0][j] = static_cast<int>((bsc[r] >> (8 * kq)) & 0xFFu);
       }
     } else if constexpr (DT == MOE_FP8_E4M3) {  // set 0 of every fragment
       const float* ss = reinterpret_cast<const float*>(sa + STAGE_BYTES);
@@ -529,9 +528,13 @@ void grouped_gemm_kernel(GemmArgs a) {
 
   // MXFP4 step: one scaled MFMA per (row block, column block) takes E4M3 activations and E2M1
   // weights with the lane's E8M0 weight scale applied inside; its fp32 partial is promoted
-  // with the row's activation scale.  Same issue order and refill points as the FP8 step.
-  auto mma_refill_mx = [&](F& f, int next) {
+  // with the row's activation scale.  Same issue order, fragment sets and placement of the next
+  // step's reads and loads as the E4M3 step.
+  auto mma_refill_mx = [&](F& f, int next, auto parity) {
     if constexpr (S::kMx) {
+      constexpr int P = decltype(parity)::value, Q = 1 - P, L = S::FM - 1;
+      constexpr int XI = S::FM > 1 ? 1 : 0;
+      constexpr int XJ_A = S::FM > 1 ? (S::FN > 1 ? 1 : 0) : S::FN - 1;
       const uint8_t* sa = smem + next * S::SLOT;
       const uint8_t* sb = sa + BM * kBlockK;
       const float* ss = reinterpret_cast<const float*>(sa + STAGE_BYTES);
@@ -539,10 +542,11 @@ void grouped_gemm_kernel(GemmArgs a) {
       f32x4 prev = f32x4{0.f, 0.f, 0.f, 0.f}, qp = prev;
 #pragma unroll
       for (int i = 0; i < S::FM; ++i) {
-        const f32x4 qs = f.sa[i];
+        const int ai = i == L ? P : 0;  // constant after unrolling
+        const f32x4 qs = f.sa[ai][i];
 #pragma unroll
         for (int j = 0; j < S::FN; ++j) {
-          const f32x4 cur = mfma_mx(f.a[0][i], f.b[0][j], f.sbx[j]);
+          const f32x4 cur = mfma_mx(f.a[ai][i], f.b[P][j], f.sbx[P][j]);
           if (i + j > 0) {
             const int pi = j > 0 ? i : i - 1, pj = j > 0 ? j - 1 : S::FN - 1;
             const f32x4& qq = j > 0 ? qs : qp;
@@ -550,10 +554,19 @@ void grouped_gemm_kernel(GemmArgs a) {
             for (int e = 0; e < 4; ++e) acc[pi][pj][e] = fmaf(prev[e], qq[e], acc[pi][pj][e]);
           }
           prev = cur;
-          if (i == S::FM - 1) {  // B column j is done: refill it and its scale
+          if (i * S::FN + j < S::LPS) issue_load(i * S::FN + j, kKeep);  // step g+3's loads
+          if (i == 0) {
             const int r = wn * S::TN + j * 16 + lr;
-            f.b[0][j] = *reinterpret_cast<const i32x4*>(sb + swz4(r, kq));
-            f.sbx[j] = static_cast<int>((bsc[r] >> (8 * kq)) & 0xFFu);
+            f.b[Q][j] = *reinterpret_cast<const i32x4*>(sb + swz4(r, kq));
+            f.sbx[Q][j] = static_cast<int>((bsc[r] >> (8 * kq)) & 0xFFu);
+          }
+          if (i == XI && j == XJ_A) {
+            f.a[Q][L] = frag_e4m3(sa, wm * S::TM + L * 16 + lr);
+            f.sa[Q][L] = *reinterpret_cast<const f32x4*>(ss + wm * S::TM + L * 16 + 4 * kq);
+          }
+          if (j == 0 && i > 0 && i - 1 < L) {  // row block i-1 is done with its fragment
+            f.a[0][i - 1] = frag_e4m3(sa, wm * S::TM + (i - 1) * 16 + lr);
+            f.sa[0][i - 1] = *reinterpret_cast<const f32x4*>(ss + wm * S::TM + (i - 1) * 16 + 4 * kq);
           }
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // the MFMA
           __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // then the VALU work
@@ -561,14 +574,9 @@ void grouped_gemm_kernel(GemmArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
         qp = qs;
-        // row block i is done with its A fragment and row scales
-        const int r = wm * S::TM + i * 16 + lr;
-        const i32x4 lo4 = *reinterpret_cast<const i32x4*>(sa + swz(r, kq));
-        const i32x4 hi4 = *reinterpret_cast<const i32x4*>(sa + swz(r, 4 + kq));
-        f.a[0][i] = i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-        f.sa[i] = *reinterpret_cast<const f32x4*>(ss + wm * S::TM + i * 16 + 4 * kq);
-        __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int n = S::FM * S::FN; n < S::LPS; ++n) issue_load(n, kKeep);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         acc[S::FM - 1][S::FN - 1][e] = fmaf(prev[e], qp[e], acc[S::FM - 1][S::FN - 1][e]);
@@ -681,7 +689,8 @@ void grouped_gemm_kernel(GemmArgs a) {
   // of step g; barrier (every wave's step-(g+1) data is in LDS and nobody reads slot g any
   // more); issue step g+3 into slot g; read the fragments of step g+1 while the MFMAs of step g
   // run; after a tile's last step, store it.  bf16 and fp32 alternate two whole fragment sets;
-  // E4M3 alternates part of one (see Frags), MXFP4 refills one set in place.
+  // E4M3 activations (FP8 and MXFP4 experts) alternate part of one (see Frags) and issue the
+  // loads of step g+3 between the MFMAs of step g rather than in one burst after the barrier.
   constexpr bool kTwoSets = !S::kFp8;
   constexpr std::integral_constant<int, 0> kEven{};
   constexpr std::integral_constant<int, 1> kOdd{};
@@ -709,7 +718,7 @@ void grouped_gemm_kernel(GemmArgs a) {
       lds_dma_wait<S::LPS>();
     }
     __syncthreads();
-    if constexpr (S::kFp8 && !S::kMx)
+    if constexpr (S::kFp8)
       issue_begin();  // the loads go out between the MFMAs
     else
       issue();
@@ -730,7 +739,7 @@ void grouped_gemm_kernel(GemmArgs a) {
       }
       __builtin_amdgcn_sched_group_barrier(0x008, NM - PER * NR, 0);
     } else if constexpr (S::kMx) {
-      mma_refill_mx(cur, next);
+      mma_refill_mx(cur, next, parity);
     } else {
       mma_refill_fp8(cur, next, parity);
     }
@@ -745,16 +754,12 @@ void grouped_gemm_kernel(GemmArgs a) {
   };
   const int total = n_my * KB;
   int gs = 0;
-  if constexpr (S::kMx) {
-    for (; gs < total; ++gs) iter(f0, f0, kEven);
-  } else {
-    // steps in pairs, one call site per parity: bf16 and fp32 trade f0 and f1, E4M3 alternates
-    // the sets inside f0
-    for (; gs < total; gs += 2) {
-      if constexpr (kTwoSets) iter(f0, f1, kEven); else iter(f0, f0, kEven);
-      if (gs + 1 == total) break;
-      if constexpr (kTwoSets) iter(f1, f0, kOdd); else iter(f0, f0, kOdd);
-    }
+  // steps in pairs, one call site per parity: bf16 and fp32 trade f0 and f1, E4M3 activations
+  // alternate the sets inside f0
+  for (; gs < total; gs += 2) {
+    if constexpr (kTwoSets) iter(f0, f1, kEven); else iter(f0, f0, kEven);
+    if (gs + 1 == total) break;
+    if constexpr (kTwoSets) iter(f1, f0, kOdd); else iter(f0, f0, kOdd);
   }
   lds_dma_wait<0>();  // no load may still write this workgroup's LDS when it ends
 }
