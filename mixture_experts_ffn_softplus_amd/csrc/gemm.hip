@@ -21,8 +21,9 @@
 // distinct banks; fragments of step s+1 are read from LDS while the MFMAs of step s run, one
 // barrier per step.  bf16 and fp32 weights of an expert whose rows fit one tile are loaded
 // non-temporally (read once); others keep the default policy so the expert's other row tiles
-// find them in L2.  (With E4M3 activations the loads go out between the MFMAs and keep the
-// default policy: measured on MI355X, the non-temporal hint gains nothing there.)
+// find them in L2.  (With E4M3 activations, and in launches of one group, a step's loads go out
+// between its MFMAs with the default policy: measured on MI355X, the non-temporal hint gains
+// nothing with E4M3 activations.)
 #include <math.h>
 
 #include <type_traits>
@@ -457,6 +458,54 @@ void grouped_gemm_kernel(GemmArgs a) {
               acc[i][j] = mfma_f32(f.a[s][i][e], f.b[s][j][e], acc[i][j]);
     }  // FP8: mma_refill_fp8
   };
+  // bf16 / fp32 step: the MFMAs of step g from `cur` while step g+1's fragments are read into
+  // `nxt`, one fragment read then its share of the MFMAs, repeated (the reads spread over the
+  // MFMAs instead of bunching at either end).  spread: load n of step g+3 goes out after
+  // fragment read n * NR / LPS (the inline-asm loads keep their place among the LDS reads, both
+  // touching memory, which the group barriers interleave with the MFMAs); otherwise the caller
+  // has issued them.  Grouped launches issue in one burst: their per-tile cache policy (see
+  // stream_b) would need a second copy of the step for each policy, and measured on MI355X,
+  // the policy is worth more there than the spread; the spread gains 6-13% on the others.
+  auto step_two_sets = [&](F& cur, F& nxt, int next, auto spread) {
+    if constexpr (!S::kFp8) {
+      constexpr int NR = 2 * (S::FM + S::FN);
+      constexpr int NM = 2 * S::FM * S::FN * (DT == MOE_F32 ? 4 : 1);
+      constexpr int PER = NM / NR;
+      static_assert(S::LPS <= NR, "one load per fragment read at most");
+      const uint8_t* sa = smem + next * S::SLOT;
+      const uint8_t* sb = sa + BM * kBlockK;
+      auto loads_after = [&](int r) {
+        if constexpr (decltype(spread)::value) {
+#pragma unroll
+          for (int n = 0; n < S::LPS; ++n)
+            if (n * NR / S::LPS == r) issue_load(n, kKeep);
+        }
+      };
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int ch = 4 * h + kq;
+#pragma unroll
+        for (int i = 0; i < S::FM; ++i) {
+          nxt.a[h][i] = *reinterpret_cast<const typename F::V*>(sa + swz(wm * S::TM + i * 16 + lr, ch));
+          loads_after(h * (S::FM + S::FN) + i);
+        }
+#pragma unroll
+        for (int j = 0; j < S::FN; ++j) {
+          nxt.b[h][j] = *reinterpret_cast<const typename F::V*>(sb + swz(wn * S::TN + j * 16 + lr, ch));
+          loads_after(h * (S::FM + S::FN) + S::FM + j);
+        }
+      }
+      mma(cur);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // MFMA
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NM - PER * NR, 0);
+    }
+  };
+
   // FP8 step (steps of parity P use fragment set P, see Frags): one E4M3 MFMA covers exactly one
   // 128-deep scale block; its fp32 partial is promoted with the row's activation scale times the
   // block's weight scale.  Written in issue order: MFMA n is issued before partial n-1 is
@@ -689,8 +738,9 @@ void grouped_gemm_kernel(GemmArgs a) {
   // of step g; barrier (every wave's step-(g+1) data is in LDS and nobody reads slot g any
   // more); issue step g+3 into slot g; read the fragments of step g+1 while the MFMAs of step g
   // run; after a tile's last step, store it.  bf16 and fp32 alternate two whole fragment sets;
-  // E4M3 activations (FP8 and MXFP4 experts) alternate part of one (see Frags) and issue the
-  // loads of step g+3 between the MFMAs of step g rather than in one burst after the barrier.
+  // E4M3 activations (FP8 and MXFP4 experts) alternate part of one (see Frags).  These, and
+  // launches of one group, issue the loads of step g+3 between the MFMAs of step g rather than
+  // in one burst after the barrier.
   constexpr bool kTwoSets = !S::kFp8;
   constexpr std::integral_constant<int, 0> kEven{};
   constexpr std::integral_constant<int, 1> kOdd{};
@@ -718,26 +768,14 @@ void grouped_gemm_kernel(GemmArgs a) {
       lds_dma_wait<S::LPS>();
     }
     __syncthreads();
-    if constexpr (S::kFp8)
-      issue_begin();  // the loads go out between the MFMAs
+    constexpr bool kSpread = S::kFp8 || !GROUPED;  // the loads go out between the MFMAs
+    if constexpr (kSpread)
+      issue_begin();
     else
       issue();
     const int next = c_slot + 1 == S::NSLOT ? 0 : c_slot + 1;
     if constexpr (kTwoSets) {
-      // one fragment read, then its share of the MFMAs, repeated: the reads of step g+1
-      // spread over the MFMAs of step g instead of bunching at either end
-      constexpr int NR = 2 * (S::FM + S::FN);
-      constexpr int NM = 2 * S::FM * S::FN * (DT == MOE_F32 ? 4 : 1);
-      constexpr int PER = NM / NR;
-      __builtin_amdgcn_sched_barrier(0);
-      load(nxt, next);
-      mma(cur);
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // MFMA
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, NM - PER * NR, 0);
+      step_two_sets(cur, nxt, next, std::integral_constant<bool, kSpread>{});
     } else if constexpr (S::kMx) {
       mma_refill_mx(cur, next, parity);
     } else {
