@@ -14,8 +14,9 @@
 // workgroup, each wave a 64 x 64 or smaller sub-tile of the BM x BN tile.  K is consumed 128
 // bytes per step (64 bf16, 32 fp32 or 128 E4M3 values -- exactly one FP8 scale block).  Every
 // step's A rows (gathered through a_map: no permuted copy of x is ever written) and B rows go
-// straight from global memory into a three-slot LDS ring with buffer loads that write LDS
-// directly, issued three steps ahead across tile boundaries, so the next tile's operands are
+// straight from global memory into an LDS ring of three slots (up to eight for row-light E4M3
+// tiles) with buffer loads that write LDS directly, issued as many steps ahead across tile
+// boundaries, so the next tile's operands are
 // already arriving while the current tile's epilogue stores its results from registers.  The
 // 16-byte chunks land XOR-swizzled by row so that fragment reads of 16 consecutive rows hit
 // distinct banks; fragments of step s+1 are read from LDS while the MFMAs of step s run, one
@@ -74,8 +75,6 @@ struct GemmShape {
   static constexpr int B_ROW = kMx ? 64 : kBlockK;    // bytes of one B row per step
   static constexpr int A_CHUNKS = BM * 8, B_CHUNKS = BN * (B_ROW / 16);  // 16-byte chunks
   static constexpr int A_PER = (A_CHUNKS + NT - 1) / NT, B_PER = (B_CHUNKS + NT - 1) / NT;
-  // LDS ring: step s multiplies out of slot s % 3 while steps s+1 and s+2 land in the others
-  static constexpr int NSLOT = 3;
   static constexpr int STAGE = BM * kBlockK + BN * B_ROW;
   // Scale loads of a step, one 4-byte load per lane of a wave (256 bytes of LDS each): ASW
   // waves the activation row scales (64 rows a wave), BSW waves the weight scales (FP8: one
@@ -88,19 +87,28 @@ struct GemmShape {
   // destination of the A/B loads a wave issues for nothing (when the chunks do not divide evenly
   // over the waves)
   static constexpr int DUMMY = (A_CHUNKS % NT || B_CHUNKS % NT) ? NW * 1024 : 0;
-  static constexpr int MAIN = NSLOT * SLOT + DUMMY;
   // FP8 h quantisation: per-row maxima of each wave column, exchanged between waves
   static constexpr int AMAX = (kFp8 && EPI == kEpiSwiglu) ? BM * WN * 4 : 0;
   // epilogue staging: one 16 x 16 fp32 block per wave, rows kEpiPitch floats apart
+  static constexpr int EPI_BYTES = NW * 16 * kEpiPitch * 4;
+  // LDS ring: step s multiplies out of slot s % NSLOT while the next NSLOT - 1 steps land in
+  // the others.  Three slots; E4M3 tiles of at most 32 rows (decode shapes, which do little
+  // but stream weights) take as many as 160 KiB of LDS hold, up to 8, for more bytes in flight
+  // per CU (measured on MI355X: three slots kept MXFP4 decode at half the HBM rate).
+  static constexpr int DEEP = (160 * 1024 - DUMMY - AMAX - EPI_BYTES) / SLOT;
+  static constexpr int NSLOT = (kFp8 && BM <= 32) ? (DEEP > 8 ? 8 : DEEP < 3 ? 3 : DEEP) : 3;
+  static constexpr int MAIN = NSLOT * SLOT + DUMMY;
   static constexpr int EPI_OFF = MAIN + AMAX;
-  static constexpr int SMEM = EPI_OFF + NW * 16 * kEpiPitch * 4;
+  static constexpr int SMEM = EPI_OFF + EPI_BYTES;
   // direct-to-LDS loads each wave issues per step (the same count in every wave)
   static constexpr int LPS = A_PER + B_PER + (kFp8 ? 1 : 0);
   // stores every wave issues in a tile's epilogue (at least; FP8 h scales come on top)
   static constexpr int EPI_STORES = EPI == kEpiStore ? FM * FN : FM * (FN / 2);
   static_assert(FM >= 1 && FN >= 1, "tile too small for its waves");
   static_assert(!kFp8 || NW >= ASW + BSW, "scale loads need ASW + BSW waves");
-  static_assert(2 * LPS < 64 && LPS + EPI_STORES < 64, "vmcnt holds at most 63");
+  static_assert((NSLOT - 1) * LPS < 64 && (NSLOT - 2) * LPS + EPI_STORES < 64,
+                "vmcnt holds at most 63");
+  static_assert(SMEM <= 160 * 1024, "LDS of one workgroup");
   static_assert(!kFp8 || kMx || (TN <= 128 && 128 % TN == 0), "FP8: two weight scales per wave");
   static_assert(!kMx || BN % 64 == 0, "MXFP4: whole waves of weight scales");
   static_assert(EPI != kEpiSwiglu || FN % 2 == 0, "gate/up pairs must stay within one wave");
@@ -734,10 +742,10 @@ void grouped_gemm_kernel(GemmArgs a) {
 
   // ---------------------------------------------------------------- the pipeline
   // Global step g runs through this workgroup's tiles back to back.  Iteration g: wait for
-  // this wave's loads of step g+1 (those of g+2 stay in flight) and for its own fragment reads
-  // of step g; barrier (every wave's step-(g+1) data is in LDS and nobody reads slot g any
-  // more); issue step g+3 into slot g; read the fragments of step g+1 while the MFMAs of step g
-  // run; after a tile's last step, store it.  bf16 and fp32 alternate two whole fragment sets;
+  // this wave's loads of step g+1 (those of g+2 .. g+NSLOT-1 stay in flight) and for its own
+  // fragment reads of step g; barrier (every wave's step-(g+1) data is in LDS and nobody reads
+  // slot g any more); issue step g+NSLOT into slot g; read the fragments of step g+1 while the
+  // MFMAs of step g run; after a tile's last step, store it.  bf16 and fp32 alternate two whole fragment sets;
   // E4M3 activations (FP8 and MXFP4 experts) alternate part of one (see Frags).  These, and
   // launches of one group, issue the loads of step g+3 between the MFMAs of step g rather than
   // in one burst after the barrier.
@@ -746,10 +754,9 @@ void grouped_gemm_kernel(GemmArgs a) {
   constexpr std::integral_constant<int, 1> kOdd{};
   F f0, f1;
   setup(0);
-  issue();
-  issue();
-  issue();
-  lds_dma_wait<2 * S::LPS>();
+#pragma unroll
+  for (int s = 0; s < S::NSLOT; ++s) issue();
+  lds_dma_wait<(S::NSLOT - 1) * S::LPS>();
   __syncthreads();
   load(f0, 0);
   int c_slot = 0, c_step = 0, c_tile = 0;
@@ -757,15 +764,15 @@ void grouped_gemm_kernel(GemmArgs a) {
   // The refill after the last step reads a slot no one wrote for it: harmless, and it keeps
   // the loop body one basic block for the scheduler.  The vector-memory counter retires loads
   // and stores in issue order, so the wait counts what was issued after the loads it needs:
-  // normally the next step's LPS loads; in the two iterations after an epilogue also that
-  // epilogue's stores, which sit between the two steps' loads.  (Counting fewer than were
-  // issued only waits longer.)
+  // normally the loads of the NSLOT - 2 steps after it; in the NSLOT - 1 iterations after an
+  // epilogue also that epilogue's stores, which were issued after the loads of those steps.
+  // (Counting fewer than were issued only waits longer.)
   auto iter = [&](F& cur, F& nxt, auto parity) {
     if (after_epi > 0) {
-      lds_dma_wait<S::LPS + S::EPI_STORES>();
+      lds_dma_wait<(S::NSLOT - 2) * S::LPS + S::EPI_STORES>();
       --after_epi;
     } else {
-      lds_dma_wait<S::LPS>();
+      lds_dma_wait<(S::NSLOT - 2) * S::LPS>();
     }
     __syncthreads();
     constexpr bool kSpread = S::kFp8 || !GROUPED;  // the loads go out between the MFMAs
@@ -784,7 +791,7 @@ void grouped_gemm_kernel(GemmArgs a) {
     c_slot = next;
     if (++c_step == KB) {
       epilogue(c_tile);
-      after_epi = 2;
+      after_epi = S::NSLOT - 1;
       zero_acc();
       c_step = 0;
       ++c_tile;
