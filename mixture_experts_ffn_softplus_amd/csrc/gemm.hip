@@ -52,10 +52,6 @@ __device__ __forceinline__ int swz(int row, int ch) { return row * kBlockK + ((c
 // puts those 16 accesses on 16 different 16-byte bank groups.
 __device__ __forceinline__ int swz4(int row, int ch) { return row * 64 + ((ch ^ ((row >> 1) & 2)) << 4); }
 
-// Row pitch (floats) of the per-wave epilogue staging block: 16 + 4, so that the four row groups
-// a wave writes at once (rows 4q + e) fall on different banks.
-constexpr int kEpiPitch = 20;
-
 // NW waves per workgroup: 8 for the wide tiles (BN = 256, each wave still 64 x 64), else 4.
 template <int DT, int BN>
 constexpr int gemm_waves() { return (DT != MOE_F32 && BN >= 256) ? 8 : 4; }
@@ -89,17 +85,14 @@ struct GemmShape {
   static constexpr int DUMMY = (A_CHUNKS % NT || B_CHUNKS % NT) ? NW * 1024 : 0;
   // FP8 h quantisation: per-row maxima of each wave column, exchanged between waves
   static constexpr int AMAX = (kFp8 && EPI == kEpiSwiglu) ? BM * WN * 4 : 0;
-  // epilogue staging: one 16 x 16 fp32 block per wave, rows kEpiPitch floats apart
-  static constexpr int EPI_BYTES = NW * 16 * kEpiPitch * 4;
   // LDS ring: step s multiplies out of slot s % NSLOT while the next NSLOT - 1 steps land in
   // the others.  Three slots; E4M3 tiles of at most 32 rows (decode shapes, which do little
   // but stream weights) take as many as 160 KiB of LDS hold, up to 8, for more bytes in flight
   // per CU (measured on MI355X: three slots kept MXFP4 decode at half the HBM rate).
-  static constexpr int DEEP = (160 * 1024 - DUMMY - AMAX - EPI_BYTES) / SLOT;
+  static constexpr int DEEP = (160 * 1024 - DUMMY - AMAX) / SLOT;
   static constexpr int NSLOT = (kFp8 && BM <= 32) ? (DEEP > 8 ? 8 : DEEP < 3 ? 3 : DEEP) : 3;
   static constexpr int MAIN = NSLOT * SLOT + DUMMY;
-  static constexpr int EPI_OFF = MAIN + AMAX;
-  static constexpr int SMEM = EPI_OFF + EPI_BYTES;
+  static constexpr int SMEM = MAIN + AMAX;
   // direct-to-LDS loads each wave issues per step (the same count in every wave)
   static constexpr int LPS = A_PER + B_PER + (kFp8 ? 1 : 0);
   // stores every wave issues in a tile's epilogue (at least; FP8 h scales come on top)
@@ -130,7 +123,7 @@ struct Frags {
 template <int FM, int FN>
 struct Frags<MOE_FP8_E4M3, FM, FN> {
   i32x8 a[2][FM], b[2][FN];
-  f32x4 sa[2][FM];
+  float sa[2][FM];
   float sb[2][2];
 };
 // E4M3 activations against E2M1 weights: 32 B of A and 16 B of B per lane, the lane's E8M0
@@ -139,7 +132,7 @@ template <int FM, int FN>
 struct Frags<MOE_MXFP4, FM, FN> {
   i32x8 a[2][FM];
   i32x4 b[2][FN];
-  f32x4 sa[2][FM];
+  float sa[2][FM];
   int sbx[2][FN];
 };
 
@@ -412,7 +405,7 @@ void grouped_gemm_kernel(GemmArgs a) {
         // A in the MFMA's K order for an E2M1 partner: bytes 0-15 of the lane hold K
         // 16*kq.., bytes 16-31 K 64+16*kq.. (the E4M3 fragment layout)
         f.a[0][i] = frag_e4m3(sa, wm * S::TM + i * 16 + lr);
-        f.sa[0][i] = *reinterpret_cast<const f32x4*>(ss + wm * S::TM + i * 16 + 4 * kq);
+        f.sa[0][i] = ss[wm * S::TM + i * 16 + lr];
       }
 #pragma unroll
       for (int j = 0; j < S::FN; ++j) {
@@ -425,7 +418,7 @@ void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < S::FM; ++i) {
         f.a[0][i] = frag_e4m3(sa, wm * S::TM + i * 16 + lr);
-        f.sa[0][i] = *reinterpret_cast<const f32x4*>(ss + wm * S::TM + i * 16 + 4 * kq);
+        f.sa[0][i] = ss[wm * S::TM + i * 16 + lr];
       }
 #pragma unroll
       for (int j = 0; j < S::FN; ++j) f.b[0][j] = frag_e4m3(sb, wn * S::TN + j * 16 + lr);
@@ -453,7 +446,7 @@ void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < S::FM; ++i)
 #pragma unroll
-          for (int j = 0; j < S::FN; ++j) acc[i][j] = mfma_bf16(f.a[s][i], f.b[s][j], acc[i][j]);
+          for (int j = 0; j < S::FN; ++j) acc[i][j] = mfma_bf16(f.b[s][j], f.a[s][i], acc[i][j]);
     } else if constexpr (DT == MOE_F32) {
 #pragma unroll
       for (int s = 0; s < 2; ++s)
@@ -463,7 +456,7 @@ void grouped_gemm_kernel(GemmArgs a) {
           for (int i = 0; i < S::FM; ++i)
 #pragma unroll
             for (int j = 0; j < S::FN; ++j)
-              acc[i][j] = mfma_f32(f.a[s][i][e], f.b[s][j][e], acc[i][j]);
+              acc[i][j] = mfma_f32(f.b[s][j][e], f.a[s][i][e], acc[i][j]);
     }  // FP8: mma_refill_fp8
   };
   // bf16 / fp32 step: the MFMAs of step g from `cur` while step g+1's fragments are read into
@@ -534,29 +527,27 @@ void grouped_gemm_kernel(GemmArgs a) {
       const uint8_t* sb = sa + BM * kBlockK;
       const float* ss = reinterpret_cast<const float*>(sa + STAGE_BYTES);
       f32x4 prev = f32x4{0.f, 0.f, 0.f, 0.f};
-      f32x4 qs[2], qp[2];
+      float qs[2], qp[2];
 #pragma unroll
       for (int i = 0; i < S::FM; ++i) {
         const int ai = i == L ? P : 0;  // constant after unrolling
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) qs[h][e] = f.sa[ai][i][e] * f.sb[P][h];
+        for (int h = 0; h < 2; ++h) qs[h] = f.sa[ai][i] * f.sb[P][h];
 #pragma unroll
         for (int j = 0; j < S::FN; ++j) {
-          const f32x4 cur = mfma_fp8(f.a[ai][i], f.b[P][j], f32x4{0.f, 0.f, 0.f, 0.f});
+          const f32x4 cur = mfma_fp8(f.b[P][j], f.a[ai][i], f32x4{0.f, 0.f, 0.f, 0.f});
           if (i + j > 0) {
             const int pi = j > 0 ? i : i - 1, pj = j > 0 ? j - 1 : S::FN - 1;
-            const f32x4& qq = j > 0 ? qs[pj & 1] : qp[pj & 1];
+            const float qq = j > 0 ? qs[pj & 1] : qp[pj & 1];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[pi][pj][e] = fmaf(prev[e], qq[e], acc[pi][pj][e]);
+            for (int e = 0; e < 4; ++e) acc[pi][pj][e] = fmaf(prev[e], qq, acc[pi][pj][e]);
           }
           prev = cur;
           if (i * S::FN + j < S::LPS) issue_load(i * S::FN + j, kKeep);  // step g+3's loads
           if (i == 0) f.b[Q][j] = frag_e4m3(sb, wn * S::TN + j * 16 + lr);
           if (i == XI && j == XJ_A) {
             f.a[Q][L] = frag_e4m3(sa, wm * S::TM + L * 16 + lr);
-            f.sa[Q][L] = *reinterpret_cast<const f32x4*>(ss + wm * S::TM + L * 16 + 4 * kq);
+            f.sa[Q][L] = ss[wm * S::TM + L * 16 + lr];
           }
           if (i == XI && j == XJ_S) {
             f.sb[Q][0] = ss[S::ASW * 64 + wn * S::TN / 16];
@@ -564,7 +555,7 @@ void grouped_gemm_kernel(GemmArgs a) {
           }
           if (j == 0 && i > 0 && i - 1 < L) {  // row block i-1 is done with its fragment
             f.a[0][i - 1] = frag_e4m3(sa, wm * S::TM + (i - 1) * 16 + lr);
-            f.sa[0][i - 1] = *reinterpret_cast<const f32x4*>(ss + wm * S::TM + (i - 1) * 16 + 4 * kq);
+            f.sa[0][i - 1] = ss[wm * S::TM + (i - 1) * 16 + lr];
           }
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // the MFMA
           __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // then the VALU work
@@ -579,7 +570,7 @@ void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         acc[S::FM - 1][S::FN - 1][e] =
-            fmaf(prev[e], qp[(S::FN - 1) & 1][e], acc[S::FM - 1][S::FN - 1][e]);
+            fmaf(prev[e], qp[(S::FN - 1) & 1], acc[S::FM - 1][S::FN - 1][e]);
     }
   };
 
@@ -596,19 +587,20 @@ void grouped_gemm_kernel(GemmArgs a) {
       const uint8_t* sb = sa + BM * kBlockK;
       const float* ss = reinterpret_cast<const float*>(sa + STAGE_BYTES);
       const uint32_t* bsc = reinterpret_cast<const uint32_t*>(sa + STAGE_BYTES + S::ASW * 256);
-      f32x4 prev = f32x4{0.f, 0.f, 0.f, 0.f}, qp = prev;
+      f32x4 prev = f32x4{0.f, 0.f, 0.f, 0.f};
+      float qp = 0.0f;
 #pragma unroll
       for (int i = 0; i < S::FM; ++i) {
         const int ai = i == L ? P : 0;  // constant after unrolling
-        const f32x4 qs = f.sa[ai][i];
+        const float qs = f.sa[ai][i];
 #pragma unroll
         for (int j = 0; j < S::FN; ++j) {
-          const f32x4 cur = mfma_mx(f.a[ai][i], f.b[P][j], f.sbx[P][j]);
+          const f32x4 cur = mfma_mx(f.b[P][j], f.a[ai][i], f.sbx[P][j]);
           if (i + j > 0) {
             const int pi = j > 0 ? i : i - 1, pj = j > 0 ? j - 1 : S::FN - 1;
-            const f32x4& qq = j > 0 ? qs : qp;
+            const float qq = j > 0 ? qs : qp;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[pi][pj][e] = fmaf(prev[e], qq[e], acc[pi][pj][e]);
+            for (int e = 0; e < 4; ++e) acc[pi][pj][e] = fmaf(prev[e], qq, acc[pi][pj][e]);
           }
           prev = cur;
           if (i * S::FN + j < S::LPS) issue_load(i * S::FN + j, kKeep);  // step g+3's loads
@@ -619,11 +611,11 @@ void grouped_gemm_kernel(GemmArgs a) {
           }
           if (i == XI && j == XJ_A) {
             f.a[Q][L] = frag_e4m3(sa, wm * S::TM + L * 16 + lr);
-            f.sa[Q][L] = *reinterpret_cast<const f32x4*>(ss + wm * S::TM + L * 16 + 4 * kq);
+            f.sa[Q][L] = ss[wm * S::TM + L * 16 + lr];
           }
           if (j == 0 && i > 0 && i - 1 < L) {  // row block i-1 is done with its fragment
             f.a[0][i - 1] = frag_e4m3(sa, wm * S::TM + (i - 1) * 16 + lr);
-            f.sa[0][i - 1] = *reinterpret_cast<const f32x4*>(ss + wm * S::TM + (i - 1) * 16 + 4 * kq);
+            f.sa[0][i - 1] = ss[wm * S::TM + (i - 1) * 16 + lr];
           }
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // the MFMA
           __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // then the VALU work
@@ -636,24 +628,30 @@ void grouped_gemm_kernel(GemmArgs a) {
       for (int n = S::FM * S::FN; n < S::LPS; ++n) issue_load(n, kKeep);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        acc[S::FM - 1][S::FN - 1][e] = fmaf(prev[e], qp[e], acc[S::FM - 1][S::FN - 1][e]);
+        acc[S::FM - 1][S::FN - 1][e] = fmaf(prev[e], qp, acc[S::FM - 1][S::FN - 1][e]);
     }
   };
 
   // ---------------------------------------------------------------- epilogues
-  // From the accumulators (lane l holds column l % 16 of each 16 x 16 block, rows 4 * (l / 16)
-  // + e), one block at a time through this wave's staging area, so that each lane stores 4
-  // consecutive values of one row (lane l: row l / 4, columns 4 * (l % 4) ...).  Stores go
-  // through a buffer resource ending at the tile's last row: rows past it are dropped.  The
-  // LDS ring meanwhile keeps receiving the next tile's operands.
-  float* stage = reinterpret_cast<float*>(smem + S::EPI_OFF) + wv * 16 * kEpiPitch;
-  const int srow = l >> 2, scol = 4 * (l & 3);
-  auto stage_block = [&](const float (&v)[4]) {  // v[e]: row 4 * kq + e, column lr
-#pragma unroll
-    for (int e = 0; e < 4; ++e) stage[(4 * kq + e) * kEpiPitch + lr] = v[e];
-    // LDS operations of one wave complete in order: the read sees the writes above
-    return *reinterpret_cast<const f32x4*>(stage + srow * kEpiPitch + scol);
+  // Every MFMA takes the weights as its first operand and the activation rows as its second,
+  // so accumulator block (i, j) holds, in lane l, output row wm*TM + 16i + l%16 at the four
+  // consecutive columns wn*TN + 16j + 4*(l/16) + e.  Before a block is stored, lane 4r + c takes
+  // the (already packed) values of lane r + 16c by a cross-lane permute, so that consecutive
+  // lanes write consecutive bytes of one row, which the store path merges (stored in the
+  // accumulator order, the down GEMMs measured 22% slower on MI355X).  16/8/4-byte buffer stores
+  // through a resource ending at the tile's last row: rows past it are dropped.  The LDS ring
+  // meanwhile keeps receiving the next tile's operands.
+  const int orow = wm * S::TM + lr;  // + 16 i: this lane's accumulator row in the tile
+  const int srow = wm * S::TM + (l >> 2), scol = 4 * (l & 3);  // its row and column once permuted
+  const int xsrc = ((l >> 2) + 16 * (l & 3)) * 4;                // ds_bpermute byte address
+  auto xpose = [&](uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(xsrc, static_cast<int>(v)));
   };
+  auto xpose4 = [&](f32x4 v) {
+    return f32x4{__uint_as_float(xpose(__float_as_uint(v[0]))), __uint_as_float(xpose(__float_as_uint(v[1]))),
+                 __uint_as_float(xpose(__float_as_uint(v[2]))), __uint_as_float(xpose(__float_as_uint(v[3])))};
+  };
+  auto xpose2 = [&](uint2 v) { return uint2{xpose(v.x), xpose(v.y)}; };
   auto epilogue = [&](int t) __attribute__((always_inline)) {
     const TileGeo g = geo(t);
     const __amdgpu_buffer_rsrc_t orsrc =
@@ -665,14 +663,13 @@ void grouped_gemm_kernel(GemmArgs a) {
       for (int i = 0; i < S::FM; ++i)
 #pragma unroll
         for (int j = 0; j < S::FN; ++j) {
-          const float v4[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-          const f32x4 v = stage_block(v4);
-          const int row = wm * S::TM + i * 16 + srow;
+          const int row = srow + i * 16;
           const int col = g.n0 + wn * S::TN + j * 16 + scol;
           if (f32o) {
-            buffer_store16(orsrc, static_cast<uint32_t>(row * a.ldo + col * 4), v);
+            buffer_store16(orsrc, static_cast<uint32_t>(row * a.ldo + col * 4), xpose4(acc[i][j]));
           } else {
-            buffer_store8(orsrc, static_cast<uint32_t>(row * a.ldo + col * 2), pack_bf16x4(v));
+            buffer_store8(orsrc, static_cast<uint32_t>(row * a.ldo + col * 2),
+                          xpose2(pack_bf16x4(acc[i][j])));
           }
         }
     } else {
@@ -689,38 +686,39 @@ void grouped_gemm_kernel(GemmArgs a) {
       const int hc0 = g.n0 / 2 + wn * HP * 16;  // first h column of this wave
       if constexpr (S::kFp8) {
         // one 128-value group per row and tile: scale = max|h| / 448, codes = E4M3(h / scale).
-        // Row maxima: over this wave's columns (the 16 lanes sharing kq), then over the WN
-        // waves through LDS.
+        // Row maxima: over the lane's own values, then over the four lanes holding the same row
+        // (l % 16 alike), then over the WN waves through LDS.
         float* amax = reinterpret_cast<float*>(smem + S::MAIN);
 #pragma unroll
-        for (int i = 0; i < S::FM; ++i)
+        for (int i = 0; i < S::FM; ++i) {
+          float m = 0.0f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float m = 0.0f;
+          for (int p = 0; p < HP; ++p)
 #pragma unroll
-            for (int p = 0; p < HP; ++p) m = fmaxf(m, fabsf(hv[i][p][e]));
-            m = row16_max(m);
-            if (lr == 0) amax[(wm * S::TM + i * 16 + 4 * kq + e) * S::WN + wn] = m;
-          }
+            for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(hv[i][p][e]));
+          m = fmaxf(m, __shfl_xor(m, 16, kWave));
+          m = fmaxf(m, __shfl_xor(m, 32, kWave));
+          if (kq == 0) amax[(orow + i * 16) * S::WN + wn] = m;
+        }
         __syncthreads();
         const int groups = (a.N / 2) / 128;
         const int grp = g.n0 / BN;
 #pragma unroll
         for (int i = 0; i < S::FM; ++i) {
-          // staged layout: this lane holds 4 consecutive h of row `row`
-          const int row = wm * S::TM + i * 16 + srow;
+          const int row = orow + i * 16;  // this lane's row before the permute
           float m = 0.0f;
 #pragma unroll
           for (int w2 = 0; w2 < S::WN; ++w2) m = fmaxf(m, amax[row * S::WN + w2]);
           const float sc = m > 0.0f ? m / 448.0f : 1.0f;
           const float inv = __builtin_amdgcn_rcpf(sc);
-          if (wn == 0 && (l & 3) == 0 && row < g.rows)
+          if (wn == 0 && kq == 0 && row < g.rows)
             a.out_scales[static_cast<int64_t>(g.m0 + row) * groups + grp] = sc;
 #pragma unroll
           for (int p = 0; p < HP; ++p) {
-            const f32x4 v = stage_block(hv[i][p]);
+            const float* v = hv[i][p];
             const uint32_t codes = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-            buffer_store4(orsrc, static_cast<uint32_t>(row * a.ldo + hc0 + p * 16 + scol), codes);
+            buffer_store4(orsrc, static_cast<uint32_t>((srow + i * 16) * a.ldo + hc0 + p * 16 + scol),
+                          xpose(codes));
           }
         }
       } else {
@@ -728,13 +726,13 @@ void grouped_gemm_kernel(GemmArgs a) {
         for (int i = 0; i < S::FM; ++i)
 #pragma unroll
           for (int p = 0; p < HP; ++p) {
-            const f32x4 v = stage_block(hv[i][p]);
-            const int row = wm * S::TM + i * 16 + srow;
+            const f32x4 v = f32x4{hv[i][p][0], hv[i][p][1], hv[i][p][2], hv[i][p][3]};
+            const int row = srow + i * 16;
             const int col = hc0 + p * 16 + scol;
             if constexpr (DT == MOE_F32)
-              buffer_store16(orsrc, static_cast<uint32_t>(row * a.ldo + col * 4), v);
+              buffer_store16(orsrc, static_cast<uint32_t>(row * a.ldo + col * 4), xpose4(v));
             else
-              buffer_store8(orsrc, static_cast<uint32_t>(row * a.ldo + col * 2), pack_bf16x4(v));
+              buffer_store8(orsrc, static_cast<uint32_t>(row * a.ldo + col * 2), xpose2(pack_bf16x4(v)));
           }
       }
     }

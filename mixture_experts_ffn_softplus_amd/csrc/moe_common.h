@@ -81,14 +81,14 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma_fp8(i32x8 a, i32x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
-// E4M3 x E2M1 (format selectors 0 and 4), K = 128, from zero.  A: 32 bytes per lane, bytes
-// 0-15 holding K 16*(l/16).. and bytes 16-31 K 64+16*(l/16).. of row l%16; B: 16 bytes per
-// lane, K 32*(l/16)..+31 of column l%16, two codes a byte, the lower K in the low nibble.  The
-// lane's E8M0 byte `sb` scales B's 32 values (A's scale field is 127 = 2^0).
-__device__ __forceinline__ f32x4 mfma_mx(i32x8 a, i32x4 b, int sb) {
-  const i32x8 b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b8, f32x4{0.f, 0.f, 0.f, 0.f}, 0,
-                                                          4, 0, 127, 0, sb);
+// E2M1 x E4M3 (format selectors 4 and 0), K = 128, from zero.  A: 16 bytes per lane, K
+// 32*(l/16)..+31 of row l%16, two codes a byte, the lower K in the low nibble, its 32 values
+// scaled by the lane's E8M0 byte `sa`; B: 32 bytes per lane, bytes 0-15 holding K 16*(l/16)..
+// and bytes 16-31 K 64+16*(l/16).. of column l%16 (B's scale field is 127 = 2^0).
+__device__ __forceinline__ f32x4 mfma_mx(i32x4 a, i32x8 b, int sa) {
+  const i32x8 a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b, f32x4{0.f, 0.f, 0.f, 0.f}, 4,
+                                                          0, 0, sa, 0, 127);
 }
 
 // ----------------------------------------------------------------------------- buffer loads
@@ -211,16 +211,6 @@ __device__ __forceinline__ float wave_max(float v) {
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
-// Maximum over each row of 16 lanes (lanes 16q .. 16q+15), by DPP lane permutes: quad swaps,
-// then the half-row and row mirrors.
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
   return v;
 }
 
