@@ -86,6 +86,16 @@ SMALL = {
                                                     d_model=512, num_experts=4, top_k=2,
                                                     d_ff=768, num_shared=1, d_ff_shared=512,
                                                     router_dtype=BF16, seed=25),
+    # one 128-deep K step per gate/up tile: with the deep LDS ring of the row-light E4M3 tiles
+    # the loads run several tiles ahead of the MFMAs
+    "fp8_decode_k128": PRESETS["fp8_block"].with_(name="fp8_decode_k128", num_tokens=20,
+                                                  d_model=128, num_experts=16, top_k=2,
+                                                  d_ff=512, num_shared=1, d_ff_shared=512,
+                                                  seed=26),
+    "mxfp4_decode_k128": PRESETS["mxfp4_decode"].with_(name="mxfp4_decode_k128", num_tokens=20,
+                                                       d_model=128, num_experts=16, top_k=2,
+                                                       d_ff=512, num_shared=1, d_ff_shared=256,
+                                                       seed=27),
 }
 
 
