@@ -247,8 +247,15 @@ void grouped_gemm_kernel(GemmArgs a) {
   // wave's lanes cover 8 consecutive rows per load instruction.
   const bool gather = a.a_map != nullptr;
   const i32x4 map_rs = rsrc_words(a.a_map, static_cast<uint32_t>(a.M) * 4);
+  // The geometry of the issuing side's current tile and of the one before it, kept for the
+  // epilogues: with at least NSLOT - 1 steps per tile the consuming side is on one of the two.
+  TileGeo g_iss{}, g_prev{};
+  int g_iss_t = -1;
   auto setup = [&](int t) {
     const TileGeo g = geo(t);
+    g_prev = g_iss;
+    g_iss = g;
+    g_iss_t = t;
 #pragma unroll
     for (int i = 0; i < S::A_PER; ++i) {
       const int c = tid + S::NT * i, r = c >> 3;
@@ -653,7 +660,8 @@ void grouped_gemm_kernel(GemmArgs a) {
   };
   auto xpose2 = [&](uint2 v) { return uint2{xpose(v.x), xpose(v.y)}; };
   auto epilogue = [&](int t) __attribute__((always_inline)) {
-    const TileGeo g = geo(t);
+    // (uniform) the kept geometry, or the tile-list lookup when the issuing side is further on
+    const TileGeo g = t == g_iss_t ? g_iss : t + 1 == g_iss_t ? g_prev : geo(t);
     const __amdgpu_buffer_rsrc_t orsrc =
         buffer_rsrc(static_cast<uint8_t*>(a.out) + static_cast<int64_t>(g.m0) * a.ldo,
                     static_cast<uint32_t>(g.rows * a.ldo));
