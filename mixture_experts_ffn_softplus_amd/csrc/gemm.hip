@@ -15,16 +15,15 @@
 // bytes per step (64 bf16, 32 fp32 or 128 E4M3 values -- exactly one FP8 scale block).  Every
 // step's A rows (gathered through a_map: no permuted copy of x is ever written) and B rows go
 // straight from global memory into an LDS ring of three slots (up to eight for row-light E4M3
-// tiles) with buffer loads that write LDS directly, issued as many steps ahead across tile
-// boundaries, so the next tile's operands are
-// already arriving while the current tile's epilogue stores its results from registers.  The
-// 16-byte chunks land XOR-swizzled by row so that fragment reads of 16 consecutive rows hit
-// distinct banks; fragments of step s+1 are read from LDS while the MFMAs of step s run, one
-// barrier per step.  bf16 and fp32 weights of an expert whose rows fit one tile are loaded
-// non-temporally (read once); others keep the default policy so the expert's other row tiles
-// find them in L2.  (With E4M3 activations, and in launches of one group, a step's loads go out
-// between its MFMAs with the default policy: measured on MI355X, the non-temporal hint gains
-// nothing with E4M3 activations.)
+// tiles) with buffer loads that write LDS directly, issued as many steps ahead, across tile
+// boundaries: the next tile's operands are already arriving while the current tile's epilogue
+// stores its results from registers.  The 16-byte chunks land XOR-swizzled by row so that
+// fragment reads of 16 consecutive rows hit distinct banks; fragments of step s+1 are read
+// from LDS while the MFMAs of step s run, one barrier per step.  bf16 and fp32 weights of an
+// expert whose rows fit one tile are loaded non-temporally (read once); others keep the default
+// policy so the expert's other row tiles find them in L2.  (With E4M3 activations, and in
+// launches of one group, a step's loads go out between its MFMAs with the default policy:
+// measured on MI355X, the non-temporal hint gains nothing with E4M3 activations.)
 #include <math.h>
 
 #include <type_traits>
@@ -109,7 +108,8 @@ struct GemmShape {
 };
 
 // Register fragments of one pipeline step: two 16x16x32 (bf16) or 16x16x4-by-4 (fp32) K-halves,
-// or one 16x16x128 E4M3 block with its row scales and the wave's two weight-block scales.
+// or one 16x16x128 E4M3 block with the activation scale of the lane's own row (sa; see the
+// epilogues for the accumulator layout) and the wave's two weight-block scales.
 template <int DT, int FM, int FN>
 struct Frags {
   using V = typename std::conditional<DT == MOE_BF16, bf16x8, f32x4>::type;
@@ -126,8 +126,9 @@ struct Frags<MOE_FP8_E4M3, FM, FN> {
   float sa[2][FM];
   float sb[2][2];
 };
-// E4M3 activations against E2M1 weights: 32 B of A and 16 B of B per lane, the lane's E8M0
-// weight scale (its column, its 32-value block) in the low byte of sbx; sets as for E4M3.
+// E4M3 activations against E2M1 weights: 32 B of activations and 16 B of weights per lane, the
+// lane's E8M0 weight scale (its output column, its 32-value block) in the low byte of sbx; sets
+// as for E4M3.
 template <int FM, int FN>
 struct Frags<MOE_MXFP4, FM, FN> {
   i32x8 a[2][FM];
@@ -236,7 +237,7 @@ void grouped_gemm_kernel(GemmArgs a) {
     const int wc = wv * kWave + S::NT * i;
     b_dst[i] = wc < S::B_CHUNKS ? BM * kBlockK + wc * 16 : -1;
   }
-  // Per-tile state of the issuing side, which runs up to three steps (and so possibly one or
+  // Per-tile state of the issuing side, which runs up to NSLOT steps (and so possibly one or
   // more tiles) ahead of the multiplying side.
   uint32_t a_off[S::A_PER], b_off[S::B_PER];
   i32x4 b_rs, s_rs = rsrc_words(a.A, 0);
@@ -409,8 +410,8 @@ void grouped_gemm_kernel(GemmArgs a) {
       const uint32_t* bsc = reinterpret_cast<const uint32_t*>(sa + STAGE_BYTES + S::ASW * 256);
 #pragma unroll
       for (int i = 0; i < S::FM; ++i) {
-        // A in the MFMA's K order for an E2M1 partner: bytes 0-15 of the lane hold K
-        // 16*kq.., bytes 16-31 K 64+16*kq.. (the E4M3 fragment layout)
+        // activations in the MFMA's K order for an E2M1 partner: bytes 0-15 of the lane hold
+        // K 16*kq.., bytes 16-31 K 64+16*kq.. (the E4M3 fragment layout)
         f.a[0][i] = frag_e4m3(sa, wm * S::TM + i * 16 + lr);
         f.sa[0][i] = ss[wm * S::TM + i * 16 + lr];
       }
@@ -468,7 +469,7 @@ void grouped_gemm_kernel(GemmArgs a) {
   };
   // bf16 / fp32 step: the MFMAs of step g from `cur` while step g+1's fragments are read into
   // `nxt`, one fragment read then its share of the MFMAs, repeated (the reads spread over the
-  // MFMAs instead of bunching at either end).  spread: load n of step g+3 goes out after
+  // MFMAs instead of bunching at either end).  spread: load n of step g+NSLOT goes out after
   // fragment read n * NR / LPS (the inline-asm loads keep their place among the LDS reads, both
   // touching memory, which the group barriers interleave with the MFMAs); otherwise the caller
   // has issued them.  Grouped launches issue in one burst: their per-tile cache policy (see
@@ -550,7 +551,7 @@ void grouped_gemm_kernel(GemmArgs a) {
             for (int e = 0; e < 4; ++e) acc[pi][pj][e] = fmaf(prev[e], qq, acc[pi][pj][e]);
           }
           prev = cur;
-          if (i * S::FN + j < S::LPS) issue_load(i * S::FN + j, kKeep);  // step g+3's loads
+          if (i * S::FN + j < S::LPS) issue_load(i * S::FN + j, kKeep);  // step g+NSLOT's loads
           if (i == 0) f.b[Q][j] = frag_e4m3(sb, wn * S::TN + j * 16 + lr);
           if (i == XI && j == XJ_A) {
             f.a[Q][L] = frag_e4m3(sa, wm * S::TM + L * 16 + lr);
@@ -610,7 +611,7 @@ void grouped_gemm_kernel(GemmArgs a) {
             for (int e = 0; e < 4; ++e) acc[pi][pj][e] = fmaf(prev[e], qq, acc[pi][pj][e]);
           }
           prev = cur;
-          if (i * S::FN + j < S::LPS) issue_load(i * S::FN + j, kKeep);  // step g+3's loads
+          if (i * S::FN + j < S::LPS) issue_load(i * S::FN + j, kKeep);  // step g+NSLOT's loads
           if (i == 0) {
             const int r = wn * S::TN + j * 16 + lr;
             f.b[Q][j] = *reinterpret_cast<const i32x4*>(sb + swz4(r, kq));
@@ -753,7 +754,7 @@ void grouped_gemm_kernel(GemmArgs a) {
   // slot g any more); issue step g+NSLOT into slot g; read the fragments of step g+1 while the
   // MFMAs of step g run; after a tile's last step, store it.  bf16 and fp32 alternate two whole fragment sets;
   // E4M3 activations (FP8 and MXFP4 experts) alternate part of one (see Frags).  These, and
-  // launches of one group, issue the loads of step g+3 between the MFMAs of step g rather than
+  // launches of one group, issue the loads of step g+NSLOT between the MFMAs of step g rather than
   // in one burst after the barrier.
   constexpr bool kTwoSets = !S::kFp8;
   constexpr std::integral_constant<int, 0> kEven{};
