@@ -29,25 +29,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
-// E4M3FN code nearest to r: ties to even, saturating at +-448 (NaN inputs unsupported).
-__device__ __forceinline__ uint32_t f32_to_e4m3(float r) {
-  uint32_t u = __float_as_uint(r);
-  uint32_t sign = (u >> 24) & 0x80u;
-  float a = fabsf(r);
-  if (a >= 448.0f) return sign | 0x7Eu;
-  if (a < 0.015625f) {                       // below 2^-6: multiples of 2^-9
-    uint32_t m = static_cast<uint32_t>(rintf(a * 512.0f));  // exact scaling, RNE
-    return sign | m;                          // m == 8 encodes 2^-6 correctly
-  }
-  uint32_t ua = __float_as_uint(a);
-  ua += 0x7FFFFu + ((ua >> 20) & 1u);         // round the 23-bit mantissa to 3 bits, ties even
-  uint32_t e = ((ua >> 23) & 0xFFu) - 127u + 7u;
-  uint32_t m = (ua >> 20) & 7u;
-  return sign | (e << 3) | m;
-}
-
-// Four E4M3FN codes (byte i from value i) by the hardware conversion (round to nearest even,
-// the same codes as f32_to_e4m3 for |r| <= 448); inputs are clamped to +-448 first.
+// Four E4M3FN codes (byte i from value i): the nearest code, ties to even, saturating at
+// +-448 -- the hardware conversion (round to nearest even) after a clamp to +-448 (NaN inputs
+// unsupported).
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   const float lim = 448.0f;
   a = fminf(fmaxf(a, -lim), lim);

@@ -205,11 +205,8 @@ __global__ __launch_bounds__(256) void quant_x_fp8_kernel(const uint16_t* __rest
 #pragma unroll
   for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
   const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(v[i] / s) << (8 * i);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(v[4 + i] / s) << (8 * i);
+  const uint32_t lo = e4m3x4(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
+  const uint32_t hi = e4m3x4(v[4] / s, v[5] / s, v[6] / s, v[7] / s);
   if (valid) {
     uint2 packed{lo, hi};
     *reinterpret_cast<uint2*>(xq + base) = packed;
