@@ -238,9 +238,8 @@ def main():
                          "scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs the block on one GPU; --gpus {args.gpus} is not "
-              f"supported (expert-parallel sharding is described in DESIGN.md, not built)",
-              file=sys.stderr)
+        print(f"bench.py: the MoE block runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(no expert-parallel sharding is implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch

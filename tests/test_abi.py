@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -190,3 +191,13 @@ def test_hashed_route_and_bias_update_argument_checks():
     assert L.moe_update_bias(cp, 8, -0.001, 8, None) == 1
     bad = api.config_struct(PRESETS["tiny_fp32"], top_k=0)
     assert L.moe_update_bias(ctypes.byref(bad), 8, 0.001, 8, None) == 1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: any other --gpus value exits with status 2 and a message,
+    before anything touches a GPU."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
