@@ -10,6 +10,7 @@ import argparse
 import ctypes
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -305,6 +306,9 @@ def main():
     for s, name in enumerate(api.STAGES):
         stage_ms[name] = sum(hip.elapsed_ms(ev[i][s], ev[i][s + 1])
                              for i in range(args.steps)) / args.steps
+    # each step from its first to its last stage boundary: median and minimum beside the mean
+    step_times = sorted(hip.elapsed_ms(ev[i][0], ev[i][n_ev - 1]) for i in range(args.steps))
+    step_median = statistics.median(step_times)
     for e in ev:
         hip.destroy(e)
     log("stage ms: " + ", ".join(f"{k}={v:.4f}" for k, v in stage_ms.items()))
@@ -353,6 +357,7 @@ def main():
     result = {
         "metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "step_ms_median": round(step_median, 5), "step_ms_min": round(step_times[0], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": DTYPE_NAME[cfg.expert_dtype], "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": T, "d_model": d,

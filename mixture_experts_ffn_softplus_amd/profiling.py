@@ -10,6 +10,12 @@ DIRs are rocprofv3 output directories (``--output-format csv``): ``--trace`` fro
 ``--copy-mib`` MiB (``bench.py --copy-calibration``), whose known size scales the counters to
 bytes.  The summary records a hash of the kernel sources so that a stale traffic figure is
 never reported for a kernel that has changed since it was measured.
+
+    python -m mixture_experts_ffn_softplus_amd.profiling counters --pmc DIR --counter NAME \
+        --kernel LABEL=REGEX ... --workload NAME --command "..." --out profiles/NAME.txt
+
+summarises one counter of a ``--pmc`` run (e.g. the derived MfmaUtil: MFMA-busy cycles over
+GPU-active cycles of every SIMD, in percent) per kernel pattern.
 """
 import argparse
 import csv
@@ -124,6 +130,29 @@ def durations(a):
     print("\n".join(lines))
 
 
+def counters(a):
+    """One counter (a plain or derived rocprofv3 counter, e.g. MfmaUtil) per kernel pattern:
+    its mean, median and minimum over the dispatches of a --pmc run."""
+    lines = [
+        f"# rocprofv3 counter {a.counter} on workload {a.workload}",
+        f"# commands (from the repository root):",
+        *[f"#   {c}" for c in a.command],
+        f"# summarised by: python -m mixture_experts_ffn_softplus_amd.profiling counters ...",
+        f"source_sha256: {source_hash()}",
+        f"workload: {a.workload}",
+        f"counter: {a.counter}",
+    ]
+    for name, pattern in (kv.split("=", 1) for kv in a.kernel):
+        v = counter_values(a.pmc, a.counter, pattern)
+        lines += [f"{name}_regex: {pattern}", f"{name}_dispatches: {len(v)}",
+                  f"{name}_mean: {statistics.mean(v):.3f}",
+                  f"{name}_median: {statistics.median(v):.3f}",
+                  f"{name}_min: {min(v):.3f}"]
+    with open(a.out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def read_summary(path: str) -> dict:
     """key: value lines of a summary file (comments and tables skipped)."""
     out = {}
@@ -160,12 +189,19 @@ def main():
         d.add_argument("--" + k, dest=k, required=True)
     d.add_argument("--kernel", action="append", default=[], metavar="NAME=REGEX")
     d.add_argument("--command", action="append", default=[])
+    c = sub.add_parser("counters")
+    for k in ("pmc", "counter", "workload", "out"):
+        c.add_argument("--" + k, dest=k, required=True)
+    c.add_argument("--kernel", action="append", default=[], metavar="NAME=REGEX")
+    c.add_argument("--command", action="append", default=[])
     sub.add_parser("hash")
     a = ap.parse_args()
     if a.cmd == "hash":
         print(source_hash())
     elif a.cmd == "durations":
         durations(a)
+    elif a.cmd == "counters":
+        counters(a)
     else:
         summarize(a)
 
