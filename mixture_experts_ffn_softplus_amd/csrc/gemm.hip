@@ -750,12 +750,12 @@ void grouped_gemm_kernel(GemmArgs a) {
   // ---------------------------------------------------------------- the pipeline
   // Global step g runs through this workgroup's tiles back to back.  Iteration g: wait for
   // this wave's loads of step g+1 (those of g+2 .. g+NSLOT-1 stay in flight) and for its own
-  // fragment reads of step g; barrier (every wave's step-(g+1) data is in LDS and nobody reads
-  // slot g any more); issue step g+NSLOT into slot g; read the fragments of step g+1 while the
-  // MFMAs of step g run; after a tile's last step, store it.  bf16 and fp32 alternate two whole
-  // fragment sets; E4M3 activations (FP8 and MXFP4 experts) alternate part of one (see Frags).
-  // These, and launches of one group, issue the loads of step g+NSLOT between the MFMAs of step
-  // g rather than in one burst after the barrier.
+  // fragment reads of step g (lds_dma_wait waits for both); barrier (every wave's step-(g+1)
+  // data is in LDS and nobody reads slot g any more); issue step g+NSLOT into slot g; read the
+  // fragments of step g+1 while the MFMAs of step g run; after a tile's last step, store it.
+  // bf16 and fp32 alternate two whole fragment sets; E4M3 activations (FP8 and MXFP4 experts)
+  // alternate part of one (see Frags).  These, and launches of one group, issue the loads of
+  // step g+NSLOT between the MFMAs of step g rather than in one burst after the barrier.
   constexpr bool kTwoSets = !S::kFp8;
   constexpr std::integral_constant<int, 0> kEven{};
   constexpr std::integral_constant<int, 1> kOdd{};

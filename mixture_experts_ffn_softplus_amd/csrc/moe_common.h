@@ -174,13 +174,20 @@ __device__ __forceinline__ int select8(i32x8 v, int idx) {
   return r;
 }
 
-// Wait until at most N vector-memory operations of this wave are outstanding.  The counter
-// retires loads and stores in issue order, so vmcnt(N) means every operation but the N most
-// recently issued is complete.
+// Wait until at most N vector-memory operations of this wave are outstanding and every LDS
+// operation of this wave has completed.  The vector counter retires loads and stores in issue
+// order, so vmcnt(N) means every operation but the N most recently issued is complete.
+// Before the barrier that precedes refilling an LDS slot both halves are needed: the loads of
+// the slot about to be read must have landed, and this wave's own reads of the slot about to
+// be refilled must have executed.  s_barrier waits on no counter, and the compiler adds no LDS
+// wait at a workgroup barrier (LDS instructions of all waves execute in one order), but a
+// direct-to-LDS load writes LDS outside that order: a refill that returns early (zeros past a
+// tile's last row, an L2 hit) could otherwise overwrite a slot that another wave's fragment
+// read, issued before the barrier, has not yet reached.
 template <int N>
 __device__ __forceinline__ void lds_dma_wait() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" :: "n"(N) : "memory");
 }
 
 // ----------------------------------------------------------------------------- wave utilities

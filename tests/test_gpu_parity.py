@@ -96,6 +96,14 @@ SMALL = {
                                                        d_model=128, num_experts=16, top_k=2,
                                                        d_ff=512, num_shared=1, d_ff_shared=256,
                                                        seed=27),
+    # about 12 rows per expert: 16-row bf16 tiles, nearly all of them ragged, whose refills of
+    # the zero rows past a tile's end return early (the LDS ring must not refill a slot before
+    # every wave's fragment reads of it have executed)
+    "bf16_short_tiles": BF.with_(name="bf16_short_tiles", num_tokens=130, d_model=256,
+                                 num_experts=96, top_k=9, d_ff=512, num_shared=1,
+                                 d_ff_shared=128, score=SQRT_SOFTPLUS, renormalize=0,
+                                 routed_scale=2.5, select_bias_range=0.1, shared_gate=1,
+                                 seed=1011),
 }
 
 
@@ -154,13 +162,15 @@ def test_split_api_matches_forward_bit_exact(name):
     assert torch.equal(out, out_f)
 
 
-def test_forward_is_deterministic():
-    cfg = SMALL["bf16_softmax_ragged"]
-    layer = Layer(cfg)
-    a = layer.forward()
-    b = layer.forward()
-    torch.cuda.synchronize()
-    assert torch.equal(a, b)
+@pytest.mark.parametrize("name", ["bf16_softmax_ragged", "bf16_short_tiles", "fp8_decode_rows"])
+def test_forward_is_deterministic(name):
+    # repeated forwards: a race inside a kernel shows as an occasional different result (a
+    # slot refilled too early once changed a whole row tile in about one forward in seven of
+    # bf16_short_tiles)
+    layer = Layer(SMALL[name])
+    first = layer.forward()
+    for _ in range(40):
+        assert torch.equal(layer.forward(), first)
 
 
 def test_route_from_logits_with_ties_bit_exact():
