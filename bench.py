@@ -67,7 +67,8 @@ def algorithmic(cfg, touched):
     wb = WEIGHT_BYTES[cfg.expert_dtype]
     rb = 4 if cfg.router_dtype == 0 else 2
     xb = 4 if cfg.act_dtype == 0 else 2
-    step_bytes = int(touched * 3 * d * f * wb + S * 3 * d * fs * wb + d * E * rb + 2 * T * d * xb)
+    ob = 4 if cfg.act_dtype == 0 or cfg.out_f32 else 2
+    step_bytes = int(touched * 3 * d * f * wb + S * 3 * d * fs * wb + d * E * rb + T * d * (xb + ob))
     step_flops = 2 * T * d * E + 6 * T * k * d * f + 6 * T * d * S * fs
     gate_up_bytes = int(touched * 2 * d * f * wb + T * d * xb)
     gate_up_flops = 4 * T * k * d * f
@@ -364,6 +365,7 @@ def main():
                    "experts": cfg.num_experts, "top_k": cfg.top_k, "d_ff": cfg.d_ff,
                    "shared": cfg.num_shared, "d_ff_shared": cfg.d_ff_shared,
                    "router": ["softmax", "sigmoid", "sqrt_softplus"][cfg.score],
+                   "output": "f32" if cfg.act_dtype == 0 or cfg.out_f32 else "bf16",
                    "parallelism": "single_gpu"},
         "roofline": roofline, "step_roofline": step, "stage_ms": {k: round(v, 5) for k, v in
                                                                    stage_ms.items()},

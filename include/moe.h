@@ -80,7 +80,8 @@ typedef struct {
   int32_t score;         /* MOE_SCORE_* */
   int32_t renormalize;   /* 1: normalise the weights over the selected experts */
   float routed_scale;    /* gamma: routed weights are multiplied by it (2.5 / 1) */
-  int32_t act_dtype;     /* storage of x and of the output: MOE_F32 or MOE_BF16 */
+  int32_t act_dtype;     /* storage of x (and of the output unless out_f32): MOE_F32 or
+                            MOE_BF16 */
   int32_t expert_dtype;  /* expert weights (routed and shared); MOE_FP8_E4M3 and
                             MOE_MXFP4 also quantise x and h to block-scaled E4M3 */
   int32_t router_dtype;  /* storage of W_r: MOE_F32 or MOE_BF16 */
@@ -91,6 +92,9 @@ typedef struct {
                             Gemma 4 31B"); x~ is what the shared experts read (the
                             block-scaled x for FP8 experts).  0: ungated (the DeepSeek-style
                             shared expert). */
+  int32_t out_f32;       /* 1: the block output is stored as fp32 whatever act_dtype, so the
+                            combine's fp32 sum is not rounded again; 0: it is stored in
+                            act_dtype (round to nearest even from that same fp32 sum). */
 } moe_config_t;
 
 /* Weights in the caller's logical layout, for moe_pack_weights (device pointers).
@@ -283,7 +287,8 @@ MOE_API moe_status_t moe_expert_ffn(const moe_config_t* cfg, const void* x_or_xq
  * active):
  * out[t] = G[t] * sum_s SwiGLU_s(x~[t]) + sum_j topk_w[t,j] * y_perm[inv_perm[t*k+j]],
  * G[t] = sigmoid(x~[t] . ws_gate_vec) when cfg->shared_gate (else 1).
- * out [T,d] act_dtype.  The residual add outside the block is not included. */
+ * out [T,d]: fp32 when cfg->out_f32, else act_dtype.  The residual add outside the
+ * block is not included. */
 MOE_API moe_status_t moe_combine(const moe_config_t* cfg, const void* x_or_xq, const float* xq_scales,
                          const void* y_perm, const int32_t* inv_perm, const float* topk_w,
                          const moe_weights_t* weights, void* out, void* ws, size_t ws_bytes,

@@ -34,7 +34,7 @@ class moe_config_t(ctypes.Structure):
                 ("renormalize", ctypes.c_int32), ("routed_scale", ctypes.c_float),
                 ("act_dtype", ctypes.c_int32), ("expert_dtype", ctypes.c_int32),
                 ("router_dtype", ctypes.c_int32), ("quant_block", ctypes.c_int32),
-                ("shared_gate", ctypes.c_int32)]
+                ("shared_gate", ctypes.c_int32), ("out_f32", ctypes.c_int32)]
 
 
 _vp = ctypes.c_void_p
@@ -144,7 +144,7 @@ def config_struct(cfg: MoEConfig, **override) -> moe_config_t:
     c = moe_config_t(cfg.num_tokens, cfg.d_model, cfg.num_experts, cfg.top_k, cfg.d_ff,
                      cfg.num_shared, cfg.d_ff_shared, cfg.score, cfg.renormalize,
                      cfg.routed_scale, cfg.act_dtype, cfg.expert_dtype, cfg.router_dtype,
-                     cfg.quant_block, cfg.shared_gate)
+                     cfg.quant_block, cfg.shared_gate, cfg.out_f32)
     for k, v in override.items():
         setattr(c, k, v)
     return c
@@ -152,6 +152,17 @@ def config_struct(cfg: MoEConfig, **override) -> moe_config_t:
 
 def _cfg(cfg):
     return ctypes.byref(cfg if isinstance(cfg, moe_config_t) else config_struct(cfg))
+
+
+def _need(t, cfg, rows, dtype_of, where, what):
+    """A tensor the library writes must be a contiguous [rows, d] buffer of the dtype the
+    config implies: the C entry points take bare pointers and cannot check it."""
+    if not isinstance(t, torch.Tensor) or not isinstance(cfg, MoEConfig):
+        return
+    n, dt = rows * cfg.d_model, dtype_of(cfg)
+    if t.dtype != dt or t.numel() < n or not t.is_contiguous():
+        raise ValueError(f"{where}: {what} must be a contiguous {dt} tensor of at least {n} "
+                         f"elements, got {t.dtype} with {t.numel()}")
 
 
 # ------------------------------------------------------------------ the C entry points
@@ -207,6 +218,8 @@ def moe_permute(cfg, topk_ids, expert_offsets, perm_token, inv_perm, ws, stream=
 
 def moe_expert_ffn(cfg, x_or_xq, xq_scales, expert_offsets, perm_token, weights, y_perm, ws,
                    stream=None):
+    _need(y_perm, cfg, cfg.assignments if isinstance(cfg, MoEConfig) else 0, y_dtype,
+          "moe_expert_ffn", "y_perm")
     _check(lib().moe_expert_ffn(_cfg(cfg), _p(x_or_xq), _p(xq_scales), _p(expert_offsets),
                                 _p(perm_token), ctypes.byref(weights), _p(y_perm), _p(ws),
                                 ws.numel() * ws.element_size(), _stream(stream)),
@@ -215,12 +228,19 @@ def moe_expert_ffn(cfg, x_or_xq, xq_scales, expert_offsets, perm_token, weights,
 
 def moe_combine(cfg, x_or_xq, xq_scales, y_perm, inv_perm, topk_w, weights, out, ws,
                 stream=None):
+    _need(out, cfg, cfg.num_tokens if isinstance(cfg, MoEConfig) else 0, out_dtype,
+          "moe_combine", "out")
     _check(lib().moe_combine(_cfg(cfg), _p(x_or_xq), _p(xq_scales), _p(y_perm), _p(inv_perm),
                              _p(topk_w), ctypes.byref(weights), _p(out), _p(ws),
                              ws.numel() * ws.element_size(), _stream(stream)), "moe_combine")
 
 
 def moe_forward(cfg, x, weights, out, ws, dbg: dict = None, stream=None):
+    _need(out, cfg, cfg.num_tokens if isinstance(cfg, MoEConfig) else 0, out_dtype,
+          "moe_forward", "out")
+    if dbg:
+        _need(dbg.get("y_perm"), cfg, cfg.assignments if isinstance(cfg, MoEConfig) else 0,
+              y_dtype, "moe_forward", "dbg['y_perm']")
     d = None
     if dbg:
         d = moe_debug_t(*[_p(dbg.get(n)) for n, _ in moe_debug_t._fields_])
@@ -239,7 +259,7 @@ def y_dtype(cfg: MoEConfig):
 
 
 def out_dtype(cfg: MoEConfig):
-    return _TORCH_ACT[cfg.act_dtype]
+    return torch.float32 if cfg.out_f32 else _TORCH_ACT[cfg.act_dtype]
 
 
 def workspace(cfg: MoEConfig, device="cuda") -> torch.Tensor:

@@ -26,6 +26,8 @@ int h_bytes(const moe_config_t* c) {
 // Bytes of one packed weight row of K elements (E2M1: two a byte).
 int64_t wrow(const moe_config_t* c, int64_t K) { return is_mx(c) ? K / 2 : K * h_bytes(c); }
 int act_bytes(const moe_config_t* c) { return c->act_dtype == MOE_F32 ? 4 : 2; }
+// bytes per element of the block output
+int out_bytes(const moe_config_t* c) { return c->out_f32 ? 4 : act_bytes(c); }
 // y_perm: fp32 unless the activations are E4M3.  A bf16 y_perm would add a third bf16 rounding
 // (after h and the output) to a budget the output rounding alone half fills.
 int y_bytes(const moe_config_t* c) { return is_fp8(c) ? 2 : 4; }
@@ -82,6 +84,7 @@ moe_status_t check_config(const moe_config_t* c) {
     return MOE_ERR_INVALID_ARGUMENT;
   if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARGUMENT;
   if (c->shared_gate != 0 && c->shared_gate != 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->out_f32 != 0 && c->out_f32 != 1) return MOE_ERR_INVALID_ARGUMENT;
   if (!isfinite(c->routed_scale)) return MOE_ERR_INVALID_ARGUMENT;
   const int dts[3] = {c->act_dtype, c->expert_dtype, c->router_dtype};
   for (int v : dts)
@@ -398,7 +401,7 @@ hipError_t do_combine(const moe_config_t* c, const void* xa, const float* xs, co
       ca.x_scales = xs;
     }
     ca.out = out;
-    ca.out_f32 = act_bytes(c) == 4;
+    ca.out_f32 = out_bytes(c) == 4;
     ca.T = static_cast<int>(T);
     ca.d = static_cast<int>(d);
     e = launch_combine(ca, s);

@@ -8,6 +8,7 @@ import subprocess
 import sys
 
 import pytest
+import torch
 
 from mixture_experts_ffn_softplus_amd import PRESETS, api
 from mixture_experts_ffn_softplus_amd.configs import BF16, F32, FP8_E4M3
@@ -82,6 +83,7 @@ def test_status_strings():
     ("expert_dtype", 4, api.MOE_ERR_INVALID_ARGUMENT),   # no such format
     ("router_dtype", 3, api.MOE_ERR_UNSUPPORTED),        # MXFP4 is for expert weights only
     ("act_dtype", 5, api.MOE_ERR_INVALID_ARGUMENT),
+    ("out_f32", 2, api.MOE_ERR_INVALID_ARGUMENT),
 ])
 def test_config_errors_return_status_without_launch(field, value, status):
     cfg = api.config_struct(PRESETS["tiny_fp32"], **{field: value})
@@ -90,6 +92,22 @@ def test_config_errors_return_status_without_launch(field, value, status):
     w = api.moe_weights_t()
     rc = L.moe_forward(ctypes.byref(cfg), 1, ctypes.byref(w), 1, None, 1, 1 << 40, None)
     assert rc == status
+
+
+@pytest.mark.parametrize("out_f32, dtype", [(1, torch.bfloat16), (0, torch.float32)])
+def test_binding_rejects_an_output_of_another_dtype(out_f32, dtype):
+    # the C entry points take bare pointers: a bf16 buffer for an fp32 output would be
+    # overrun, so the binding refuses it before anything is launched
+    cfg = PRESETS["softmax_bf16"].with_(num_tokens=4, out_f32=out_f32)
+    out = torch.empty(4, cfg.d_model, dtype=dtype)
+    ws = torch.empty(16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="out must be"):
+        api.moe_forward(cfg, None, api.moe_weights_t(), out, ws)
+    with pytest.raises(ValueError, match="out must be"):
+        api.moe_combine(cfg, None, None, None, None, None, api.moe_weights_t(), out, ws)
+    y = torch.empty(cfg.assignments, cfg.d_model, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="y_perm must be"):
+        api.moe_expert_ffn(cfg, None, None, None, None, api.moe_weights_t(), y, ws)
 
 
 def test_large_and_fp8_constraints():

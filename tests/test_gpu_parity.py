@@ -147,7 +147,7 @@ def test_split_api_matches_forward_bit_exact(name):
     perm = torch.empty(A, dtype=torch.int32, device=dev)
     inv = torch.empty(A, dtype=torch.int32, device=dev)
     y = torch.empty(A, d, dtype=api.y_dtype(cfg), device=dev)
-    out = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(T, d, dtype=api.out_dtype(cfg), device=dev)
     x = layer.inp["x"]
     api.moe_route(cfg, x, layer.w, logits, ids, w, ws=layer.ws)
     # route_from_logits on the same logits gives the same ids and weights
@@ -171,6 +171,22 @@ def test_forward_is_deterministic(name):
     first = layer.forward()
     for _ in range(40):
         assert torch.equal(layer.forward(), first)
+
+
+@pytest.mark.parametrize("name", ["bf16_softmax_ragged", "bf16_short_tiles", "fp8_f32_router",
+                                  "mxfp4_decode_rows"])
+def test_bf16_output_is_the_rounded_fp32_output(name):
+    # out_f32 changes only the store of the combine's fp32 sum: the bf16 output is that sum
+    # rounded to nearest even, bit for bit (so its parity follows from the fp32 output's)
+    base = SMALL[name]
+    layer = Layer(base.with_(out_f32=1))
+    full = layer.forward()
+    cfg16 = base.with_(out_f32=0)
+    out = torch.empty(cfg16.num_tokens, cfg16.d_model, dtype=torch.bfloat16, device="cuda")
+    api.moe_forward(cfg16, layer.inp["x"], layer.w, out, layer.ws)
+    torch.cuda.synchronize()
+    assert full.dtype == torch.float32
+    assert torch.equal(out, full.to(torch.bfloat16))
 
 
 def test_route_from_logits_with_ties_bit_exact():
@@ -273,7 +289,7 @@ def test_zero_tokens_launches_nothing():
     cfg = SMALL["bf16_softmax_ragged"]
     layer = Layer(cfg)
     c0 = cfg.with_(num_tokens=0)
-    out = torch.full((1, cfg.d_model), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = torch.full((1, cfg.d_model), 7.0, dtype=api.out_dtype(cfg), device="cuda")
     api.moe_forward(c0, layer.inp["x"], layer.w, out, layer.ws)
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
@@ -281,9 +297,10 @@ def test_zero_tokens_launches_nothing():
 
 def test_identity_like_experts_reproduce_input():
     # f = d; x[:, 0] = 1; gate columns 32 e_0; up = I/32; down = I; shared down = 0 -> out = x
+    # (bf16 output: its rounding is what the bound below allows for)
     cfg = BF.with_(name="identity", num_tokens=96, d_model=128, num_experts=8, top_k=3,
                    d_ff=128, num_shared=1, d_ff_shared=128, score=SQRT_SOFTPLUS,
-                   routed_scale=2.5)
+                   routed_scale=2.5, out_f32=0)
     d, E = 128, 8
     inp = synth.inputs(cfg, "cuda")
     x = inp["x"].clone()
@@ -298,7 +315,7 @@ def test_identity_like_experts_reproduce_input():
               "down": torch.zeros(1, d, d, dtype=torch.bfloat16, device="cuda")}
     pw = api.pack(cfg, inp["w_router"], routed, shared)
     ws = api.workspace(cfg)
-    out = torch.empty_like(x)
+    out = torch.empty(x.shape, dtype=api.out_dtype(cfg), device="cuda")
     api.moe_forward(cfg, x, pw.struct(), out, ws)
     torch.cuda.synchronize()
     # the output is the bf16 rounding of sum_j w_j x with sum_j w_j = 2.5 up to fp32 rounding:
