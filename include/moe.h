@@ -295,7 +295,8 @@ MOE_API moe_status_t moe_combine(const moe_config_t* cfg, const void* x_or_xq, c
                          hipStream_t stream);
 
 /* The whole block: moe_route -> moe_permute -> moe_expert_ffn -> moe_combine on
- * one stream with no host synchronisation.  dbg may be NULL (host struct). */
+ * one stream with no host synchronisation.  out as for moe_combine (fp32 when
+ * cfg->out_f32, else act_dtype).  dbg may be NULL (host struct). */
 MOE_API moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const moe_weights_t* weights,
                          void* out, const moe_debug_t* dbg, void* ws, size_t ws_bytes,
                          hipStream_t stream);
