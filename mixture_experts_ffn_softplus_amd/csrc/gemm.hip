@@ -68,6 +68,9 @@ struct GemmShape {
   // E2M1 weights with one E8M0 scale per column and 32 K values, applied inside the MFMA
   static constexpr bool kMx = DT == MOE_MXFP4;
   static constexpr int B_ROW = kMx ? 64 : kBlockK;    // bytes of one B row per step
+  // bytes between consecutive steps of one B row: E2M1 weights are packed by column tile and
+  // step (a tile's step is one contiguous BN x 64-byte block), the others row-major
+  static constexpr int B_STEP = kMx ? BN * 64 : kBlockK;
   static constexpr int A_CHUNKS = BM * 8, B_CHUNKS = BN * (B_ROW / 16);  // 16-byte chunks
   static constexpr int A_PER = (A_CHUNKS + NT - 1) / NT, B_PER = (B_CHUNKS + NT - 1) / NT;
   static constexpr int STAGE = BM * kBlockK + BN * B_ROW;
@@ -276,10 +279,10 @@ void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < S::B_PER; ++i) {
       const int c = tid + S::NT * i;
-      if constexpr (S::kMx) {  // 64-byte rows, see swz4
+      if constexpr (S::kMx) {  // 64-byte rows, see swz4; the tile's block starts at n0 * ldb
         const int r = c >> 2;
         b_off[i] = c < S::B_CHUNKS
-                       ? static_cast<uint32_t>(static_cast<int64_t>(g.n0 + r) * ldb +
+                       ? static_cast<uint32_t>(static_cast<int64_t>(g.n0) * ldb + r * 64 +
                                                (((c & 3) ^ ((r >> 1) & 2)) << 4))
                        : kOob;
       } else {
@@ -354,7 +357,7 @@ void grouped_gemm_kernel(GemmArgs a) {
     iss_slot = iss_slot + 1 == S::NSLOT ? 0 : iss_slot + 1;
     ++iss_s;
     q_as = static_cast<uint32_t>(step < a_steps ? step : step - a_steps) * kBlockK;
-    q_bs = static_cast<uint32_t>(step) * S::B_ROW;
+    q_bs = static_cast<uint32_t>(step) * S::B_STEP;
     q_ss = static_cast<uint32_t>(step) * 4;
   };
   // nt: the weights' loads are non-temporal (stream_b of the step being issued)
@@ -871,8 +874,8 @@ static hipError_t launch_dt(int bm, const GemmArgs& a, int max_tiles, hipStream_
       constexpr int BMv = decltype(bm_tag)::value;
       if constexpr (EPI == kEpiSwiglu) return launch_one<DT, BMv, 256, EPI, G>(a, max_tiles, s);
       else
-        return a.N % 256 == 0 ? launch_one<DT, BMv, 256, EPI, G>(a, max_tiles, s)
-                              : launch_one<DT, BMv, 128, EPI, G>(a, max_tiles, s);
+        return e4m3_tile_n(EPI, a.N) == 256 ? launch_one<DT, BMv, 256, EPI, G>(a, max_tiles, s)
+                                            : launch_one<DT, BMv, 128, EPI, G>(a, max_tiles, s);
     };
     switch (bm) {
       case 16: return wide(std::integral_constant<int, 16>{});

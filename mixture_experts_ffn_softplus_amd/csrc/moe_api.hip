@@ -312,28 +312,33 @@ hipError_t do_expert_ffn(const moe_config_t* c, const void* xa, const float* xs,
 hipError_t pack_mx(const moe_config_t* c, const moe_logical_weights_t* lw, void* const* packed,
                    hipStream_t s) {
   const int d = c->d_model, f = c->d_ff, E = c->num_experts;
+  // E2M1 weights by column tile and K-step (one contiguous block per step of a tile, the
+  // GEMMs' tile widths); the E8M0 scales stay row-major
+  const int tn_gu = e4m3_tile_n(kEpiSwiglu, 2 * f), tn_dn = e4m3_tile_n(kEpiStore, d);
   hipError_t e = launch_pack_rows_gate_up(lw->w_gate, lw->w_up, packed[MOE_PACK_GATE_UP], f, 1,
-                                          E, d / 2, s);
+                                          E, d / 2, tn_gu, s);
   if (e == hipSuccess)
     e = launch_pack_rows_gate_up(lw->w_gate_scales, lw->w_up_scales,
-                                 packed[MOE_PACK_GATE_UP_SCALES], f, 1, E, d / 32, s);
+                                 packed[MOE_PACK_GATE_UP_SCALES], f, 1, E, d / 32, 0, s);
   if (e == hipSuccess)
-    e = launch_pack_rows_concat(lw->w_down, packed[MOE_PACK_DOWN], d, 1, E, f / 2, s);
+    e = launch_pack_rows_concat(lw->w_down, packed[MOE_PACK_DOWN], d, 1, E, f / 2, tn_dn, s);
   if (e == hipSuccess)
     e = launch_pack_rows_concat(lw->w_down_scales, packed[MOE_PACK_DOWN_SCALES], d, 1, E,
-                                f / 32, s);
+                                f / 32, 0, s);
   if (e != hipSuccess || c->num_shared == 0) return e;
   const int S = c->num_shared, fs = c->d_ff_shared;
+  const int tn_sgu = e4m3_tile_n(kEpiSwiglu, 2 * S * fs);
   e = launch_pack_rows_gate_up(lw->ws_gate, lw->ws_up, packed[MOE_PACK_SHARED_GATE_UP], fs, S, 1,
-                               d / 2, s);
+                               d / 2, tn_sgu, s);
   if (e == hipSuccess)
     e = launch_pack_rows_gate_up(lw->ws_gate_scales, lw->ws_up_scales,
-                                 packed[MOE_PACK_SHARED_GATE_UP_SCALES], fs, S, 1, d / 32, s);
+                                 packed[MOE_PACK_SHARED_GATE_UP_SCALES], fs, S, 1, d / 32, 0, s);
   if (e == hipSuccess)
-    e = launch_pack_rows_concat(lw->ws_down, packed[MOE_PACK_SHARED_DOWN], d, S, 1, fs / 2, s);
+    e = launch_pack_rows_concat(lw->ws_down, packed[MOE_PACK_SHARED_DOWN], d, S, 1, fs / 2,
+                                tn_dn, s);
   if (e == hipSuccess)
     e = launch_pack_rows_concat(lw->ws_down_scales, packed[MOE_PACK_SHARED_DOWN_SCALES], d, S, 1,
-                                fs / 32, s);
+                                fs / 32, 0, s);
   return e;
 }
 
