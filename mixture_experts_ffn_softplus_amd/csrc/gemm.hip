@@ -245,6 +245,9 @@ void grouped_gemm_kernel(GemmArgs a) {
   uint32_t a_off[S::A_PER], b_off[S::B_PER];
   i32x4 b_rs, s_rs = rsrc_words(a.A, 0);
   uint32_t s_off = kOob;
+  // bytes per step of this wave's scale loads: the E8M0 waves read step-major blocks of BN
+  // dwords, the others one dword per step of a row-major row
+  const uint32_t s_step = S::kMx && wv >= S::ASW && wv < S::ASW + S::BSW ? BN * 4u : 4u;
   int s_dst = 0;
   bool stream_b = false;
   // The gathered rows of a tile come through the scalar path (see scalar_buffer_load32): a
@@ -317,12 +320,12 @@ void grouped_gemm_kernel(GemmArgs a) {
       } else if (wv < S::ASW + S::BSW) {
         const int bw = wv - S::ASW;
         if constexpr (S::kMx) {
-          // E8M0 scales [N, K/32] bytes per group: column n's four scales of a step are one
-          // dword at n * K/32 + 4 * step
+          // E8M0 scales [N, K/32] bytes per group, by column tile and step: column n0 + c's
+          // four scales of a step are one dword at n0 * K/32 + 4 * c + BN * 4 * step
           const int kb32 = a.K / 32;
           s_rs = rsrc_words(a.b_e8m0 + g.group * a.be_group_stride,
                             static_cast<uint32_t>(a.N) * kb32);
-          s_off = static_cast<uint32_t>(g.n0 + bw * 64 + l) * kb32;
+          s_off = static_cast<uint32_t>(g.n0) * kb32 + static_cast<uint32_t>(bw * 64 + l) * 4;
         } else {
           s_rs = rsrc_words(a.b_scales + g.group * a.bs_group_stride,
                             static_cast<uint32_t>((a.N / 16) * kb_bytes));
@@ -358,7 +361,7 @@ void grouped_gemm_kernel(GemmArgs a) {
     ++iss_s;
     q_as = static_cast<uint32_t>(step < a_steps ? step : step - a_steps) * kBlockK;
     q_bs = static_cast<uint32_t>(step) * S::B_STEP;
-    q_ss = static_cast<uint32_t>(step) * 4;
+    q_ss = static_cast<uint32_t>(step) * s_step;
   };
   // nt: the weights' loads are non-temporal (stream_b of the step being issued)
   auto issue_load = [&](int n, auto nt) __attribute__((always_inline)) {

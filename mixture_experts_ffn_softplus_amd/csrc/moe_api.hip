@@ -312,33 +312,34 @@ hipError_t do_expert_ffn(const moe_config_t* c, const void* xa, const float* xs,
 hipError_t pack_mx(const moe_config_t* c, const moe_logical_weights_t* lw, void* const* packed,
                    hipStream_t s) {
   const int d = c->d_model, f = c->d_ff, E = c->num_experts;
-  // E2M1 weights by column tile and K-step (one contiguous block per step of a tile, the
-  // GEMMs' tile widths); the E8M0 scales stay row-major
+  // E2M1 weights (64 bytes a step) and their E8M0 scales (4 bytes a step) by column tile and
+  // K-step: one contiguous block per step of a tile, the GEMMs' tile widths
   const int tn_gu = e4m3_tile_n(kEpiSwiglu, 2 * f), tn_dn = e4m3_tile_n(kEpiStore, d);
   hipError_t e = launch_pack_rows_gate_up(lw->w_gate, lw->w_up, packed[MOE_PACK_GATE_UP], f, 1,
-                                          E, d / 2, tn_gu, s);
+                                          E, d / 2, tn_gu, 64, s);
   if (e == hipSuccess)
     e = launch_pack_rows_gate_up(lw->w_gate_scales, lw->w_up_scales,
-                                 packed[MOE_PACK_GATE_UP_SCALES], f, 1, E, d / 32, 0, s);
+                                 packed[MOE_PACK_GATE_UP_SCALES], f, 1, E, d / 32, tn_gu, 4, s);
   if (e == hipSuccess)
-    e = launch_pack_rows_concat(lw->w_down, packed[MOE_PACK_DOWN], d, 1, E, f / 2, tn_dn, s);
+    e = launch_pack_rows_concat(lw->w_down, packed[MOE_PACK_DOWN], d, 1, E, f / 2, tn_dn, 64, s);
   if (e == hipSuccess)
     e = launch_pack_rows_concat(lw->w_down_scales, packed[MOE_PACK_DOWN_SCALES], d, 1, E,
-                                f / 32, 0, s);
+                                f / 32, tn_dn, 4, s);
   if (e != hipSuccess || c->num_shared == 0) return e;
   const int S = c->num_shared, fs = c->d_ff_shared;
   const int tn_sgu = e4m3_tile_n(kEpiSwiglu, 2 * S * fs);
   e = launch_pack_rows_gate_up(lw->ws_gate, lw->ws_up, packed[MOE_PACK_SHARED_GATE_UP], fs, S, 1,
-                               d / 2, tn_sgu, s);
+                               d / 2, tn_sgu, 64, s);
   if (e == hipSuccess)
     e = launch_pack_rows_gate_up(lw->ws_gate_scales, lw->ws_up_scales,
-                                 packed[MOE_PACK_SHARED_GATE_UP_SCALES], fs, S, 1, d / 32, 0, s);
+                                 packed[MOE_PACK_SHARED_GATE_UP_SCALES], fs, S, 1, d / 32, tn_sgu, 4,
+                                 s);
   if (e == hipSuccess)
     e = launch_pack_rows_concat(lw->ws_down, packed[MOE_PACK_SHARED_DOWN], d, S, 1, fs / 2,
-                                tn_dn, s);
+                                tn_dn, 64, s);
   if (e == hipSuccess)
     e = launch_pack_rows_concat(lw->ws_down_scales, packed[MOE_PACK_SHARED_DOWN_SCALES], d, S, 1,
-                                fs / 32, 0, s);
+                                fs / 32, tn_dn, 4, s);
   return e;
 }
 

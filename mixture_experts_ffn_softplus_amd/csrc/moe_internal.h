@@ -124,14 +124,15 @@ hipError_t launch_pack_down(const void* down, void* dst, int N, int C, int sub, 
 // MXFP4 (N-major rows of `row_bytes`, a multiple of 4): gate/up rows [C] per source expert
 // interleaved 16 at a time into [2F, row] per group (F = sub * C, `sub` sources a group), and
 // down rows [N] per source concatenated along K into [N, sub * row] per group.  tile_rows = 0
-// keeps each group's rows in row-major order (the E8M0 scales); tile_rows = BN (rows a
-// multiple of BN, packed rows a multiple of 64 bytes) stores them by column tile and K-step:
-// the 64-byte piece s of row n lands at ((n / BN) * (row / 64) + s) * BN * 64 + (n % BN) * 64,
-// so each step of a tile is one contiguous BN * 64-byte block (the E2M1 weights).
+// keeps each group's rows in row-major order; tile_rows = BN (rows a multiple of BN, packed
+// rows a multiple of step_bytes = b) stores them by column tile and K-step: piece s of row n
+// lands at ((n / BN) * (row / b) + s) * BN * b + (n % BN) * b, so each step of a tile is one
+// contiguous BN * b-byte block (E2M1 weights: b = 64; their E8M0 scales: b = 4).
 hipError_t launch_pack_rows_gate_up(const void* gate, const void* up, void* dst, int C, int sub,
-                                    int groups, int row_bytes, int tile_rows, hipStream_t s);
+                                    int groups, int row_bytes, int tile_rows, int step_bytes,
+                                    hipStream_t s);
 hipError_t launch_pack_rows_concat(const void* src, void* dst, int N, int sub, int groups,
-                                   int row_bytes, int tile_rows, hipStream_t s);
+                                   int row_bytes, int tile_rows, int step_bytes, hipStream_t s);
 // Router [d, E] -> [E_pad, d] (rows >= E zero).  hilo: fp32 source split into bf16 hi and
 // lo = bf16(w - hi), one [E_pad, 2d] bf16 matrix; otherwise the element type is kept.
 hipError_t launch_pack_router(const void* wr, int esize, int hilo, void* dst, int d, int E,

@@ -108,11 +108,13 @@ __global__ void pack_scales_down_kernel(const float* __restrict__ ds, float* __r
 }
 
 // Row-wise packing of N-major (MXFP4) operands, one dword per thread; rows are R bytes.
-// Dword w of packed row n within a group of `rows` rows of W dwords: row-major (tile_rows 0),
-// or by column tile and 64-byte K-step (16 dwords) so that one step of a tile is contiguous.
-__device__ __forceinline__ int64_t packed_dword(int64_t n, int64_t w, int64_t W, int tile_rows) {
+// Dword w of packed row n within a group of rows of W dwords: row-major (tile_rows 0), or by
+// column tile and K-step of P dwords (16 for the E2M1 weights, 1 for the E8M0 scales) so that
+// one step of a tile is contiguous.
+__device__ __forceinline__ int64_t packed_dword(int64_t n, int64_t w, int64_t W, int tile_rows,
+                                                int P) {
   if (tile_rows == 0) return n * W + w;
-  return ((n / tile_rows) * (W / 16) + w / 16) * (tile_rows * 16) + (n % tile_rows) * 16 + w % 16;
+  return ((n / tile_rows) * (W / P) + w / P) * (tile_rows * P) + (n % tile_rows) * P + w % P;
 }
 
 // gate/up: packed row p of a group (2F rows, F = sub * C) is gate row n = 16 (p / 32) + p % 16
@@ -120,7 +122,7 @@ __device__ __forceinline__ int64_t packed_dword(int64_t n, int64_t w, int64_t W,
 // n / C.
 __global__ __launch_bounds__(256) void pack_rows_gate_up_kernel(
     const uint32_t* __restrict__ gate, const uint32_t* __restrict__ up,
-    uint32_t* __restrict__ dst, int C, int sub, int groups, int R4, int tile_rows) {
+    uint32_t* __restrict__ dst, int C, int sub, int groups, int R4, int tile_rows, int P) {
   const int64_t F = static_cast<int64_t>(sub) * C;
   const int64_t total = static_cast<int64_t>(groups) * 2 * F * R4;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(256) void pack_rows_gate_up_kernel(
   const int64_t g = row / (2 * F), p = row % (2 * F);
   const int64_t n = 16 * (p / 32) + p % 16;
   const uint32_t* src = (p % 32) < 16 ? gate : up;
-  dst[g * 2 * F * R4 + packed_dword(p, w, R4, tile_rows)] =
+  dst[g * 2 * F * R4 + packed_dword(p, w, R4, tile_rows, P)] =
       src[((g * sub + n / C) * C + n % C) * R4 + w];
 }
 
@@ -138,7 +140,7 @@ __global__ __launch_bounds__(256) void pack_rows_gate_up_kernel(
 __global__ __launch_bounds__(256) void pack_rows_concat_kernel(const uint32_t* __restrict__ src,
                                                                uint32_t* __restrict__ dst, int N,
                                                                int sub, int groups, int R4,
-                                                               int tile_rows) {
+                                                               int tile_rows, int P) {
   const int64_t total = static_cast<int64_t>(groups) * N * sub * R4;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= total) return;
@@ -146,30 +148,34 @@ __global__ __launch_bounds__(256) void pack_rows_concat_kernel(const uint32_t* _
   const int64_t sidx = rest % sub, rest2 = rest / sub;
   const int64_t n = rest2 % N, g = rest2 / N;
   const int64_t W = static_cast<int64_t>(sub) * R4;
-  dst[g * N * W + packed_dword(n, sidx * R4 + w, W, tile_rows)] =
+  dst[g * N * W + packed_dword(n, sidx * R4 + w, W, tile_rows, P)] =
       src[((g * sub + sidx) * N + n) * R4 + w];
 }
 
 hipError_t launch_pack_rows_gate_up(const void* gate, const void* up, void* dst, int C, int sub,
-                                    int groups, int row_bytes, int tile_rows, hipStream_t s) {
-  if (row_bytes % 4) return hipErrorInvalidValue;
-  if (tile_rows > 0 && ((2 * sub * C) % tile_rows || row_bytes % 64)) return hipErrorInvalidValue;
+                                    int groups, int row_bytes, int tile_rows, int step_bytes,
+                                    hipStream_t s) {
+  if (row_bytes % 4 || step_bytes < 4 || step_bytes % 4) return hipErrorInvalidValue;
+  if (tile_rows > 0 && ((2 * sub * C) % tile_rows || row_bytes % step_bytes))
+    return hipErrorInvalidValue;
   const int64_t n = static_cast<int64_t>(groups) * 2 * sub * C * (row_bytes / 4);
   hipLaunchKernelGGL(pack_rows_gate_up_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
                      dim3(256), 0, s, static_cast<const uint32_t*>(gate),
                      static_cast<const uint32_t*>(up), static_cast<uint32_t*>(dst), C, sub,
-                     groups, row_bytes / 4, tile_rows);
+                     groups, row_bytes / 4, tile_rows, step_bytes / 4);
   return hipGetLastError();
 }
 
 hipError_t launch_pack_rows_concat(const void* src, void* dst, int N, int sub, int groups,
-                                   int row_bytes, int tile_rows, hipStream_t s) {
-  if (row_bytes % 4) return hipErrorInvalidValue;
-  if (tile_rows > 0 && (N % tile_rows || (sub * row_bytes) % 64)) return hipErrorInvalidValue;
+                                   int row_bytes, int tile_rows, int step_bytes, hipStream_t s) {
+  if (row_bytes % 4 || step_bytes < 4 || step_bytes % 4) return hipErrorInvalidValue;
+  if (tile_rows > 0 && (N % tile_rows || (sub * row_bytes) % step_bytes))
+    return hipErrorInvalidValue;
   const int64_t n = static_cast<int64_t>(groups) * N * sub * (row_bytes / 4);
   hipLaunchKernelGGL(pack_rows_concat_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
                      dim3(256), 0, s, static_cast<const uint32_t*>(src),
-                     static_cast<uint32_t*>(dst), N, sub, groups, row_bytes / 4, tile_rows);
+                     static_cast<uint32_t*>(dst), N, sub, groups, row_bytes / 4, tile_rows,
+                     step_bytes / 4);
   return hipGetLastError();
 }
 
