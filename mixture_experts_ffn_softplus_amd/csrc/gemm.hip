@@ -1,7 +1,8 @@
 // gemm.hip -- grouped expert GEMMs on gfx950 MFMA with fused epilogues.
 //
 // Computes, for every tile of rows of every group (expert), OUT = A_rows x B_group^T with B
-// stored [N, K] K-contiguous (the packed weight layout), followed by one of:
+// stored [N, K] K-contiguous (the packed weight layout; E2M1 weights and their E8M0 scales by
+// column tile and K-step, one contiguous block per step of a tile), followed by one of:
 //   kEpiSwiglu  -- h = SiLU(gate) * up: B interleaves gate and up columns in blocks of 16
 //                  packed rows, so each wave's accumulators hold matching gate/up columns and
 //                  h is formed in registers (SwiGLU experts, routed-experts row of
@@ -90,7 +91,7 @@ struct GemmShape {
   // LDS ring: step s multiplies out of slot s % NSLOT while the next NSLOT - 1 steps land in
   // the others.  Three slots; E4M3 tiles of at most 32 rows (decode shapes, which do little
   // but stream weights) take as many as 160 KiB of LDS hold, up to 8, for more bytes in flight
-  // per CU (measured on MI355X: three slots kept MXFP4 decode at half the HBM rate).
+  // per CU (measured on MI355X: three slots instead make the MXFP4 decode gate/up ~4% slower).
   static constexpr int DEEP = (160 * 1024 - DUMMY - AMAX) / SLOT;
   static constexpr int NSLOT = (kFp8 && BM <= 32) ? (DEEP > 8 ? 8 : DEEP < 3 ? 3 : DEEP) : 3;
   static constexpr int MAIN = NSLOT * SLOT + DUMMY;
