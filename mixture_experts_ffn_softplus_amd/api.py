@@ -154,12 +154,21 @@ def _cfg(cfg):
     return ctypes.byref(cfg if isinstance(cfg, moe_config_t) else config_struct(cfg))
 
 
-def _need(t, cfg, rows, dtype_of, where, what):
-    """A tensor the library writes must be a contiguous [rows, d] buffer of the dtype the
-    config implies: the C entry points take bare pointers and cannot check it."""
+def _tokens(c: MoEConfig) -> int:
+    return c.num_tokens
+
+
+def _assignments(c: MoEConfig) -> int:
+    return c.assignments
+
+
+def _need(t, cfg, rows_of, dtype_of, where, what):
+    """A tensor the library writes must be a contiguous [rows_of(cfg), d] buffer of the dtype
+    the config implies: the C entry points take bare pointers and cannot check it.  (Checked
+    for a MoEConfig and a torch tensor; raw structs and pointers pass through.)"""
     if not isinstance(t, torch.Tensor) or not isinstance(cfg, MoEConfig):
         return
-    n, dt = rows * cfg.d_model, dtype_of(cfg)
+    n, dt = rows_of(cfg) * cfg.d_model, dtype_of(cfg)
     if t.dtype != dt or t.numel() < n or not t.is_contiguous():
         raise ValueError(f"{where}: {what} must be a contiguous {dt} tensor of at least {n} "
                          f"elements, got {t.dtype} with {t.numel()}")
@@ -218,8 +227,7 @@ def moe_permute(cfg, topk_ids, expert_offsets, perm_token, inv_perm, ws, stream=
 
 def moe_expert_ffn(cfg, x_or_xq, xq_scales, expert_offsets, perm_token, weights, y_perm, ws,
                    stream=None):
-    _need(y_perm, cfg, cfg.assignments if isinstance(cfg, MoEConfig) else 0, y_dtype,
-          "moe_expert_ffn", "y_perm")
+    _need(y_perm, cfg, _assignments, y_dtype, "moe_expert_ffn", "y_perm")
     _check(lib().moe_expert_ffn(_cfg(cfg), _p(x_or_xq), _p(xq_scales), _p(expert_offsets),
                                 _p(perm_token), ctypes.byref(weights), _p(y_perm), _p(ws),
                                 ws.numel() * ws.element_size(), _stream(stream)),
@@ -228,19 +236,16 @@ def moe_expert_ffn(cfg, x_or_xq, xq_scales, expert_offsets, perm_token, weights,
 
 def moe_combine(cfg, x_or_xq, xq_scales, y_perm, inv_perm, topk_w, weights, out, ws,
                 stream=None):
-    _need(out, cfg, cfg.num_tokens if isinstance(cfg, MoEConfig) else 0, out_dtype,
-          "moe_combine", "out")
+    _need(out, cfg, _tokens, out_dtype, "moe_combine", "out")
     _check(lib().moe_combine(_cfg(cfg), _p(x_or_xq), _p(xq_scales), _p(y_perm), _p(inv_perm),
                              _p(topk_w), ctypes.byref(weights), _p(out), _p(ws),
                              ws.numel() * ws.element_size(), _stream(stream)), "moe_combine")
 
 
 def moe_forward(cfg, x, weights, out, ws, dbg: dict = None, stream=None):
-    _need(out, cfg, cfg.num_tokens if isinstance(cfg, MoEConfig) else 0, out_dtype,
-          "moe_forward", "out")
+    _need(out, cfg, _tokens, out_dtype, "moe_forward", "out")
     if dbg:
-        _need(dbg.get("y_perm"), cfg, cfg.assignments if isinstance(cfg, MoEConfig) else 0,
-              y_dtype, "moe_forward", "dbg['y_perm']")
+        _need(dbg.get("y_perm"), cfg, _assignments, y_dtype, "moe_forward", "dbg['y_perm']")
     d = None
     if dbg:
         d = moe_debug_t(*[_p(dbg.get(n)) for n, _ in moe_debug_t._fields_])
