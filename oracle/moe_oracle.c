@@ -169,7 +169,8 @@ static double orc_elem(int dtype, const void* w, const void* scales, int rows, i
 /* Router                                                                     */
 /* ------------------------------------------------------------------------- */
 
-/* "A linear router scores the experts" (router row, Qwen3.5 cell):
+/* Router logits (router row, Qwen3.5 cell: one linear map of the token gives
+ * a logit for every expert):
  * l[t,e] = sum_i x[t,i] * W_r[i,e] (+ z_e, a per-expert logit bias used to
  * skew load in the synthetic workloads).  W_r is [d, E]. */
 void orc_router_logits(int T, int d, int E, const double* x, int wr_dtype, const void* wr,
@@ -444,7 +445,8 @@ static int orc_swiglu(const orc_ffn_cfg* c, int f, const orc_expert_set* s, int 
 /* The block output for n tokens:
  * out[t] = G(t) * sum_s SharedSwiGLU_s(x~[t]) + sum_j w[t,j] * SwiGLU_{ids[t,j]}(x~[t]),
  * with x~ = x, or for FP8 the dequantised block-scaled x.  Shared experts are
- * always active (blueprint shared-expert box "1-2, always active"); ungated,
+ * always active (blueprint shared-expert box: one or two, used by every
+ * token); ungated,
  * G = 1 (DeepSeek-style), or with a gate vector w_g the per-token sigmoid gate
  * G(t) = sigma(x~[t] . w_g) of the Qwen3.5 cell of the shared-expert row of
  * "Qwen3.5-397B-A17B vs Gemma 4 31B" (it scales the shared output before the

@@ -125,3 +125,25 @@ def test_bias_steps_balance_a_skewed_router():
 def test_bias_rejects_bad_ids():
     with pytest.raises(ValueError):
         oracle.bias_update(np.zeros(4, np.float32), np.array([[0, 4]]), 4)
+
+
+@pytest.mark.parametrize("kind", [oracle.SIGMOID, oracle.SQRT_SOFTPLUS])
+def test_hashed_sigma_family_without_renormalising(kind):
+    # the table's experts in its order, each weighted by gamma times its own unbiased score
+    l = np.array([[0.0, 1.0, -1.0], [0.5, -2.0, 3.0]])
+    table = np.array([[2, 0], [1, 2]], np.int32)
+    ids, w = oracle.route_hashed(l, [0, 1], table, kind, False, 2.5)
+    assert ids.tolist() == [[2, 0], [1, 2]]
+    if kind == oracle.SIGMOID:
+        sc = lambda v: 1.0 / (1.0 + math.exp(-v))  # noqa: E731
+        assert w[0].tolist() == pytest.approx([2.5 * 0.2689414213699951, 1.25], abs=1e-15)
+    else:
+        sc = lambda v: math.sqrt(math.log1p(math.exp(v)))  # noqa: E731
+        assert w[0].tolist() == pytest.approx([2.5 * 0.5596978537731075,
+                                               2.5 * 0.8325546111576977], abs=1e-15)
+    for t in range(2):
+        want = [2.5 * sc(l[t, e]) for e in table[t]]
+        assert np.allclose(w[t], want, rtol=1e-15, atol=0)
+    # and the renormalised variant is the same vector over its sum, times gamma
+    _, wr = oracle.route_hashed(l, [0, 1], table, kind, True, 2.5)
+    assert np.allclose(wr, 2.5 * w / w.sum(axis=1, keepdims=True), rtol=1e-14, atol=0)

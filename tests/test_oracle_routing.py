@@ -200,3 +200,60 @@ def test_permute_skewed_and_bad_id():
     assert inv.tolist() == [4, 0, 5, 2, 6, 3, 1, 7]
     with pytest.raises(ValueError):
         oracle.permute(np.array([[5]], np.int32), 5)
+
+
+# ---------------------------------------------------------------- weights without renormalising
+# Router row of "Qwen3.5-397B-A17B vs DeepSeek-V4-Pro", DeepSeek-V4-Pro cell: the picked scores
+# are normalised and then scaled.  With the normalisation switched off (renormalize = 0) each
+# weight is gamma times the expert's own unbiased score: nothing is divided by the selected sum,
+# gamma still applies, and the selection bias still only chooses.
+
+SIG = [0.5, 0.7310585786300049, 0.2689414213699951]          # sigma(0), sigma(1), sigma(-1)
+SQS = [0.8325546111576977, 1.145976303209723, 0.5596978537731075]  # sqrt(softplus(.)) of the same
+
+
+def test_sigmoid_scores_without_renormalising_hand_example():
+    l = np.array([[0.0, 1.0, -1.0]])
+    ids, w, s = oracle.route(l, 3, oracle.SIGMOID, False, 2.5)
+    assert ids.tolist() == [[1, 0, 2]]
+    want = 2.5 * np.array([SIG[1], SIG[0], SIG[2]])
+    assert np.allclose(w[0], want, rtol=0, atol=1e-15)
+    assert np.allclose(w[0], [1.8276464465750123, 1.25, 0.6723535534249878], rtol=0, atol=1e-14)
+    # not divided by the selected sum (that would give 2.5 in total) and gamma is applied
+    assert abs(w.sum() - 2.5 * 1.5) < 1e-14
+    assert np.allclose(s[0], [SIG[1], SIG[0], SIG[2]], rtol=0, atol=1e-15)
+
+
+def test_sqrt_softplus_without_renormalising_hand_example():
+    l = np.array([[0.0, 1.0, -1.0]])
+    assert SQS[1] == pytest.approx(math.sqrt(math.log(1 + math.e)), abs=1e-15)
+    assert SQS[2] == pytest.approx(math.sqrt(math.log(1 + 1 / math.e)), abs=1e-15)
+    ids, w, _ = oracle.route(l, 2, oracle.SQRT_SOFTPLUS, False, 2.5)
+    assert ids.tolist() == [[1, 0]]
+    assert np.allclose(w[0], [2.5 * SQS[1], 2.5 * SQS[0]], rtol=0, atol=1e-15)
+    # the bias flips the choice order; each weight stays gamma times its own score
+    b = np.array([0.4, 0.0, 0.0], np.float32)
+    ids, w, _ = oracle.route(l, 2, oracle.SQRT_SOFTPLUS, False, 2.5, b)
+    assert ids.tolist() == [[0, 1]]
+    assert np.allclose(w[0], [2.5 * SQS[0], 2.5 * SQS[1]], rtol=0, atol=1e-15)
+    # k = 1: the weight is the score times gamma, not gamma
+    ids, w, _ = oracle.route(l, 1, oracle.SQRT_SOFTPLUS, False, 1.0)
+    assert ids.tolist() == [[1]] and w[0, 0] == pytest.approx(SQS[1], abs=1e-15)
+
+
+@pytest.mark.parametrize("kind", [oracle.SIGMOID, oracle.SQRT_SOFTPLUS])
+def test_sigma_family_without_renormalising_is_gamma_times_score(kind):
+    # random logits and biases: w[t, j] = gamma * score(l[t, ids[t, j]]) for every slot, and the
+    # renormalised weights are exactly these divided by their row sum times gamma
+    rng = np.random.default_rng(21)
+    T, E, k, gamma = 50, 33, 7, 1.75
+    l = rng.standard_normal((T, E)) * 2
+    b = rng.uniform(-0.1, 0.1, E).astype(np.float32)
+    ids, w, _ = oracle.route(l, k, kind, False, gamma, b)
+    ids_r, w_r, _ = oracle.route(l, k, kind, True, gamma, b)
+    assert np.array_equal(ids, ids_r)   # renormalising never changes the choice
+    f = (lambda v: 1 / (1 + np.exp(-v))) if kind == oracle.SIGMOID else \
+        (lambda v: np.sqrt(np.logaddexp(0.0, v)))
+    want = gamma * f(np.take_along_axis(l, ids, axis=1))
+    assert np.allclose(w, want, rtol=1e-14, atol=0)
+    assert np.allclose(w_r, gamma * w / w.sum(axis=1, keepdims=True), rtol=1e-14, atol=0)
