@@ -75,24 +75,36 @@ def algorithmic(cfg, touched):
     return step_bytes, step_flops, gate_up_bytes, gate_up_flops
 
 
-def cpu_baseline(cfg, inp, n_tokens, seed=0):
-    """The oracle, as it stands, on a bounded token sample of the same workload."""
+def _np_storage(t):
+    import numpy as np
+    import torch
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
+    return t.numpy()
+
+
+def _exact64(t):
+    import torch
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+def cpu_baseline(cfg, inp, out, logits_gpu, n_tokens, seed=0):
+    """The oracle, as it stands, on a bounded token sample of the same workload, timed on the
+    host cores; the same run is a parity check of the timed forward's output rows.
+
+    Timed: the oracle's own fp64 router logits for the sample, top-k and weights, the
+    permutation and the routed + shared SwiGLU experts.  The routing is taken on the GPU's fp32
+    logits (as in the parity tests: near-ties at the top-k boundary are decided by fp32
+    rounding, so both sides route on the same numbers); the oracle's own logits are compared
+    with the GPU's and the tokens its own routing would choose differently are counted."""
     import numpy as np
     import torch
 
     import oracle
     from mixture_experts_ffn_softplus_amd import synth
-
-    def np_storage(t):
-        t = t.detach().contiguous().cpu()
-        if t.dtype == torch.bfloat16:
-            return t.view(torch.int16).numpy().view(np.uint16)
-        if t.dtype == torch.float8_e4m3fn:
-            return t.view(torch.uint8).numpy()
-        return t.numpy()
-
-    def exact64(t):
-        return t.detach().cpu().to(torch.float64).numpy()
 
     def expert_set(n, parts):
         col = lambda key: [None if p is None else p.get(key) for p in parts]  # noqa: E731
@@ -103,25 +115,27 @@ def cpu_baseline(cfg, inp, n_tokens, seed=0):
 
     rng = np.random.default_rng(seed)
     tok = np.sort(rng.choice(cfg.num_tokens, min(n_tokens, cfg.num_tokens), replace=False))
-    x = exact64(inp["x"][torch.as_tensor(tok, device=inp["x"].device)])
-    wr = np_storage(inp["w_router"])
+    tok_dev = torch.as_tensor(tok, device=inp["x"].device)
+    x = _exact64(inp["x"][tok_dev])
+    wr = _np_storage(inp["w_router"])
     z = None if inp["logit_bias"] is None else inp["logit_bias"].cpu().numpy()
     sb = None if inp["select_bias"] is None else inp["select_bias"].cpu().numpy()
+    l_gpu = logits_gpu[tok_dev].double().cpu().numpy()
     quant = cfg.expert_dtype in (2, 3)   # E4M3 activations
 
     def host(d):
-        return {k: (v.cpu().numpy() if k.endswith("scales") else np_storage(v))
+        return {k: (v.cpu().numpy() if k.endswith("scales") else _np_storage(v))
                 for k, v in d.items()}
 
     shared = None
     if cfg.num_shared:
         sh = [host(synth.shared_expert(cfg, s, inp["x"].device)) for s in range(cfg.num_shared)]
         shared = expert_set(cfg.num_shared, sh)
-    # the oracle's own routing for the sample, then every expert it needs fetched once; only
-    # the oracle's arithmetic is timed
+    # only the oracle's arithmetic is timed, not the fetching of the experts it needs
+    route_args = (cfg.top_k, cfg.score, bool(cfg.renormalize), cfg.routed_scale, sb)
     t0 = time.perf_counter()
-    l = oracle.router_logits(x, wr, z)
-    ids, w, _ = oracle.route(l, cfg.top_k, cfg.score, bool(cfg.renormalize), cfg.routed_scale, sb)
+    l_own = oracle.router_logits(x, wr, z)
+    ids, w, _ = oracle.route(l_gpu, *route_args)
     oracle.permute(ids, cfg.num_experts)
     t_cpu = time.perf_counter() - t0
     used = sorted(set(ids.ravel().tolist()))
@@ -129,17 +143,31 @@ def cpu_baseline(cfg, inp, n_tokens, seed=0):
     routed = expert_set(cfg.num_experts, [parts.get(e) for e in range(cfg.num_experts)])
     log(f"cpu_baseline: {len(tok)} tokens use {len(used)} experts; running the oracle")
     t0 = time.perf_counter()
-    gate = None if inp.get("shared_gate") is None else exact64(inp["shared_gate"])
-    oracle.moe_tokens(x, ids, w, routed, shared, cfg.d_model, cfg.d_ff, cfg.d_ff_shared,
-                      quant=quant, shared_gate=gate)
+    gate = None if inp.get("shared_gate") is None else _exact64(inp["shared_gate"])
+    ref = oracle.moe_tokens(x, ids, w, routed, shared, cfg.d_model, cfg.d_ff, cfg.d_ff_shared,
+                            quant=quant, shared_gate=gate)
     t_cpu += time.perf_counter() - t0
     log(f"cpu_baseline: {t_cpu:.1f} s of oracle time")
-    return {"value": len(tok) / t_cpu, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": (f"{len(tok)} seeded tokens of {cfg.name}: fp64 router logits, top-k, "
-                       f"permutation and routed+shared SwiGLU experts for those tokens; "
-                       f"{t_cpu:.1f} s of CPU time"),
-            "seconds": t_cpu}
+    got = out[tok_dev].double().cpu().numpy()
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    ids_own, _, _ = oracle.route(l_own, *route_args)
+    tol = {0: 1e-5, 1: 2e-2, 2: 6e-2, 3: 6e-2}[cfg.expert_dtype]
+    parity = {"max_abs_over_rms": float(np.max(np.abs(got - ref)) / rms), "tolerance": tol,
+              "tokens": int(len(tok)),
+              "logit_max_abs_over_rms": float(np.max(np.abs(l_gpu - l_own)) /
+                                              np.sqrt(np.mean(l_own * l_own))),
+              "own_route_diff_tokens": int(np.sum(np.any(ids_own != ids, axis=1))),
+              "what": ("the timed forward's output rows against the fp64 oracle on the "
+                       "cpu_baseline sample, routed on the GPU's fp32 logits")}
+    log(f"parity: {parity['max_abs_over_rms']:.4g} max-abs/RMS over {len(tok)} tokens "
+        f"(bar {tol})")
+    cpu = {"value": len(tok) / t_cpu, "unit": "tokens/s", "cores": oracle.num_threads(),
+           "kind": "oracle",
+           "sample": (f"{len(tok)} seeded tokens of {cfg.name}: fp64 router logits, top-k, "
+                      f"permutation and routed+shared SwiGLU experts for those tokens; "
+                      f"{t_cpu:.1f} s of CPU time"),
+           "seconds": t_cpu}
+    return cpu, parity
 
 
 def _timed(fn, steps, warmup, marks=0):
@@ -222,45 +250,88 @@ def time_bias_update(cfg, x, w, out, ws, steps, warmup):
             "bytes": (E + 1) * 4 + 2 * E * 4}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="softmax_bf16")
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--hash-routing", action="store_true",
-                    help="also time the step with experts chosen by a fixed token-id table "
-                         "(moe_route_hashed, then permute / experts / combine)")
-    ap.add_argument("--bias-update", action="store_true",
-                    help="also time the bias-balancing step (moe_update_bias)")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="only run a plain device copy of MIB MiB (3 times): the reference for "
-                         "scaling HBM byte counters")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py: the MoE block runs on one GPU; --gpus {args.gpus} is not supported "
-              f"(no expert-parallel sharding is implemented)", file=sys.stderr)
-        sys.exit(2)
+def gpu_info(dev):
+    """Name, architecture, compute units and the peak shader clock the runtime reports."""
+    import torch
+    p = torch.cuda.get_device_properties(dev)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count}
+    try:
+        rt = ctypes.CDLL("libamdhip64.so.7")
+        v = ctypes.c_int()
+        # hipDeviceAttributeClockRate (kHz) = 5 in hipDeviceAttribute_t
+        if rt.hipDeviceGetAttribute(ctypes.byref(v), 5, dev.index or 0) == 0:
+            info["peak_sclk_mhz"] = v.value // 1000
+    except OSError:
+        pass
+    return info
 
+
+def cpu_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "logical_cpus": os.cpu_count(),
+            "usable_cpus": len(os.sched_getaffinity(0))}
+
+
+class SclkSampler:
+    """Samples the GPU's current shader clock (rocm-smi) from a thread while a loop of forwards
+    runs; null where rocm-smi is unavailable."""
+
+    def __init__(self):
+        import threading
+        self.samples, self.stop, self.err = [], threading.Event(), None
+        self.t = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        import re
+        import subprocess
+        while not self.stop.is_set():
+            try:
+                r = subprocess.run(["rocm-smi", "--showgpuclocks", "--json"], capture_output=True,
+                                   text=True, timeout=5)
+                for card in json.loads(r.stdout).values():
+                    for key, val in card.items():
+                        if "sclk" in key.lower() and "speed" in key.lower():
+                            m = re.search(r"(\d+)\s*mhz", str(val).lower())
+                            if m:
+                                self.samples.append(int(m.group(1)))
+            except Exception as e:  # noqa: BLE001 -- a missing tool only loses the figure
+                self.err = repr(e)
+                return
+            self.stop.wait(0.2)
+
+    def __enter__(self):
+        self.t.start()
+        return self
+
+    def __exit__(self, *a):
+        self.stop.set()
+        self.t.join(timeout=10)
+
+    def result(self):
+        busy = sorted(self.samples)
+        if not busy:
+            return None
+        return {"median_mhz": busy[len(busy) // 2], "max_mhz": busy[-1], "samples": len(busy),
+                "how": "rocm-smi --showgpuclocks every 0.2 s during untimed forwards"}
+
+
+def run_workload(cfg, steps, warmup, dev, keep=False):
+    """Pack one workload, run `warmup` untimed and `steps` timed forwards with a HIP event at
+    every stage boundary, and return its record (and, with keep, the objects a parity check
+    needs)."""
     import torch
 
-    from mixture_experts_ffn_softplus_amd import PRESETS, api, synth
+    from mixture_experts_ffn_softplus_amd import api, profiling, synth
 
-    if args.copy_calibration:
-        n = args.copy_calibration << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"copied {n} bytes 3 times")
-        return
-
-    cfg = PRESETS[args.workload]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     log(f"workload {cfg.describe()}")
     inp = synth.inputs(cfg, dev)
     pw = api.pack(cfg, inp["w_router"], inp["routed"], inp["shared"], inp["logit_bias"],
@@ -275,50 +346,47 @@ def main():
     x = inp["x"]
     log(f"packed weights {pw.nbytes() / 1e9:.2f} GB, workspace {ws.numel() / 1e9:.2f} GB")
 
-    # routing statistics of this input (untimed)
+    # routing statistics of this input, and its logits for the parity sample (untimed)
     off = torch.empty(cfg.num_experts + 1, dtype=torch.int32, device=dev)
-    api.moe_forward(cfg, x, w, out, ws, {"expert_offsets": off})
+    logits = torch.empty(T, cfg.num_experts, dtype=torch.float32, device=dev) if keep else None
+    api.moe_forward(cfg, x, w, out, ws, {"expert_offsets": off, "logits": logits})
     torch.cuda.synchronize()
     counts = (off[1:] - off[:-1]).cpu()
     touched = int((counts > 0).sum())
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         api.moe_forward(cfg, x, w, out, ws)
     torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps)")
 
     # The timed region: the library records a HIP event on the stream at each stage boundary of
     # every step (a marker each, no synchronisation), so the per-kernel durations below come
     # from these same steps.
     hip = HipEvents()
     n_ev = api.NUM_STAGE_EVENTS
-    ev = [hip.create(n_ev) for _ in range(args.steps)]
+    ev = [hip.create(n_ev) for _ in range(steps)]
     stream = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         api.moe_forward(cfg, x, w, out, ws, {"stage_events": ctypes.addressof(ev[i])})
     end.record(stream)
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    log(f"timed {args.steps} steps: {ms:.4f} ms/step")
+    ms = start.elapsed_time(end) / steps
+    log(f"{cfg.name}: timed {steps} steps: {ms:.4f} ms/step")
     stage_ms = {}
     for s, name in enumerate(api.STAGES):
-        stage_ms[name] = sum(hip.elapsed_ms(ev[i][s], ev[i][s + 1])
-                             for i in range(args.steps)) / args.steps
+        stage_ms[name] = sum(hip.elapsed_ms(ev[i][s], ev[i][s + 1]) for i in range(steps)) / steps
     # each step from its first to its last stage boundary: median and minimum beside the mean
-    step_times = sorted(hip.elapsed_ms(ev[i][0], ev[i][n_ev - 1]) for i in range(args.steps))
-    step_median = statistics.median(step_times)
+    step_times = sorted(hip.elapsed_ms(ev[i][0], ev[i][n_ev - 1]) for i in range(steps))
     for e in ev:
         hip.destroy(e)
-    log("stage ms: " + ", ".join(f"{k}={v:.4f}" for k, v in stage_ms.items()))
+    log(f"{cfg.name} stage ms: " + ", ".join(f"{k}={v:.4f}" for k, v in stage_ms.items()))
 
     step_bytes, step_flops, gu_bytes, gu_flops = algorithmic(cfg, touched)
     gu_ms = stage_ms["gate_up"]
     # HBM bytes per launch measured by rocprofv3 counters (profiles/), if the kernel sources
     # are unchanged since; otherwise null
-    from mixture_experts_ffn_softplus_amd import profiling
     traffic = profiling.traffic_if_current(
         os.path.join(ROOT, "profiles", f"gate_up_gemm_{cfg.name}.txt"))
     # the binding roof of the dominant kernel: MFMA when its arithmetic intensity is above the
@@ -337,12 +405,86 @@ def main():
                 "kernel": "grouped_gemm_kernel (routed gate/up + SiLU*up)",
                 "kernel_ms": round(gu_ms, 5), "bytes_per_launch": gu_bytes,
                 "flops_per_launch": gu_flops}
+    t_hbm = step_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
+    t_mfma = step_flops / (mfma_peak * 1e12) * 1e3
     step = {"bytes": step_bytes, "flops": step_flops,
             "GB_s": round(step_bytes / (ms * 1e-3) / 1e9, 1),
-            "hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "hbm_frac": round(t_hbm / ms, 4),
             "TFLOP_s": round(step_flops / (ms * 1e-3) / 1e12, 2),
-            "mfma_frac": round(step_flops / (ms * 1e-3) / 1e12 / mfma_peak, 4),
+            "mfma_frac": round(t_mfma / ms, 4),
+            "binding_roof": "hbm" if t_hbm >= t_mfma else "mfma",
+            "roof_frac": round(max(t_hbm, t_mfma) / ms, 4),
             "touched_experts": touched, "max_rows_per_expert": int(counts.max())}
+    rec = {"ms_per_step": round(ms, 5), "tokens_per_s": round(T / (ms * 1e-3), 1),
+           "step_ms_median": round(statistics.median(step_times), 5),
+           "step_ms_min": round(step_times[0], 5), "dtype": DTYPE_NAME[cfg.expert_dtype],
+           "config": config_record(cfg), "roofline": roofline, "step_roofline": step,
+           "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()}}
+    ctx = None
+    if keep:
+        ctx = {"inp": inp, "out": out, "logits": logits, "w": w, "ws": ws, "pw": pw}
+    else:
+        del inp, pw, w, ws, out, x
+        torch.cuda.empty_cache()
+    return rec, ctx
+
+
+def config_record(cfg):
+    return {"workload": cfg.name, "tokens": cfg.num_tokens, "d_model": cfg.d_model,
+            "experts": cfg.num_experts, "top_k": cfg.top_k, "d_ff": cfg.d_ff,
+            "shared": cfg.num_shared, "d_ff_shared": cfg.d_ff_shared,
+            "router": ["softmax", "sigmoid", "sqrt_softplus"][cfg.score],
+            "output": "f32" if cfg.act_dtype == 0 or cfg.out_f32 else "bf16",
+            "parallelism": "single_gpu"}
+
+
+# the other graded shapes of the metric, timed in the same run after the headline workload
+OTHER_WORKLOADS = ("decode_bf16", "softplus_bf16", "fp8_block")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="softmax_bf16")
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", action="store_true",
+                    help="time the named workload alone (no other workloads, no clock samples)")
+    ap.add_argument("--hash-routing", action="store_true",
+                    help="also time the step with experts chosen by a fixed token-id table "
+                         "(moe_route_hashed, then permute / experts / combine)")
+    ap.add_argument("--bias-update", action="store_true",
+                    help="also time the bias-balancing step (moe_update_bias)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (3 times): the reference for "
+                         "scaling HBM byte counters")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: the MoE block runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(no expert-parallel sharding is implemented)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from mixture_experts_ffn_softplus_amd import PRESETS, api
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {n} bytes 3 times")
+        return
+
+    cfg = PRESETS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rec, ctx = run_workload(cfg, args.steps, args.warmup, dev, keep=True)
+    x, w, ws, out = ctx["inp"]["x"], ctx["w"], ctx["ws"], ctx["out"]
 
     extra = {}
     if args.hash_routing:
@@ -350,26 +492,44 @@ def main():
     if args.bias_update:
         extra["bias_update"] = time_bias_update(cfg, x, w, out, ws, args.steps, args.warmup)
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        inp["routed"] = None
-        cpu = cpu_baseline(cfg, inp, args.cpu_tokens)
+    sclk = None
+    if not args.only:
+        # the shader clock under this workload: sampled during about 2 s of untimed forwards
+        with SclkSampler() as smp:
+            t_end = time.perf_counter() + 2.0
+            while time.perf_counter() < t_end:
+                for _ in range(20):
+                    api.moe_forward(cfg, x, w, out, ws)
+                torch.cuda.synchronize()
+        sclk = smp.result() if smp.samples else {"error": smp.err}
 
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        # the output of the last forward is the timed forwards' output (same inputs)
+        api.moe_forward(cfg, x, w, out, ws)
+        torch.cuda.synchronize()
+        cpu, parity = cpu_baseline(cfg, ctx["inp"], out, ctx["logits"], args.cpu_tokens)
+    del ctx, x, w, ws, out
+    torch.cuda.empty_cache()
+
+    others = {}
+    if not args.only:
+        for name in OTHER_WORKLOADS:
+            if name != cfg.name:
+                others[name], _ = run_workload(PRESETS[name], args.steps, args.warmup, dev)
+
+    ms = rec["ms_per_step"]
     result = {
-        "metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-        "step_ms_median": round(step_median, 5), "step_ms_min": round(step_times[0], 5),
+        "metric": METRIC, "value": rec["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "step_ms_median": rec["step_ms_median"], "step_ms_min": rec["step_ms_min"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": DTYPE_NAME[cfg.expert_dtype], "data": "synthetic",
-        "config": {"workload": cfg.name, "tokens": T, "d_model": d,
-                   "experts": cfg.num_experts, "top_k": cfg.top_k, "d_ff": cfg.d_ff,
-                   "shared": cfg.num_shared, "d_ff_shared": cfg.d_ff_shared,
-                   "router": ["softmax", "sigmoid", "sqrt_softplus"][cfg.score],
-                   "output": "f32" if cfg.act_dtype == 0 or cfg.out_f32 else "bf16",
-                   "parallelism": "single_gpu"},
-        "roofline": roofline, "step_roofline": step, "stage_ms": {k: round(v, 5) for k, v in
-                                                                   stage_ms.items()},
-        "cpu_baseline": cpu,
+        "dtype": rec["dtype"], "data": "synthetic", "config": rec["config"],
+        "roofline": rec["roofline"], "step_roofline": rec["step_roofline"],
+        "stage_ms": rec["stage_ms"], "cpu_baseline": cpu, "parity": parity,
+        "workloads": {cfg.name: {k: rec[k] for k in ("ms_per_step", "tokens_per_s", "dtype")}
+                      | {"step_roofline": rec["step_roofline"]}} | others,
+        "gpu": gpu_info(dev) | {"sclk_under_load": sclk}, "host_cpu": cpu_info(),
     }
     result.update(extra)
     print(json.dumps(result), flush=True)

@@ -28,8 +28,16 @@
  *  - A call with num_tokens == 0 is valid and launches nothing.
  *  - Supported type combinations (act / experts / router):
  *      F32 / F32 / F32, BF16 / BF16 / BF16, BF16 / FP8_E4M3 / F32 or BF16.
- *    d_model, d_ff and d_ff_shared must be multiples of 128, num_experts <= 1024
- *    and top_k <= 64; otherwise MOE_ERR_UNSUPPORTED.
+ *    d_model, d_ff and d_ff_shared must be multiples of 128 and at most 2^24
+ *    (d_ff_shared only when num_shared > 0),
+ *    num_experts <= 1024, top_k <= 64 and T*k < 2^30; otherwise
+ *    MOE_ERR_UNSUPPORTED.  The kernels address each operand through a 32-bit
+ *    buffer resource, so a config is also UNSUPPORTED (and moe_workspace_size
+ *    returns 0) when any one operand reaches 4 GiB: x, the E4M3 activations or
+ *    their scales, h = [T*k, d_ff] or the shared experts' h = [T, S*d_ff_shared]
+ *    in the expert dtype (or their scales), the permutation, one routed
+ *    expert's packed gate/up or down weights (or their scales), the shared
+ *    experts' packed weights, or the packed router.
  *  - No function throws; all are safe to call from several host threads.
  */
 #ifndef MOE_MI355X_H
@@ -263,7 +271,10 @@ MOE_API moe_status_t moe_route_from_logits(const moe_config_t* cfg, const float*
                                    hipStream_t stream);
 
 /* Permutation of the T*k (token, slot) assignments into expert-contiguous
- * order, stable in token order: expert_offsets [E+1] (exclusive prefix sum of
+ * order (router row of "Qwen3.5-397B-A17B vs DeepSeek-V4-Pro": each token
+ * picks its top k of the routed experts, so each expert's SwiGLU, routed-
+ * experts row of "Qwen3.5-397B-A17B vs Gemma 4 31B", runs over the rows that
+ * picked it), stable in token order: expert_offsets [E+1] (exclusive prefix sum of
  * the per-expert counts, last = T*k), perm_token [T*k] (token of each row),
  * inv_perm [T*k] (row of assignment t*k + j).  Ids may come from any source
  * (router replay, hash routing); ids outside [0, E) are a precondition

@@ -27,6 +27,7 @@
 // measured on MI355X, the non-temporal hint gains nothing with E4M3 activations.)
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "moe_common.h"
@@ -726,13 +727,18 @@ void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
           for (int w2 = 0; w2 < S::WN; ++w2) m = fmaxf(m, amax[row * S::WN + w2]);
           const float sc = m > 0.0f ? m / 448.0f : 1.0f;
-          const float inv = __builtin_amdgcn_rcpf(sc);
           if (wn == 0 && kq == 0 && row < g.rows)
             a.out_scales[static_cast<int64_t>(g.m0 + row) * groups + grp] = sc;
+          // h / sc correctly rounded to fp32 without an fp32 division per value: the fp64
+          // product h * RN64(1/sc) lies within 2^-52 (relative) of h / sc, and a quotient of two
+          // fp32 numbers is never closer than about 2^-49 to an fp32 rounding midpoint, so
+          // rounding that product to fp32 gives the correctly rounded quotient.
+          const double rs = 1.0 / static_cast<double>(sc);
+          auto quo = [rs](float v) { return static_cast<float>(static_cast<double>(v) * rs); };
 #pragma unroll
           for (int p = 0; p < HP; ++p) {
             const float* v = hv[i][p];
-            const uint32_t codes = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+            const uint32_t codes = e4m3x4(quo(v[0]), quo(v[1]), quo(v[2]), quo(v[3]));
             buffer_store4(orsrc, static_cast<uint32_t>((srow + i * 16) * a.ldo + hc0 + p * 16 + scol),
                           xpose(codes));
           }
@@ -833,18 +839,24 @@ int gemm_bm(int dtype, int epi, int avg_rows) {
   return 128;
 }
 
-// Persistent grid: as many workgroups as fit on the device at once (a multiple of the XCD
-// count), never more than there are tiles (rounded up to that multiple).
+// Persistent grid: as many workgroups as fit on the current device at once (a multiple of the
+// XCD count), never more than there are tiles (rounded up to that multiple).  The resident
+// count is cached per kernel instantiation and device; concurrent first calls from several
+// host threads compute the same value and store it atomically.
+constexpr int kMaxDevices = 64;
 template <typename Kern>
 static int persistent_grid(Kern kernel, int threads, int64_t max_blocks) {
-  static int resident = 0;  // per kernel instantiation
+  static std::atomic<int> cache[kMaxDevices];  // 0: not known yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  int resident = dev < kMaxDevices ? cache[dev].load(std::memory_order_relaxed) : 0;
   if (resident == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
       return -1;
     resident = cus * (per_cu > 0 ? per_cu : 1);
+    if (dev < kMaxDevices) cache[dev].store(resident, std::memory_order_relaxed);
   }
   int64_t g = max_blocks < resident ? max_blocks : resident;
   g = (g + kNumXcd - 1) / kNumXcd * kNumXcd;

@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -74,6 +75,38 @@ int64_t routed_max_tiles(const moe_config_t* c) {
   return (assignments(c) + bm - 1) / bm + c->num_experts;
 }
 
+// The GEMMs read every operand through a buffer resource whose size and per-lane offsets are
+// 32-bit: one operand (x, the FP8 activations and their scales, h and h_s and their scales, the
+// permutation, one group's packed weights or weight scales) must stay below 4 GiB, or loads
+// past the wrap would read zeros.  Outputs are addressed per tile from a 64-bit base.  Sizes
+// are taken in 64-bit arithmetic after check_config has bounded each factor.
+bool addressable(const moe_config_t* c) {
+  const int64_t lim = 1LL << 32;
+  const int64_t T = c->num_tokens, d = c->d_model, f = c->d_ff, A = assignments(c);
+  const int64_t F = shared_width(c), hb = h_bytes(c);
+  const bool q = is_fp8(c);
+  // bytes of one group's weight scales: FP8 fp32 per 16 packed rows and 128 K; MXFP4 a byte
+  // per row and 32 K
+  auto scales = [&](int64_t N, int64_t K) -> int64_t {
+    return !q ? 0 : is_mx(c) ? N * (K / 32) : (N / 16) * (K / 128) * 4;
+  };
+  const int64_t rk = router_kind(c);
+  const int64_t router = e_pad(c) * (rk == kRouterBF16HiLo ? 2 * d : d) * (rk == kRouterF32 ? 4 : 2);
+  const int64_t sizes[] = {
+      T * d * act_bytes(c),                   // x (router; bf16 / fp32 experts)
+      q ? T * d : 0, q ? T * (d / 128) * 4 : 0,  // E4M3 x and its scales
+      A * f * hb, q ? A * (f / 128) * 4 : 0,  // h and its scales
+      T * F * hb, q ? T * (F / 128) * 4 : 0,  // h_s and its scales
+      A * 4,                                  // perm_token
+      2 * f * wrow(c, d), d * wrow(c, f),     // one routed expert's gate/up and down
+      2 * F * wrow(c, d), d * wrow(c, F),     // the shared experts' gate/up and down
+      scales(2 * f, d), scales(d, f), scales(2 * F, d), scales(d, F),
+      router};
+  for (int64_t v : sizes)
+    if (v >= lim) return false;
+  return true;
+}
+
 moe_status_t check_config(const moe_config_t* c) {
   if (!c) return MOE_ERR_INVALID_ARGUMENT;
   if (c->num_tokens < 0 || c->d_model <= 0 || c->num_experts <= 0 || c->top_k < 1 ||
@@ -99,7 +132,12 @@ moe_status_t check_config(const moe_config_t* c) {
   if (c->d_model % 128 || c->d_ff % 128 || (c->num_shared > 0 && c->d_ff_shared % 128))
     return MOE_ERR_UNSUPPORTED;
   if (c->num_experts > 1024 || c->top_k > 64) return MOE_ERR_UNSUPPORTED;
-  if (assignments(c) > (1LL << 30) || shared_width(c) > (1 << 20)) return MOE_ERR_UNSUPPORTED;
+  // (bounds every factor of the operand sizes below, so their 64-bit products cannot overflow)
+  if (c->d_model > (1 << 24) || c->d_ff > (1 << 24) ||
+      (c->num_shared > 0 && c->d_ff_shared > (1 << 24)))
+    return MOE_ERR_UNSUPPORTED;
+  if (assignments(c) >= (1LL << 30) || shared_width(c) > (1 << 20)) return MOE_ERR_UNSUPPORTED;
+  if (!addressable(c)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -416,6 +454,34 @@ hipError_t do_combine(const moe_config_t* c, const void* xa, const float* xs, co
   return e;
 }
 
+// The launch sequence of moe_forward on a workspace laid out by ws_layout (arguments checked).
+hipError_t forward(const moe_config_t* c, const void* x, const moe_weights_t* w, void* out,
+                   const moe_debug_t* dbg, void* ws, hipStream_t s) {
+  const WsLayout L = ws_layout(c);
+  moe_debug_t d{};
+  if (dbg) d = *dbg;
+  int32_t* ids = d.topk_ids ? d.topk_ids : at<int32_t>(ws, L.ids);
+  float* tw = d.topk_w ? d.topk_w : at<float>(ws, L.w);
+  int32_t* offsets = d.expert_offsets ? d.expert_offsets : at<int32_t>(ws, L.offsets);
+  int32_t* perm = d.perm_token ? d.perm_token : at<int32_t>(ws, L.perm);
+  int32_t* inv = d.inv_perm ? d.inv_perm : at<int32_t>(ws, L.inv);
+  void* y = d.y_perm ? d.y_perm : at<void>(ws, L.y);
+  void* xq = is_fp8(c) ? at<void>(ws, L.xq) : nullptr;
+  float* xs = is_fp8(c) ? at<float>(ws, L.xq_scales) : nullptr;
+  const void* xa = is_fp8(c) ? static_cast<const void*>(xq) : x;
+  hipEvent_t* ev = d.stage_events;
+  hipError_t e = mark(ev, MOE_STAGE_BEGIN, s);
+  if (e == hipSuccess) e = do_route(c, x, w, d.logits, ids, tw, xq, xs, ws, s);
+  if (e == hipSuccess) e = mark(ev, MOE_STAGE_ROUTED, s);
+  if (e == hipSuccess)
+    e = launch_permute(ids, c->num_tokens, c->top_k, c->num_experts, offsets, perm, inv,
+                       at<int32_t>(ws, L.hist), s);
+  if (e == hipSuccess) e = mark(ev, MOE_STAGE_PERMUTED, s);
+  if (e == hipSuccess) e = do_expert_ffn(c, xa, xs, offsets, perm, w, y, ws, s, ev);
+  if (e == hipSuccess) e = do_combine(c, xa, xs, y, inv, tw, w, out, ws, s, ev);
+  return e;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -615,29 +681,7 @@ moe_status_t moe_forward(const moe_config_t* c, const void* x, const moe_weights
   if ((st = check_weights(c, w, true, true, true)) != MOE_OK) return st;
   if ((st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
   if (c->num_tokens == 0) return MOE_OK;
-  const WsLayout L = ws_layout(c);
-  moe_debug_t d{};
-  if (dbg) d = *dbg;
-  int32_t* ids = d.topk_ids ? d.topk_ids : at<int32_t>(ws, L.ids);
-  float* tw = d.topk_w ? d.topk_w : at<float>(ws, L.w);
-  int32_t* offsets = d.expert_offsets ? d.expert_offsets : at<int32_t>(ws, L.offsets);
-  int32_t* perm = d.perm_token ? d.perm_token : at<int32_t>(ws, L.perm);
-  int32_t* inv = d.inv_perm ? d.inv_perm : at<int32_t>(ws, L.inv);
-  void* y = d.y_perm ? d.y_perm : at<void>(ws, L.y);
-  void* xq = is_fp8(c) ? at<void>(ws, L.xq) : nullptr;
-  float* xs = is_fp8(c) ? at<float>(ws, L.xq_scales) : nullptr;
-  const void* xa = is_fp8(c) ? static_cast<const void*>(xq) : x;
-  hipEvent_t* ev = d.stage_events;
-  hipError_t e = mark(ev, MOE_STAGE_BEGIN, s);
-  if (e == hipSuccess) e = do_route(c, x, w, d.logits, ids, tw, xq, xs, ws, s);
-  if (e == hipSuccess) e = mark(ev, MOE_STAGE_ROUTED, s);
-  if (e == hipSuccess)
-    e = launch_permute(ids, c->num_tokens, c->top_k, c->num_experts, offsets, perm, inv,
-                       at<int32_t>(ws, L.hist), s);
-  if (e == hipSuccess) e = mark(ev, MOE_STAGE_PERMUTED, s);
-  if (e == hipSuccess) e = do_expert_ffn(c, xa, xs, offsets, perm, w, y, ws, s, ev);
-  if (e == hipSuccess) e = do_combine(c, xa, xs, y, inv, tw, w, out, ws, s, ev);
-  return hip_status(e);
+  return hip_status(forward(c, x, w, out, dbg, ws, s));
 }
 
 }  // extern "C"

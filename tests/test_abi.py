@@ -121,6 +121,41 @@ def test_large_and_fp8_constraints():
         api.MOE_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("name,over,ok", [
+    # h = [T*k, d_ff] bf16 = 65536 * 8 * 4096 * 2 B = 4 GiB exactly
+    ("softmax_bf16", dict(num_tokens=65536, top_k=8, d_ff=4096), dict(num_tokens=65535)),
+    # x = [T, d] bf16 = 4 GiB
+    ("softmax_bf16", dict(num_tokens=1 << 19, top_k=1, d_model=4096),
+     dict(num_tokens=(1 << 19) - 1)),
+    # the shared experts' h = [T, S*f_s] bf16 = 4 GiB
+    ("softplus_bf16", dict(num_tokens=1 << 18, top_k=1, num_shared=2, d_ff_shared=4096),
+     dict(num_tokens=(1 << 18) - 1)),
+    # one routed expert's gate/up weights [2f, d] fp32 = 4 GiB
+    ("tiny_fp32", dict(num_tokens=1, d_model=32768, d_ff=16384, d_ff_shared=128),
+     dict(d_ff=16384 - 128)),
+    # the FP8 h = [T*k, d_ff] E4M3 = 4 GiB
+    ("fp8_block", dict(num_tokens=1 << 18, top_k=32, d_ff=512), dict(top_k=31)),
+    # T*k = 2^30 assignments: the permutation's row count
+    ("softmax_bf16", dict(num_tokens=1 << 27, top_k=8, d_model=128, d_ff=128, d_ff_shared=128),
+     dict(num_tokens=1 << 20)),
+    # the largest int32 widths: the products of the size arithmetic would overflow 64 bits
+    ("softmax_bf16", dict(num_tokens=0, d_model=2**31 - 128, d_ff=2**31 - 128),
+     dict(d_model=1 << 20, d_ff=128, d_ff_shared=128)),
+])
+def test_configs_beyond_32_bit_operands_are_refused(name, over, ok):
+    # every GEMM operand goes through a 32-bit buffer resource: a config with an operand of
+    # 4 GiB or more is refused before anything is launched, instead of reading wrapped rows
+    c = api.config_struct(PRESETS[name], **over)
+    L = api.lib()
+    assert L.moe_workspace_size(ctypes.byref(c)) == 0
+    w = api.moe_weights_t()
+    assert L.moe_forward(ctypes.byref(c), 1, ctypes.byref(w), 1, None, 1, 1 << 40, None) == \
+        api.MOE_ERR_UNSUPPORTED
+    # just inside the limits the same shape is accepted
+    c = api.config_struct(PRESETS[name], **{**over, **ok})
+    assert L.moe_workspace_size(ctypes.byref(c)) > 0
+
+
 def test_null_pointers_and_small_workspace():
     L = api.lib()
     cfg = api.config_struct(PRESETS["tiny_fp32"])
@@ -219,3 +254,4 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+

@@ -329,10 +329,12 @@ def test_identity_like_experts_reproduce_input():
 
 # ---------------------------------------------------------------- full-size workloads
 
-@pytest.mark.parametrize("name,sample", [("decode_bf16", 64), ("softmax_bf16", 24),
-                                         ("softplus_bf16", 12), ("fp8_block", 16),
-                                         ("qwen_gated_bf16", 16), ("mxfp4_decode", 64),
-                                         ("mxfp4_block", 16)])
+# decode shapes check every token; the prefill shapes a seeded sample of 256 tokens (0.4-6% of
+# their rows), which the oracle computes in seconds on the host's cores
+@pytest.mark.parametrize("name,sample", [("decode_bf16", 64), ("softmax_bf16", 256),
+                                         ("softplus_bf16", 256), ("fp8_block", 256),
+                                         ("qwen_gated_bf16", 64), ("mxfp4_decode", 64),
+                                         ("mxfp4_block", 64)])
 def test_full_size_workloads(name, sample):
     cfg = PRESETS[name]
     layer = Layer(cfg)
