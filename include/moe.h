@@ -312,6 +312,27 @@ MOE_API moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const m
                          void* out, const moe_debug_t* dbg, void* ws, size_t ws_bytes,
                          hipStream_t stream);
 
+/* Bytes of the library's own device workspace used by moe_forward_noalloc (per GPU). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* moe_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight decode-serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels and results as moe_forward, without ws / ws_bytes:
+ * the workspace is a static array of MOE_NOALLOC_SCRATCH_BYTES (64 MiB) that
+ * the library's code object places on each GPU it runs on, held until the
+ * process ends.  Nothing is allocated or freed.  Configs whose
+ * moe_workspace_size exceeds that limit return MOE_ERR_WORKSPACE_TOO_SMALL
+ * before anything is launched (decode shapes fit: e.g. 64 tokens at d 4096, 256
+ * experts, top 8, d_ff 1536 need 11 MB).  All calls on one GPU share its array:
+ * calls that may run concurrently on one GPU (other host threads, other
+ * streams) race and must be serialised by the caller.  Nothing in the array has
+ * to start at zero; each call fully writes what it reads.  The first call on a
+ * device looks the array's address up (hipGetSymbolAddress) with that device
+ * current; MOE_ERR_HIP if that fails. */
+MOE_API moe_status_t moe_forward_noalloc(const moe_config_t* cfg, const void* x,
+                                         const moe_weights_t* weights, void* out,
+                                         const moe_debug_t* dbg, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,10 @@ PACK_COUNT = 9
 
 EXPORTED = ["moe_status_string", "moe_workspace_size", "moe_packed_size", "moe_pack_weights",
             "moe_route", "moe_route_from_logits", "moe_route_hashed", "moe_update_bias",
-            "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward"]
+            "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_noalloc"]
+
+# bytes of the library's own workspace behind moe_forward_noalloc (MOE_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class moe_config_t(ctypes.Structure):
@@ -110,6 +113,8 @@ def lib():
         L.moe_forward.restype = ctypes.c_int
         L.moe_forward.argtypes = [cp, _vp, wp, _vp, ctypes.POINTER(moe_debug_t), _vp,
                                   ctypes.c_size_t, _vp]
+        L.moe_forward_noalloc.restype = ctypes.c_int
+        L.moe_forward_noalloc.argtypes = [cp, _vp, wp, _vp, ctypes.POINTER(moe_debug_t), _vp]
         _LIB = L
     return _LIB
 
@@ -252,6 +257,20 @@ def moe_forward(cfg, x, weights, out, ws, dbg: dict = None, stream=None):
     _check(lib().moe_forward(_cfg(cfg), _p(x), ctypes.byref(weights), _p(out),
                              ctypes.byref(d) if d is not None else None, _p(ws),
                              ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")
+
+
+def moe_forward_noalloc(cfg, x, weights, out, dbg: dict = None, stream=None):
+    """moe_forward on the library's own static device workspace (no workspace argument)."""
+    _need(out, cfg, _tokens, out_dtype, "moe_forward_noalloc", "out")
+    if dbg:
+        _need(dbg.get("y_perm"), cfg, _assignments, y_dtype, "moe_forward_noalloc",
+              "dbg['y_perm']")
+    d = None
+    if dbg:
+        d = moe_debug_t(*[_p(dbg.get(n)) for n, _ in moe_debug_t._fields_])
+    _check(lib().moe_forward_noalloc(_cfg(cfg), _p(x), ctypes.byref(weights), _p(out),
+                                     ctypes.byref(d) if d is not None else None,
+                                     _stream(stream)), "moe_forward_noalloc")
 
 
 # ------------------------------------------------------------------ memory plumbing

@@ -3,12 +3,46 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 
 #include "moe_common.h"
 #include "moe_internal.h"
 
+// Workspace of moe_forward_noalloc, for callers that cannot allocate: a file-scope device array
+// that each GPU the library runs on holds until the process ends.  In host code `scratch` only
+// names the symbol; its device address on the current device comes from hipGetSymbolAddress
+// (static_scratch), and only that address is ever handed to kernels.  Every call on one GPU
+// shares that GPU's copy: calls that overlap on one GPU race.  No kernel of the block relies on
+// the workspace's previous contents (each buffer in it is fully written before it is read), so
+// nothing has to be cleared between calls.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 namespace moe {
 namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::once_flag g_scratch_once[kMaxScratchDevices];
+void* g_scratch_ptr[kMaxScratchDevices];
+hipError_t g_scratch_err[kMaxScratchDevices];
+
+// Device address of `scratch` on the current device, looked up once per device (on the first
+// call that runs there, with that device current).
+hipError_t static_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  *ptr = g_scratch_ptr[dev];
+  return g_scratch_err[dev] != hipSuccess ? g_scratch_err[dev]
+         : *ptr == nullptr                ? hipErrorInvalidSymbol
+                                          : hipSuccess;
+}
+
 
 constexpr size_t kAlign = 256;
 
@@ -681,6 +715,19 @@ moe_status_t moe_forward(const moe_config_t* c, const void* x, const moe_weights
   if ((st = check_weights(c, w, true, true, true)) != MOE_OK) return st;
   if ((st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
   if (c->num_tokens == 0) return MOE_OK;
+  return hip_status(forward(c, x, w, out, dbg, ws, s));
+}
+
+moe_status_t moe_forward_noalloc(const moe_config_t* c, const void* x, const moe_weights_t* w,
+                                 void* out, const moe_debug_t* dbg, hipStream_t s) {
+  moe_status_t st = check_config(c);
+  if (st != MOE_OK) return st;
+  if (!x || !out) return MOE_ERR_INVALID_ARGUMENT;
+  if ((st = check_weights(c, w, true, true, true)) != MOE_OK) return st;
+  if (ws_layout(c).total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (c->num_tokens == 0) return MOE_OK;
+  void* ws = nullptr;
+  if (static_scratch(&ws) != hipSuccess) return MOE_ERR_HIP;
   return hip_status(forward(c, x, w, out, dbg, ws, s));
 }
 

@@ -255,3 +255,22 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
 
+
+def test_noalloc_forward_refuses_configs_beyond_its_scratch():
+    # the allocation-free forward has a fixed workspace: a config that needs more is refused
+    # on the host, before any HIP call
+    L = api.lib()
+    # placeholder pointers: the checks below return before anything is dereferenced
+    w = api.moe_weights_t(*([1] * len(api.moe_weights_t._fields_)))
+    big = api.config_struct(PRESETS["softmax_bf16"])
+    assert L.moe_workspace_size(ctypes.byref(big)) > api.NOALLOC_SCRATCH_BYTES
+    assert L.moe_forward_noalloc(ctypes.byref(big), 1, ctypes.byref(w), 1, None, None) == \
+        api.MOE_ERR_WORKSPACE_TOO_SMALL
+    # the decode workload fits; argument errors still come first
+    dec = api.config_struct(PRESETS["decode_bf16"])
+    assert 0 < L.moe_workspace_size(ctypes.byref(dec)) <= api.NOALLOC_SCRATCH_BYTES
+    assert L.moe_forward_noalloc(ctypes.byref(dec), None, ctypes.byref(w), 1, None, None) == \
+        api.MOE_ERR_INVALID_ARGUMENT
+    bad = api.config_struct(PRESETS["decode_bf16"], top_k=0)
+    assert L.moe_forward_noalloc(ctypes.byref(bad), 1, ctypes.byref(w), 1, None, None) == \
+        api.MOE_ERR_INVALID_ARGUMENT

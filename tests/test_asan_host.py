@@ -76,6 +76,9 @@ int main(void) {
     EXPECT(moe_combine(&c, P, P, P, NULL, P, &w, P, P, ws, 0), MOE_ERR_INVALID_ARGUMENT);
     EXPECT(moe_combine(&c, P, P, P, P, P, &w, P, P, 1, 0), MOE_ERR_WORKSPACE_TOO_SMALL);
     EXPECT(moe_pack_weights(&c, NULL, packed, 0), MOE_ERR_INVALID_ARGUMENT);
+    EXPECT(moe_forward_noalloc(&c, NULL, &w, P, NULL, 0), MOE_ERR_INVALID_ARGUMENT);
+    if (ws > MOE_NOALLOC_SCRATCH_BYTES)
+      EXPECT(moe_forward_noalloc(&c, P, &w, P, NULL, 0), MOE_ERR_WORKSPACE_TOO_SMALL);
     /* zero tokens: valid, launches nothing */
     moe_config_t z = c;
     z.num_tokens = 0;
@@ -86,6 +89,7 @@ int main(void) {
     EXPECT(moe_expert_ffn(&z, P, P, P, P, &w, P, P, wz, 0), MOE_OK);
     EXPECT(moe_combine(&z, P, P, P, P, P, &w, P, P, wz, 0), MOE_OK);
     EXPECT(moe_route_from_logits(&z, P, NULL, P, P, 0), MOE_OK);
+    EXPECT(moe_forward_noalloc(&z, P, &w, P, NULL, 0), MOE_OK);
     /* bad and unsupported configs: every field pushed out of range */
     int32_t* f = (int32_t*)&c;
     for (size_t i = 0; i < sizeof c / sizeof(int32_t); ++i) {
