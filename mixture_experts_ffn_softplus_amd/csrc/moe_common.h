@@ -102,6 +102,16 @@ __device__ __forceinline__ void buffer_store8(__amdgpu_buffer_rsrc_t r, uint32_t
   __builtin_amdgcn_raw_buffer_store_b64(i32x2{static_cast<int>(v.x), static_cast<int>(v.y)}, r,
                                         static_cast<int>(voff), 0, 0);
 }
+// The same stores marked non-temporal (streamed: written once, read once by a later kernel).
+__device__ __forceinline__ void buffer_store16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, static_cast<int>(voff), 0,
+                                         kNonTemporal);
+}
+__device__ __forceinline__ void buffer_store8_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint2 v) {
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(i32x2{static_cast<int>(v.x), static_cast<int>(v.y)}, r,
+                                        static_cast<int>(voff), 0, kNonTemporal);
+}
 __device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t v) {
   __builtin_amdgcn_raw_buffer_store_b32(static_cast<int>(v), r, static_cast<int>(voff), 0, 0);
 }
