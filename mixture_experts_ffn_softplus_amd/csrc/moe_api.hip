@@ -258,8 +258,9 @@ RouteArgs route_args(const moe_config_t* c, const float* select_bias, int32_t* i
   return a;
 }
 
-// Router logits on the MFMA GEMM (fp32 out, logit bias in the epilogue) into the workspace,
-// then scoring and top-k; FP8 experts also get their block-scaled activations.
+// Router logits on the MFMA GEMM (fp32 out) into the workspace, then one kernel for the logit
+// bias, scoring, top-k and weights -- and for FP8 experts the block-scaled activations of each
+// token, written by the wave that routes it.
 hipError_t do_route(const moe_config_t* c, const void* x, const moe_weights_t* w, float* logits,
                     int32_t* ids, float* tw, void* xq, float* xq_scales, void* ws,
                     hipStream_t s, const int32_t* token_ids = nullptr,
@@ -290,12 +291,13 @@ hipError_t do_route(const moe_config_t* c, const void* x, const moe_weights_t* w
   ra.token_ids = token_ids;
   ra.table = table;
   ra.vocab = vocab;
-  e = launch_topk(ra, lg, static_cast<int>(Ep), logits, s);
-  if (e != hipSuccess) return e;
-  if (is_fp8(c) && xq && xq_scales)
-    e = launch_quant_x_fp8(static_cast<const uint16_t*>(x), static_cast<uint8_t*>(xq), xq_scales,
-                           c->num_tokens, c->d_model, s);
-  return e;
+  if (is_fp8(c) && xq && xq_scales) {  // the same waves quantise their token's activations
+    ra.x = static_cast<const uint16_t*>(x);
+    ra.xq = static_cast<uint8_t*>(xq);
+    ra.xq_scales = xq_scales;
+    ra.d = c->d_model;
+  }
+  return launch_topk(ra, lg, static_cast<int>(Ep), logits, s);
 }
 
 // Records stage event i when the caller asked for stage timing.

@@ -21,14 +21,18 @@ struct RouteArgs {
   const int32_t* token_ids;  // [T], or null (top-k choice)
   const int32_t* table;      // [vocab, k]
   int vocab;
+  // block-scaled FP8 activations of the same tokens, written by the same waves when xq is set:
+  // x [T, d] bf16 -> xq [T, d] E4M3 codes and xq_scales [T, d/128]
+  const uint16_t* x;
+  uint8_t* xq;
+  float* xq_scales;
+  int d;
 };
 enum RouterKind { kRouterF32 = 0, kRouterBF16 = 1, kRouterBF16HiLo = 2 };
-// Scoring + top-k of fp32 logits rows `ld` apart (plus logit_bias); copy: optional [T, E]
-// copy of the biased logits.
+// Scoring + top-k of fp32 logits rows `ld` apart (plus logit_bias), and the FP8 activations
+// when a.xq is set; copy: optional [T, E] copy of the biased logits.
 hipError_t launch_topk(const RouteArgs& a, const float* logits, int ld, float* copy,
                        hipStream_t s);
-hipError_t launch_quant_x_fp8(const uint16_t* x, uint8_t* xq, float* scales, int T, int d,
-                              hipStream_t s);
 // Balancing step of the fp32 selection bias from the permutation's expert offsets [E+1]:
 // bias[e] += speed * sign(A - E * load_e), A = offsets[E].
 hipError_t launch_bias_update(const int32_t* offsets, int E, float speed, float* bias,

@@ -9,7 +9,8 @@
 //
 // The logits come from the grouped MFMA GEMM (one group, fp32 out); the logit bias is added
 // here as each logit is read.  One wave owns one token: each lane scores E/64 experts held in
-// registers, then k rounds of a 64-lane argmax pick the experts in key order.  In the layers
+// registers and sorts their keys, then k rounds of a 64-lane maximum over the lanes' largest
+// remaining keys pick the experts in key order.  In the layers
 // that choose by a fixed token-id hash (same row, DeepSeek-V4-Pro cell) a table gives the k
 // experts instead, and only the combine weights are computed.
 #include <math.h>
@@ -19,7 +20,6 @@
 
 namespace moe {
 
-constexpr int kMaxPerLane = 16;       // experts per lane in top-k: E <= 1024
 
 // Score of the sigma family, evaluated in fp64 and rounded once to fp32, so the
 // selection key is one fixed fp32 number.
@@ -70,68 +70,82 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-// Top-k of one token over `row[0..E)` (LDS or global), executed by one full wave.
+// The lane's N keys sorted into descending order in registers (a bitonic network: the indices
+// are compile-time constants once unrolled, so nothing leaves the registers).
+template <int N>
+__device__ __forceinline__ void sort_desc(uint64_t* k) {
+#pragma unroll
+  for (int size = 2; size <= N; size <<= 1)
+#pragma unroll
+    for (int stride = size / 2; stride > 0; stride >>= 1)
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          // blocks of `size` alternate direction; the last merge (size = N) is descending
+          const bool desc = (i & size) == 0;
+          const uint64_t a = k[i], b = k[j];
+          const bool sw = desc ? a < b : a > b;
+          k[i] = sw ? b : a;
+          k[j] = sw ? a : b;
+        }
+      }
+}
+
+// Logit of expert e with the logit bias, and its unbiased score (softmax: the logit).
+__device__ __forceinline__ float expert_value(const float* row, int e, const RouteArgs& a) {
+  const float lg = a.logit_bias ? __fadd_rn(row[e], a.logit_bias[e]) : row[e];
+  return a.score == MOE_SCORE_SOFTMAX ? lg : sigma_family_score(a.score, lg);
+}
+
+// Top-k of one token over `row[0..E)`, executed by one full wave; lane l holds experts
+// l + 64 i, i < SLOTS (E <= 64 * SLOTS).  Each lane sorts its keys once; a round is then the
+// wave's largest lane head (the winner) and one shift of the winner's lane, instead of a scan of
+// every slot of every lane.  The winners' scores are evaluated again from their ids, by the same
+// function that made the keys.
+template <int SLOTS>
 __device__ void topk_row(const float* row, int t, const RouteArgs& a) {
   const int l = lane_id();
-  uint64_t key[kMaxPerLane];
-  float val[kMaxPerLane];
+  uint64_t key[SLOTS];
+  float val[SLOTS];
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
+  for (int i = 0; i < SLOTS; ++i) {
     int e = l + kWave * i;
     key[i] = 0;
     val[i] = 0.0f;
     if (e < a.E) {
-      const float lg = a.logit_bias ? __fadd_rn(row[e], a.logit_bias[e]) : row[e];
+      const float s = expert_value(row, e, a);
+      val[i] = s;
       if (a.score == MOE_SCORE_SOFTMAX) {
-        key[i] = select_key(lg, e);
-        val[i] = lg;
+        key[i] = select_key(s, e);
       } else {
-        float s = sigma_family_score(a.score, lg);
-        float b = a.select_bias ? a.select_bias[e] : 0.0f;
-        val[i] = s;
+        const float b = a.select_bias ? a.select_bias[e] : 0.0f;
         key[i] = select_key(__fadd_rn(s, b), e);
       }
     }
   }
   int my_id = 0;
-  float my_val = 0.0f;
   if (a.table) {
-    // fixed token-id table: lane j < k takes slot j's expert and its unbiased score.  Values
-    // outside their ranges (a precondition violation) are clamped, so nothing reads out of
-    // bounds.
+    // fixed token-id table: lane j < k takes slot j's expert.  Values outside their ranges (a
+    // precondition violation) are clamped, so nothing reads out of bounds.
     if (l < a.k) {
       const int tok = min(max(a.token_ids[t], 0), a.vocab - 1);
-      const int e = min(max(a.table[static_cast<size_t>(tok) * a.k + l], 0), a.E - 1);
-      const float lg = a.logit_bias ? __fadd_rn(row[e], a.logit_bias[e]) : row[e];
-      my_id = e;
-      my_val = a.score == MOE_SCORE_SOFTMAX ? lg : sigma_family_score(a.score, lg);
+      my_id = min(max(a.table[static_cast<size_t>(tok) * a.k + l], 0), a.E - 1);
+    }
+  } else {
+    sort_desc<SLOTS>(key);
+    // k rounds: the largest head wins, its lane drops it; lane j keeps the winner of round j
+    for (int j = 0; j < a.k; ++j) {
+      const uint64_t win = wave_max_key(key[0]);
+      const int we = static_cast<int>(~static_cast<uint32_t>(win));
+      const bool mine = l == (we & (kWave - 1));
+#pragma unroll
+      for (int i = 0; i + 1 < SLOTS; ++i) key[i] = mine ? key[i + 1] : key[i];
+      key[SLOTS - 1] = mine ? 0 : key[SLOTS - 1];
+      if (l == j) my_id = we;
     }
   }
-  // k rounds: each lane's largest remaining key, the wave's largest of those; its owner lane
-  // drops it and lane j keeps the winner of round j
-  for (int j = 0; j < (a.table ? 0 : a.k); ++j) {
-    uint64_t best = 0;
-    float bv = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-      const bool gt = key[i] > best;
-      best = gt ? key[i] : best;
-      bv = gt ? val[i] : bv;
-    }
-    const uint64_t win = wave_max_key(best);
-    const int we = static_cast<int>(~static_cast<uint32_t>(win));
-    const int owner = we & (kWave - 1);
-    const float wv = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(bv), owner));
-    if (l == owner) {
-#pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i)
-        if (i == (we >> 6)) key[i] = 0;
-    }
-    if (l == j) {
-      my_id = we;
-      my_val = wv;
-    }
-  }
+  const float my_val = l < a.k ? expert_value(row, my_id, a) : 0.0f;
   float w;
   if (a.score == MOE_SCORE_SOFTMAX) {
     float m, denom;
@@ -142,12 +156,12 @@ __device__ void topk_row(const float* row, int t, const RouteArgs& a) {
     } else {
       float mm = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i)
+      for (int i = 0; i < SLOTS; ++i)
         if (l + kWave * i < a.E) mm = fmaxf(mm, val[i]);
       m = wave_max(mm);
       float part = 0.0f;
 #pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i)
+      for (int i = 0; i < SLOTS; ++i)
         if (l + kWave * i < a.E) part += expf(val[i] - m);
       denom = wave_sum(part);
     }
@@ -162,9 +176,44 @@ __device__ void topk_row(const float* row, int t, const RouteArgs& a) {
   }
 }
 
+// Block-scaled FP8 activations of token t, by the wave that routed it: one fp32 scale =
+// max|x| / 448 (1 for an all-zero group) per 128 consecutive values of the row, codes =
+// E4M3(x / scale), both divisions correctly rounded fp32 (blueprint training box: FP8 with
+// block scales).  16 lanes own one group, 8 values each; the wave covers four groups at a time.
+__device__ void quant_row_fp8(const RouteArgs& a, int t) {
+  const int l = lane_id(), sub = l & 15, groups = a.d / 128;
+  const uint16_t* xr = a.x + static_cast<size_t>(t) * a.d;
+  uint8_t* qr = a.xq + static_cast<size_t>(t) * a.d;
+  for (int g0 = 0; g0 < groups; g0 += 4) {
+    const int grp = g0 + (l >> 4);
+    const bool valid = grp < groups;  // whole 16-lane groups
+    const int at = (valid ? grp : 0) * 128 + sub * 8;
+    const i32x4 raw = *reinterpret_cast<const i32x4*>(xr + at);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(static_cast<uint32_t>(raw[i]) << 16);
+      v[2 * i + 1] = __uint_as_float(static_cast<uint32_t>(raw[i]) & 0xFFFF0000u);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+    const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+    const uint32_t lo = e4m3x4(v[0] / sc, v[1] / sc, v[2] / sc, v[3] / sc);
+    const uint32_t hi = e4m3x4(v[4] / sc, v[5] / sc, v[6] / sc, v[7] / sc);
+    if (valid) {
+      *reinterpret_cast<uint2*>(qr + at) = uint2{lo, hi};
+      if (sub == 0) a.xq_scales[static_cast<size_t>(t) * groups + grp] = sc;
+    }
+  }
+}
+
 // One wave per token.  `logits` rows are `ld` floats apart; a.logit_bias (if any) is added to
 // each (one fp32 add, the last step of the logits); when `copy` is non-null the E finished
 // logits of each row are also written there as [T, E].
+template <int SLOTS>
 __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a, const float* __restrict__ logits,
                                                    int ld, float* __restrict__ copy) {
   int t = blockIdx.x * 4 + threadIdx.x / kWave;
@@ -174,50 +223,21 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a, const float* __r
     for (int e = lane_id(); e < a.E; e += kWave)
       copy[static_cast<size_t>(t) * a.E + e] =
           a.logit_bias ? __fadd_rn(row[e], a.logit_bias[e]) : row[e];
-  topk_row(row, t, a);
-}
-
-// Block-scaled FP8 activations: one fp32 scale = max|x| / 448 (1 for an all-zero group)
-// per 128 consecutive values of a row, codes = E4M3(x / scale), both divisions correctly
-// rounded fp32.  16 lanes own one group, 8 values each.
-__global__ __launch_bounds__(256) void quant_x_fp8_kernel(const uint16_t* __restrict__ x,
-                                                          uint8_t* __restrict__ xq,
-                                                          float* __restrict__ scales, int T,
-                                                          int d) {
-  const int groups_per_row = d / 128;
-  const int64_t total = static_cast<int64_t>(T) * groups_per_row;
-  const int64_t gid = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / 16;
-  const int sub = threadIdx.x & 15;
-  const bool valid = gid < total;
-  const int64_t g = valid ? gid : 0;
-  const int64_t row = g / groups_per_row, grp = g - row * groups_per_row;
-  const size_t base = static_cast<size_t>(row) * d + grp * 128 + sub * 8;
-  i32x4 raw = *reinterpret_cast<const i32x4*>(x + base);
-  float v[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(static_cast<uint32_t>(raw[i]) << 16);
-    v[2 * i + 1] = __uint_as_float(static_cast<uint32_t>(raw[i]) & 0xFFFF0000u);
-  }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
-  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-  const uint32_t lo = e4m3x4(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
-  const uint32_t hi = e4m3x4(v[4] / s, v[5] / s, v[6] / s, v[7] / s);
-  if (valid) {
-    uint2 packed{lo, hi};
-    *reinterpret_cast<uint2*>(xq + base) = packed;
-    if (sub == 0) scales[g] = s;
-  }
+  topk_row<SLOTS>(row, t, a);
+  if (a.xq) quant_row_fp8(a, t);
 }
 
 hipError_t launch_topk(const RouteArgs& a, const float* logits, int ld, float* copy,
                        hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a, logits, ld, copy);
+  // experts per lane: E <= 64 * SLOTS (E <= 1024, checked by the caller)
+  const dim3 grid((a.T + 3) / 4), block(256);
+  if (a.E <= 256)
+    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, a, logits, ld, copy);
+  else if (a.E <= 512)
+    hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, a, logits, ld, copy);
+  else
+    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, a, logits, ld, copy);
   return hipGetLastError();
 }
 
@@ -242,14 +262,5 @@ hipError_t launch_bias_update(const int32_t* offsets, int E, float speed, float*
   return hipGetLastError();
 }
 
-hipError_t launch_quant_x_fp8(const uint16_t* x, uint8_t* xq, float* scales, int T, int d,
-                              hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  int64_t groups = static_cast<int64_t>(T) * (d / 128);
-  int64_t blocks = (groups * 16 + 255) / 256;
-  hipLaunchKernelGGL(quant_x_fp8_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
-                     x, xq, scales, T, d);
-  return hipGetLastError();
-}
 
 }  // namespace moe
