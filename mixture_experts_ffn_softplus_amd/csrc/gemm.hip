@@ -163,8 +163,10 @@ struct TileGeo {
 };
 
 // GROUPED: rows come from the device tile list of an expert-grouped problem (the routed
-// experts); otherwise one group of a.M rows (router, shared experts).
-template <int DT, int BM, int BN, int EPI, bool GROUPED>
+// experts); otherwise one group of a.M rows (router, shared experts).  G2 (grouped only): the
+// tile list also holds the extra group of GemmArgs (the shared experts of decode-sized
+// batches); a separate instantiation, so the other launches carry none of its registers.
+template <int DT, int BM, int BN, int EPI, bool GROUPED, bool G2>
 __global__ __launch_bounds__((gemm_waves<DT, BN>() * kWave), (gemm_occupancy<DT, BM, BN, EPI>()))
 void grouped_gemm_kernel(GemmArgs a) {
   using S = GemmShape<DT, BM, BN, EPI>;
@@ -232,7 +234,11 @@ void grouped_gemm_kernel(GemmArgs a) {
   // lane-to-chunk map is chosen on the global side so that the tile lands in the swizzled
   // layout the fragment reads expect (row r's logical chunk c at slot r*8 + (c ^ (r & 7))).
   // No staging registers, no LDS store instructions.
-  const i32x4 a_rs = rsrc_words(a.A, static_cast<uint32_t>(a.a_bytes));
+  // the extra group (the shared experts, rows = the tokens in order) reads its own operands
+  constexpr bool has2 = GROUPED && G2;
+  const i32x4 a_rs1 = rsrc_words(a.A, static_cast<uint32_t>(a.a_bytes));
+  const i32x4 a_rs2 = has2 ? rsrc_words(a.A2, static_cast<uint32_t>(a.a2_bytes)) : a_rs1;
+  i32x4 a_rs = a_rs1;
   int a_dst[S::A_PER], b_dst[S::B_PER];  // LDS byte offsets within a slot (-1: dummy)
 #pragma unroll
   for (int i = 0; i < S::A_PER; ++i) {
@@ -267,11 +273,14 @@ void grouped_gemm_kernel(GemmArgs a) {
     g_prev = g_iss;
     g_iss = g;
     g_iss_t = t;
+    const bool second = has2 && g.group == a.group2;  // (uniform)
+    const int row0 = second ? g.m0 - a.m2 : g.m0;     // first A row of an unmapped tile
+    a_rs = second ? a_rs2 : a_rs1;
 #pragma unroll
     for (int i = 0; i < S::A_PER; ++i) {
       const int c = tid + S::NT * i, r = c >> 3;
-      int arow = g.m0 + r;
-      if (gather) {
+      int arow = row0 + r;
+      if (gather && !second) {
         const int rb = (wv * kWave + S::NT * i) >> 3;  // this wave's first row of load i
         arow = select8(scalar_buffer_load32(map_rs, static_cast<uint32_t>(g.m0 + rb) * 4), l >> 3);
       }
@@ -281,7 +290,8 @@ void grouped_gemm_kernel(GemmArgs a) {
                                              (((c & 7) ^ (r & 7)) << 4))
                      : kOob;
     }
-    const uint8_t* bg = static_cast<const uint8_t*>(a.B) + g.group * a.b_group_stride;
+    const uint8_t* bg = second ? static_cast<const uint8_t*>(a.B2)
+                               : static_cast<const uint8_t*>(a.B) + g.group * a.b_group_stride;
     b_rs = rsrc_words(bg, static_cast<uint32_t>(static_cast<int64_t>(a.N) * ldb));
 #pragma unroll
     for (int i = 0; i < S::B_PER; ++i) {
@@ -308,11 +318,11 @@ void grouped_gemm_kernel(GemmArgs a) {
       const int kb_bytes = KB * 4;
       s_off = kOob;
       if (wv < S::ASW) {
-        const uint32_t a_rows = static_cast<uint32_t>(a.a_bytes / a.lda);
-        s_rs = rsrc_words(a.a_scales, a_rows * kb_bytes);
+        const uint32_t a_rows = static_cast<uint32_t>((second ? a.a2_bytes : a.a_bytes) / a.lda);
+        s_rs = rsrc_words(second ? a.a2_scales : a.a_scales, a_rows * kb_bytes);
         const int r = wv * 64 + l;
-        int arow = g.m0 + r;
-        if (gather) {
+        int arow = row0 + r;
+        if (gather && !second) {
 #pragma unroll
           for (int qd = 0; qd < 8; ++qd) {
             const i32x8 v = scalar_buffer_load32(map_rs, static_cast<uint32_t>(g.m0 + wv * 64 + 8 * qd) * 4);
@@ -327,11 +337,11 @@ void grouped_gemm_kernel(GemmArgs a) {
           // E8M0 scales [N, K/32] bytes per group, by column tile and step: column n0 + c's
           // four scales of a step are one dword at n0 * K/32 + 4 * c + BN * 4 * step
           const int kb32 = a.K / 32;
-          s_rs = rsrc_words(a.b_e8m0 + g.group * a.be_group_stride,
+          s_rs = rsrc_words(second ? a.b2_e8m0 : a.b_e8m0 + g.group * a.be_group_stride,
                             static_cast<uint32_t>(a.N) * kb32);
           s_off = static_cast<uint32_t>(g.n0) * kb32 + static_cast<uint32_t>(bw * 64 + l) * 4;
         } else {
-          s_rs = rsrc_words(a.b_scales + g.group * a.bs_group_stride,
+          s_rs = rsrc_words(second ? a.b2_scales : a.b_scales + g.group * a.bs_group_stride,
                             static_cast<uint32_t>((a.N / 16) * kb_bytes));
           if (l < BN / 16) s_off = static_cast<uint32_t>(g.n0 / 16 + l) * kb_bytes;
         }
@@ -673,11 +683,15 @@ void grouped_gemm_kernel(GemmArgs a) {
   auto epilogue = [&](int t) __attribute__((always_inline)) {
     // (uniform) the kept geometry, or the tile-list lookup when the issuing side is further on
     const TileGeo g = t == g_iss_t ? g_iss : t + 1 == g_iss_t ? g_prev : geo(t);
+    // the extra group stores to its own output, rows counted from its first row
+    const bool second = has2 && g.group == a.group2;
+    const int64_t ldo = second ? a.ldo2 : a.ldo;
+    const int orow0 = second ? g.m0 - a.m2 : g.m0;
     const __amdgpu_buffer_rsrc_t orsrc =
-        buffer_rsrc(static_cast<uint8_t*>(a.out) + static_cast<int64_t>(g.m0) * a.ldo,
-                    static_cast<uint32_t>(g.rows * a.ldo));
+        buffer_rsrc(static_cast<uint8_t*>(second ? a.out2 : a.out) + static_cast<int64_t>(orow0) * ldo,
+                    static_cast<uint32_t>(g.rows * ldo));
     if constexpr (EPI == kEpiStore) {
-      const bool f32o = a.out_f32 != 0;
+      const bool f32o = (second ? a.out2_f32 : a.out_f32) != 0;
 #pragma unroll
       for (int i = 0; i < S::FM; ++i)
 #pragma unroll
@@ -685,9 +699,9 @@ void grouped_gemm_kernel(GemmArgs a) {
           const int row = srow + i * 16;
           const int col = g.n0 + wn * S::TN + j * 16 + scol;
           if (f32o) {
-            buffer_store16(orsrc, static_cast<uint32_t>(row * a.ldo + col * 4), xpose4(acc[i][j]));
+            buffer_store16(orsrc, static_cast<uint32_t>(row * ldo + col * 4), xpose4(acc[i][j]));
           } else {
-            buffer_store8(orsrc, static_cast<uint32_t>(row * a.ldo + col * 2),
+            buffer_store8(orsrc, static_cast<uint32_t>(row * ldo + col * 2),
                           xpose2(pack_bf16x4(acc[i][j])));
           }
         }
@@ -730,7 +744,7 @@ void grouped_gemm_kernel(GemmArgs a) {
           for (int w2 = 0; w2 < S::WN; ++w2) m = fmaxf(m, amax[row * S::WN + w2]);
           const float sc = m > 0.0f ? m / 448.0f : 1.0f;
           if (wn == 0 && kq == 0 && row < g.rows)
-            a.out_scales[static_cast<int64_t>(g.m0 + row) * groups + grp] = sc;
+            (second ? a.out2_scales : a.out_scales)[static_cast<int64_t>(orow0 + row) * groups + grp] = sc;
           // h / sc correctly rounded to fp32 without an fp32 division per value: the fp64
           // product h * RN64(1/sc) lies within 2^-52 (relative) of h / sc, and a quotient of two
           // fp32 numbers is never closer than about 2^-49 to an fp32 rounding midpoint, so
@@ -741,7 +755,7 @@ void grouped_gemm_kernel(GemmArgs a) {
           for (int p = 0; p < HP; ++p) {
             const float* v = hv[i][p];
             const uint32_t codes = e4m3x4(quo(v[0]), quo(v[1]), quo(v[2]), quo(v[3]));
-            buffer_store4(orsrc, static_cast<uint32_t>((srow + i * 16) * a.ldo + hc0 + p * 16 + scol),
+            buffer_store4(orsrc, static_cast<uint32_t>((srow + i * 16) * ldo + hc0 + p * 16 + scol),
                           xpose(codes));
           }
         }
@@ -756,9 +770,9 @@ void grouped_gemm_kernel(GemmArgs a) {
             // h is read once, by the down GEMM: non-temporal stores (measured on MI355X: the
             // softmax_bf16 gate/up 2-4% faster; no change elsewhere)
             if constexpr (DT == MOE_F32)
-              buffer_store16_nt(orsrc, static_cast<uint32_t>(row * a.ldo + col * 4), xpose4(v));
+              buffer_store16_nt(orsrc, static_cast<uint32_t>(row * ldo + col * 4), xpose4(v));
             else
-              buffer_store8_nt(orsrc, static_cast<uint32_t>(row * a.ldo + col * 2),
+              buffer_store8_nt(orsrc, static_cast<uint32_t>(row * ldo + col * 2),
                                xpose2(pack_bf16x4(v)));
           }
       }
@@ -868,18 +882,30 @@ static int persistent_grid(Kern kernel, int threads, int64_t max_blocks) {
   return static_cast<int>(g < kNumXcd ? kNumXcd : g);
 }
 
-template <int DT, int BM, int BN, int EPI, bool G>
-static hipError_t launch_one(const GemmArgs& a, int max_tiles, hipStream_t s) {
+template <int DT, int BM, int BN, int EPI, bool G, bool G2 = false>
+static hipError_t launch_kernel(const GemmArgs& a, int max_tiles, hipStream_t s) {
   // grouped: worst-case tile count from the caller; one group: exact, for this BM
   if (!G) max_tiles = (a.M + BM - 1) / BM;
   const int64_t nb = static_cast<int64_t>(max_tiles) * (a.N / BN);
   if (nb <= 0) return hipSuccess;
-  auto kernel = grouped_gemm_kernel<DT, BM, BN, EPI, G>;
+  auto kernel = grouped_gemm_kernel<DT, BM, BN, EPI, G, G2>;
   constexpr int threads = gemm_waves<DT, BN>() * kWave;
   const int grid = persistent_grid(kernel, threads, nb);
   if (grid < 0) return hipErrorInvalidDevice;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, s, a);
   return hipGetLastError();
+}
+
+// The extra group is instantiated for grouped launches of 16- and 32-row bf16 / E4M3 tiles
+// (decode-sized batches, the only ones that merge their shared experts).
+template <int DT, int BM, int BN, int EPI, bool G>
+static hipError_t launch_one(const GemmArgs& a, int max_tiles, hipStream_t s) {
+  if constexpr (G && BM <= 32 && DT != MOE_F32) {
+    if (a.has_group2) return launch_kernel<DT, BM, BN, EPI, G, true>(a, max_tiles, s);
+  } else {
+    if (a.has_group2) return hipErrorInvalidValue;
+  }
+  return launch_kernel<DT, BM, BN, EPI, G>(a, max_tiles, s);
 }
 
 template <int DT, int EPI, bool G>

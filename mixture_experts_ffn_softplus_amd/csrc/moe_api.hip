@@ -104,9 +104,21 @@ int shared_bm(const moe_config_t* c) {
   if (c->expert_dtype == MOE_F32) return gemm_bm(MOE_F32, kEpiSwiglu, 0);
   return gemm_bm(c->expert_dtype, kEpiSwiglu, c->num_tokens);
 }
+// The shared experts run as one extra group of the routed grouped GEMMs for decode-sized
+// batches (T <= 256, routed tiles of at most 32 rows, bf16 or E4M3 activations) when together
+// they are exactly as wide as a routed expert (S * f_s = f): their few rows then stream their
+// weights beside the routed experts' instead of in two launches of their own.  (Measured on
+// MI355X: decode_bf16 1.477 -> 1.423 ms, mxfp4_decode 0.538 -> 0.500 ms; at T = 4096 the shared
+// tiles are MFMA-bound and lengthened the routed gate/up by as much as their own launches took,
+// so larger batches keep them separate.)
+bool merge_shared(const moe_config_t* c) {
+  return c->num_shared > 0 && shared_width(c) == c->d_ff && c->num_tokens <= 256 &&
+         c->expert_dtype != MOE_F32 && routed_bm(c) <= 32;
+}
 int64_t routed_max_tiles(const moe_config_t* c) {
   int bm = routed_bm(c);
-  return (assignments(c) + bm - 1) / bm + c->num_experts;
+  return (assignments(c) + bm - 1) / bm + c->num_experts +
+         (merge_shared(c) ? (c->num_tokens + bm - 1) / bm : 0);
 }
 
 // The GEMMs read every operand through a buffer resource whose size and per-lane offsets are
@@ -318,16 +330,30 @@ void set_weight_scales(const moe_config_t* c, GemmArgs& g, const void* scales, i
   }
 }
 
+// The extra group's weights and their scales (the shared experts, packed like one routed expert).
+void set_group2_weights(const moe_config_t* c, GemmArgs& g, const void* wts, const void* scales) {
+  g.B2 = wts;
+  if (is_mx(c))
+    g.b2_e8m0 = static_cast<const uint8_t*>(scales);
+  else
+    g.b2_scales = static_cast<const float*>(scales);
+}
+
+// Routed experts; with_shared (and merge_shared) also the shared experts, as one extra group
+// whose h goes to the workspace's h_s and whose output rows to the fp32 shared output.
 hipError_t do_expert_ffn(const moe_config_t* c, const void* xa, const float* xs,
                          const int32_t* offsets, const int32_t* perm, const moe_weights_t* w,
-                         void* y, void* ws, hipStream_t s, hipEvent_t* ev = nullptr) {
+                         void* y, void* ws, hipStream_t s, hipEvent_t* ev = nullptr,
+                         bool with_shared = false) {
   const WsLayout L = ws_layout(c);
-  const int64_t A = assignments(c), d = c->d_model, f = c->d_ff;
+  const int64_t A = assignments(c), d = c->d_model, f = c->d_ff, T = c->num_tokens;
   const int hb = h_bytes(c);
   const int bm = routed_bm(c);
+  const bool ms = with_shared && merge_shared(c);
   int4* tiles = at<int4>(ws, L.tiles);
   int32_t* tcount = at<int32_t>(ws, L.tiles_count);
-  hipError_t e = launch_tile_list(offsets, c->num_experts, bm, tiles, tcount, s);
+  hipError_t e = launch_tile_list(offsets, c->num_experts, bm, ms ? static_cast<int>(T) : 0,
+                                  tiles, tcount, s);
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_TILED, s);
   if (e != hipSuccess) return e;
   const int max_tiles = static_cast<int>(routed_max_tiles(c));
@@ -352,6 +378,18 @@ hipError_t do_expert_ffn(const moe_config_t* c, const void* xa, const float* xs,
   g.out_scales = is_fp8(c) ? at<float>(ws, L.h_scales) : nullptr;
   // an expert whose rows fit one tile streams its weights past the caches
   g.b_stream = 1;
+  if (ms) {  // the shared experts: every token, in order, from the same activations
+    g.has_group2 = 1;
+    g.group2 = c->num_experts;
+    g.m2 = static_cast<int>(A);
+    g.A2 = xa;
+    g.a2_bytes = g.a_bytes;
+    g.a2_scales = xs;
+    set_group2_weights(c, g, w->ws_gate_up, w->ws_gate_up_scales);
+    g.out2 = at<uint8_t>(ws, L.hs);
+    g.ldo2 = f * hb;
+    g.out2_scales = is_fp8(c) ? at<float>(ws, L.hs_scales) : nullptr;
+  }
   e = launch_grouped_gemm(c->expert_dtype, kEpiSwiglu, bm, g, max_tiles, s);
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_GATE_UP, s);
   if (e != hipSuccess) return e;
@@ -375,6 +413,18 @@ hipError_t do_expert_ffn(const moe_config_t* c, const void* xa, const float* xs,
   h.ldo = d * y_bytes(c);
   h.out_f32 = y_bytes(c) == 4;
   h.b_stream = g.b_stream;
+  if (ms) {
+    h.has_group2 = 1;
+    h.group2 = c->num_experts;
+    h.m2 = static_cast<int>(A);
+    h.A2 = at<uint8_t>(ws, L.hs);
+    h.a2_bytes = T * f * hb;
+    h.a2_scales = is_fp8(c) ? at<float>(ws, L.hs_scales) : nullptr;
+    set_group2_weights(c, h, w->ws_down, w->ws_down_scales);
+    h.out2 = at<float>(ws, L.so);
+    h.ldo2 = d * 4;
+    h.out2_f32 = 1;
+  }
   e = launch_grouped_gemm(c->expert_dtype, kEpiStore, bm, h, max_tiles, s);
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_DOWN, s);
   return e;
@@ -417,9 +467,12 @@ hipError_t pack_mx(const moe_config_t* c, const moe_logical_weights_t* lw, void*
   return e;
 }
 
+// shared_done: the shared experts' fp32 output is already in the workspace (they ran as the
+// extra group of the routed GEMMs), so only the combine runs.
 hipError_t do_combine(const moe_config_t* c, const void* xa, const float* xs, const void* y,
                       const int32_t* inv, const float* tw, const moe_weights_t* w, void* out,
-                      void* ws, hipStream_t s, hipEvent_t* ev = nullptr) {
+                      void* ws, hipStream_t s, hipEvent_t* ev = nullptr,
+                      bool shared_done = false) {
   const WsLayout L = ws_layout(c);
   const int64_t T = c->num_tokens, d = c->d_model, F = shared_width(c);
   const int hb = h_bytes(c);
@@ -427,7 +480,10 @@ hipError_t do_combine(const moe_config_t* c, const void* xa, const float* xs, co
   const int max_tiles = static_cast<int>((T + bm - 1) / bm);
   hipError_t e = hipSuccess;
   float* shared_out = nullptr;
-  if (c->num_shared > 0) {
+  if (c->num_shared > 0 && shared_done) {
+    shared_out = at<float>(ws, L.so);
+    e = mark(ev, MOE_STAGE_SHARED_GATE_UP, s);
+  } else if (c->num_shared > 0) {
     GemmArgs g{};
     g.A = xa;
     g.lda = d * (is_fp8(c) ? 1 : act_bytes(c));
@@ -513,8 +569,10 @@ hipError_t forward(const moe_config_t* c, const void* x, const moe_weights_t* w,
     e = launch_permute(ids, c->num_tokens, c->top_k, c->num_experts, offsets, perm, inv,
                        at<int32_t>(ws, L.hist), s);
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_PERMUTED, s);
-  if (e == hipSuccess) e = do_expert_ffn(c, xa, xs, offsets, perm, w, y, ws, s, ev);
-  if (e == hipSuccess) e = do_combine(c, xa, xs, y, inv, tw, w, out, ws, s, ev);
+  // the shared experts join the routed GEMMs as one extra group when they fit (merge_shared)
+  const bool ms = merge_shared(c);
+  if (e == hipSuccess) e = do_expert_ffn(c, xa, xs, offsets, perm, w, y, ws, s, ev, ms);
+  if (e == hipSuccess) e = do_combine(c, xa, xs, y, inv, tw, w, out, ws, s, ev, ms);
   return e;
 }
 

@@ -43,7 +43,9 @@ int permute_num_chunks(int T, int k);
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
                           int32_t* perm_token, int32_t* inv_perm, int32_t* hist,
                           hipStream_t s);
-hipError_t launch_tile_list(const int32_t* offsets, int E, int bm, int4* tiles,
+// extra_rows > 0 appends group E: rows [offsets[E], offsets[E] + extra_rows) (the shared
+// experts' tokens, after the routed rows).
+hipError_t launch_tile_list(const int32_t* offsets, int E, int bm, int extra_rows, int4* tiles,
                             int32_t* tiles_count, hipStream_t s);
 
 // ---- grouped GEMMs (gemm.hip)
@@ -77,6 +79,23 @@ struct GemmArgs {
   int out_f32;                // store epilogue: fp32 rows (else bf16)
   // A rows repeat every a_steps K-steps when > 0 (0: no repeat)
   int a_steps;
+  // One extra group after the routed experts when has_group2 (group index group2): the shared
+  // experts, whose rows are the tokens in order.  Its rows [m2, m2 + rows) of the M space take
+  // A row (r - m2) of A2 (no a_map), the weights B2 (+ scales), and store to out2 (+ scales)
+  // with row stride ldo2 (fp32 rows when out2_f32, store epilogue).
+  int has_group2;
+  int group2;
+  int m2;
+  const void* A2;
+  int64_t a2_bytes;
+  const float* a2_scales;
+  const void* B2;
+  const float* b2_scales;
+  const uint8_t* b2_e8m0;
+  void* out2;
+  int64_t ldo2;
+  float* out2_scales;
+  int out2_f32;
 };
 
 // dtype: MOE_F32 / MOE_BF16 / MOE_FP8_E4M3 / MOE_MXFP4 (E4M3 activations, E2M1 weights).

@@ -140,10 +140,12 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
 // Device tile list of a grouped GEMM with row tile `bm`: tiles[i] = {group, first row,
 // rows | (index of the tile within its group << 8), row tiles of that group},
 // groups in order, tiles of a group in row order; tiles_count[0] = number of tiles.  The
-// GEMM grid is sized for the worst case (ceil(T*k/bm) + E tiles) and reads the real count,
-// so per-expert counts never travel to the host.
+// GEMM grid is sized for the worst case (ceil(T*k/bm) + E tiles, plus the extra group's) and
+// reads the real count, so per-expert counts never travel to the host.  extra_rows > 0 adds
+// group E over rows [offsets[E], offsets[E] + extra_rows).
 __global__ __launch_bounds__(1024) void tile_list_kernel(const int32_t* __restrict__ offsets,
-                                                         int E, int bm, int4* __restrict__ tiles,
+                                                         int E, int bm, int extra_rows,
+                                                         int4* __restrict__ tiles,
                                                          int32_t* __restrict__ tiles_count) {
   __shared__ int s_tot[kWave + 1];
   int total = 0;
@@ -166,7 +168,13 @@ __global__ __launch_bounds__(1024) void tile_list_kernel(const int32_t* __restri
     carry += chunk_total;
   }
   total = carry;
-  if (threadIdx.x == 0) tiles_count[0] = total;
+  const int nt2 = (extra_rows + bm - 1) / bm;
+  const int r2 = offsets[E];
+  for (int i = threadIdx.x; i < nt2; i += blockDim.x) {
+    const int m0 = r2 + i * bm;
+    tiles[total + i] = int4{E, m0, min(bm, r2 + extra_rows - m0) | (i << 8), nt2};
+  }
+  if (threadIdx.x == 0) tiles_count[0] = total + nt2;
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
@@ -195,10 +203,10 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offs
   return hipGetLastError();
 }
 
-hipError_t launch_tile_list(const int32_t* offsets, int E, int bm, int4* tiles,
+hipError_t launch_tile_list(const int32_t* offsets, int E, int bm, int extra_rows, int4* tiles,
                             int32_t* tiles_count, hipStream_t s) {
-  hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm, tiles,
-                     tiles_count);
+  hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm, extra_rows,
+                     tiles, tiles_count);
   return hipGetLastError();
 }
 

@@ -104,6 +104,16 @@ SMALL = {
                                  d_ff_shared=128, score=SQRT_SOFTPLUS, renormalize=0,
                                  routed_scale=2.5, select_bias_range=0.1, shared_gate=1,
                                  seed=1011),
+    # decode-sized batches whose shared experts are as wide as a routed expert (S * f_s = f):
+    # moe_forward runs them as one extra group of the routed GEMMs (the split calls do not)
+    "bf16_decode_merged_shared": BF.with_(name="bf16_decode_merged_shared", num_tokens=48,
+                                          d_model=256, num_experts=32, top_k=4, d_ff=256,
+                                          num_shared=2, d_ff_shared=128, score=SQRT_SOFTPLUS,
+                                          routed_scale=2.5, select_bias_range=0.1,
+                                          shared_gate=1, seed=1012),
+    "bf16_decode_merged_one_tile": BF.with_(name="bf16_decode_merged_one_tile", num_tokens=13,
+                                            d_model=384, num_experts=40, top_k=3, d_ff=128,
+                                            num_shared=1, d_ff_shared=128, seed=1013),
 }
 
 
@@ -133,7 +143,11 @@ def test_fp8_activation_codes_bit_exact(name):
     assert np.array_equal(xq.cpu().numpy(), codes)
 
 
-@pytest.mark.parametrize("name", ["bf16_sqrt_softplus_zipf", "bf16_gated_shared"])
+# The split calls run the shared experts in launches of their own; moe_forward of the
+# decode-sized layers here runs them as an extra group of the routed GEMMs: the same bits.
+@pytest.mark.parametrize("name", ["bf16_sqrt_softplus_zipf", "bf16_gated_shared",
+                                  "bf16_decode_merged_shared", "bf16_decode_merged_one_tile",
+                                  "fp8_decode_rows", "mxfp4_decode_rows"])
 def test_split_api_matches_forward_bit_exact(name):
     cfg = SMALL[name]
     layer = Layer(cfg)
@@ -149,14 +163,19 @@ def test_split_api_matches_forward_bit_exact(name):
     y = torch.empty(A, d, dtype=api.y_dtype(cfg), device=dev)
     out = torch.empty(T, d, dtype=api.out_dtype(cfg), device=dev)
     x = layer.inp["x"]
-    api.moe_route(cfg, x, layer.w, logits, ids, w, ws=layer.ws)
+    xq = xs = None
+    if cfg.expert_dtype in (FP8_E4M3, MXFP4):  # block-scaled E4M3 activations from the router
+        xq = torch.empty(T, d, dtype=torch.uint8, device=dev)
+        xs = torch.empty(T, d // 128, dtype=torch.float32, device=dev)
+    api.moe_route(cfg, x, layer.w, logits, ids, w, xq, xs, ws=layer.ws)
     # route_from_logits on the same logits gives the same ids and weights
     ids2 = torch.empty_like(ids)
     w2 = torch.empty_like(w)
     api.moe_route_from_logits(cfg, logits, layer.inp["select_bias"], ids2, w2)
     api.moe_permute(cfg, ids, off, perm, inv, layer.ws)
-    api.moe_expert_ffn(cfg, x, None, off, perm, layer.w, y, layer.ws)
-    api.moe_combine(cfg, x, None, y, inv, w, layer.w, out, layer.ws)
+    xa = x if xq is None else xq
+    api.moe_expert_ffn(cfg, xa, xs, off, perm, layer.w, y, layer.ws)
+    api.moe_combine(cfg, xa, xs, y, inv, w, layer.w, out, layer.ws)
     torch.cuda.synchronize()
     assert torch.equal(ids, ids2) and torch.equal(w, w2)
     assert torch.equal(out, out_f)
