@@ -692,6 +692,12 @@ void grouped_gemm_kernel(GemmArgs a) {
                     static_cast<uint32_t>(g.rows * ldo));
     if constexpr (EPI == kEpiStore) {
       const bool f32o = (second ? a.out2_f32 : a.out_f32) != 0;
+      // Rows of an expert whose rows fit one tile (the y_perm of weight-streaming experts) are
+      // stored non-temporally: measured on MI355X, softmax_bf16's combine, which reads them,
+      // 0.236 -> 0.216 ms.  Multi-tile experts keep the default policy (all-non-temporal y_perm
+      // stores made the fp8_block down GEMM 35% slower), and so do the E4M3-activation kernels,
+      // whose registers the extra store path costs (fp8_block down +4%).
+      const bool nt_out = !S::kFp8 && GROUPED && g.count == 1;
 #pragma unroll
       for (int i = 0; i < S::FM; ++i)
 #pragma unroll
@@ -699,10 +705,17 @@ void grouped_gemm_kernel(GemmArgs a) {
           const int row = srow + i * 16;
           const int col = g.n0 + wn * S::TN + j * 16 + scol;
           if (f32o) {
-            buffer_store16(orsrc, static_cast<uint32_t>(row * ldo + col * 4), xpose4(acc[i][j]));
+            const uint32_t off = static_cast<uint32_t>(row * ldo + col * 4);
+            if (nt_out)
+              buffer_store16_nt(orsrc, off, xpose4(acc[i][j]));
+            else
+              buffer_store16(orsrc, off, xpose4(acc[i][j]));
           } else {
-            buffer_store8(orsrc, static_cast<uint32_t>(row * ldo + col * 2),
-                          xpose2(pack_bf16x4(acc[i][j])));
+            const uint32_t off = static_cast<uint32_t>(row * ldo + col * 2);
+            if (nt_out)
+              buffer_store8_nt(orsrc, off, xpose2(pack_bf16x4(acc[i][j])));
+            else
+              buffer_store8(orsrc, off, xpose2(pack_bf16x4(acc[i][j])));
           }
         }
     } else {
