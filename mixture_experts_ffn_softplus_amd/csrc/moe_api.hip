@@ -344,7 +344,7 @@ void set_group2_weights(const moe_config_t* c, GemmArgs& g, const void* wts, con
 hipError_t do_expert_ffn(const moe_config_t* c, const void* xa, const float* xs,
                          const int32_t* offsets, const int32_t* perm, const moe_weights_t* w,
                          void* y, void* ws, hipStream_t s, hipEvent_t* ev = nullptr,
-                         bool with_shared = false) {
+                         bool with_shared = false, bool tiles_ready = false) {
   const WsLayout L = ws_layout(c);
   const int64_t A = assignments(c), d = c->d_model, f = c->d_ff, T = c->num_tokens;
   const int hb = h_bytes(c);
@@ -352,8 +352,10 @@ hipError_t do_expert_ffn(const moe_config_t* c, const void* xa, const float* xs,
   const bool ms = with_shared && merge_shared(c);
   int4* tiles = at<int4>(ws, L.tiles);
   int32_t* tcount = at<int32_t>(ws, L.tiles_count);
-  hipError_t e = launch_tile_list(offsets, c->num_experts, bm, ms ? static_cast<int>(T) : 0,
-                                  tiles, tcount, s);
+  // (tiles_ready: the one-workgroup permutation of a small batch has written the tile list)
+  hipError_t e = tiles_ready ? hipSuccess
+                             : launch_tile_list(offsets, c->num_experts, bm,
+                                                ms ? static_cast<int>(T) : 0, tiles, tcount, s);
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_TILED, s);
   if (e != hipSuccess) return e;
   const int max_tiles = static_cast<int>(routed_max_tiles(c));
@@ -565,13 +567,19 @@ hipError_t forward(const moe_config_t* c, const void* x, const moe_weights_t* w,
   hipError_t e = mark(ev, MOE_STAGE_BEGIN, s);
   if (e == hipSuccess) e = do_route(c, x, w, d.logits, ids, tw, xq, xs, ws, s);
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_ROUTED, s);
-  if (e == hipSuccess)
+  // the shared experts join the routed GEMMs as one extra group when they fit (merge_shared)
+  const bool ms = merge_shared(c);
+  // a small batch is permuted, and its tile list built, by one workgroup
+  const bool small = permute_small_ok(assignments(c), c->num_experts);
+  if (e == hipSuccess && small)
+    e = launch_permute_small(ids, c->num_tokens, c->top_k, c->num_experts, offsets, perm, inv,
+                             routed_bm(c), ms ? c->num_tokens : 0, at<int4>(ws, L.tiles),
+                             at<int32_t>(ws, L.tiles_count), s);
+  else if (e == hipSuccess)
     e = launch_permute(ids, c->num_tokens, c->top_k, c->num_experts, offsets, perm, inv,
                        at<int32_t>(ws, L.hist), s);
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_PERMUTED, s);
-  // the shared experts join the routed GEMMs as one extra group when they fit (merge_shared)
-  const bool ms = merge_shared(c);
-  if (e == hipSuccess) e = do_expert_ffn(c, xa, xs, offsets, perm, w, y, ws, s, ev, ms);
+  if (e == hipSuccess) e = do_expert_ffn(c, xa, xs, offsets, perm, w, y, ws, s, ev, ms, small);
   if (e == hipSuccess) e = do_combine(c, xa, xs, y, inv, tw, w, out, ws, s, ev, ms);
   return e;
 }
@@ -738,6 +746,9 @@ moe_status_t moe_permute(const moe_config_t* c, const int32_t* ids, int32_t* off
   if ((st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
   if (c->num_tokens == 0) return MOE_OK;
   const WsLayout L = ws_layout(c);
+  if (permute_small_ok(assignments(c), c->num_experts))
+    return hip_status(launch_permute_small(ids, c->num_tokens, c->top_k, c->num_experts, offsets,
+                                           perm, inv, 0, 0, nullptr, nullptr, s));
   return hip_status(launch_permute(ids, c->num_tokens, c->top_k, c->num_experts, offsets, perm,
                                    inv, at<int32_t>(ws, L.hist), s));
 }

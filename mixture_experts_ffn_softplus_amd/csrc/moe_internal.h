@@ -43,6 +43,12 @@ int permute_num_chunks(int T, int k);
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
                           int32_t* perm_token, int32_t* inv_perm, int32_t* hist,
                           hipStream_t s);
+// The permutation and (when tiles is set) the tile list in one workgroup, for small batches:
+// permute_small_ok(T * k, E).  Same outputs as launch_permute + launch_tile_list.
+bool permute_small_ok(int64_t A, int E);
+hipError_t launch_permute_small(const int32_t* ids, int T, int k, int E, int32_t* offsets,
+                                int32_t* perm_token, int32_t* inv_perm, int bm, int extra_rows,
+                                int4* tiles, int32_t* tiles_count, hipStream_t s);
 // extra_rows > 0 appends group E: rows [offsets[E], offsets[E] + extra_rows) (the shared
 // experts' tokens, after the routed rows).
 hipError_t launch_tile_list(const int32_t* offsets, int E, int bm, int extra_rows, int4* tiles,

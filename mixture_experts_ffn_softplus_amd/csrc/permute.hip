@@ -142,11 +142,10 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
 // groups in order, tiles of a group in row order; tiles_count[0] = number of tiles.  The
 // GEMM grid is sized for the worst case (ceil(T*k/bm) + E tiles, plus the extra group's) and
 // reads the real count, so per-expert counts never travel to the host.  extra_rows > 0 adds
-// group E over rows [offsets[E], offsets[E] + extra_rows).
-__global__ __launch_bounds__(1024) void tile_list_kernel(const int32_t* __restrict__ offsets,
-                                                         int E, int bm, int extra_rows,
-                                                         int4* __restrict__ tiles,
-                                                         int32_t* __restrict__ tiles_count) {
+// group E over rows [offsets[E], offsets[E] + extra_rows).  Run by one whole workgroup;
+// `offsets` [E+1] may live in global memory or in LDS.
+__device__ void build_tile_list(const int32_t* offsets, int E, int bm, int extra_rows,
+                                int4* __restrict__ tiles, int32_t* __restrict__ tiles_count) {
   __shared__ int s_tot[kWave + 1];
   int total = 0;
   int carry = 0;
@@ -177,6 +176,94 @@ __global__ __launch_bounds__(1024) void tile_list_kernel(const int32_t* __restri
   if (threadIdx.x == 0) tiles_count[0] = total + nt2;
 }
 
+__global__ __launch_bounds__(1024) void tile_list_kernel(const int32_t* __restrict__ offsets,
+                                                         int E, int bm, int extra_rows,
+                                                         int4* __restrict__ tiles,
+                                                         int32_t* __restrict__ tiles_count) {
+  build_tile_list(offsets, E, bm, extra_rows, tiles, tiles_count);
+}
+
+// The whole permutation in one workgroup for small batches (A <= kSmallA assignments,
+// E <= kSmallE experts; decode shapes), and the tile list with it: the same stable counting
+// sort as the multi-kernel path, one round of 1024 assignments at a time -- each wave ranks its
+// 64 assignments among equal experts in lower lanes with ballots, the waves' per-expert counts
+// (summed in wave order through LDS) and the experts' counts of the earlier rounds place every
+// assignment.  No atomics decide any order.
+constexpr int kSmallThreads = 1024, kSmallWaves = kSmallThreads / kWave;
+constexpr int kSmallRounds = 4, kSmallA = kSmallThreads * kSmallRounds, kSmallE = 768;
+__global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
+    const int32_t* __restrict__ ids, int A, int k, int E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm_token, int32_t* __restrict__ inv_perm, int bm, int extra_rows,
+    int4* __restrict__ tiles, int32_t* __restrict__ tiles_count) {
+  extern __shared__ int sm[];
+  int* s_run = sm;                       // [E] assignments to each expert so far
+  int* s_off = sm + E;                   // [E + 1] expert offsets
+  int* s_wave = sm + 2 * E + 1;          // [kSmallWaves][E] this round's per-wave counts
+  __shared__ int s_tot[kWave + 1];
+  const int tid = threadIdx.x, l = lane_id(), wv = tid / kWave;
+  const uint64_t lt_mask = (l == 0) ? 0ull : (~0ull >> (kWave - l));
+  for (int e = tid; e < E; e += kSmallThreads) s_run[e] = 0;
+  int my_e[kSmallRounds], my_rank[kSmallRounds];
+#pragma unroll
+  for (int r = 0; r < kSmallRounds; ++r) {
+    my_e[r] = -1;
+    my_rank[r] = 0;
+    if (r * kSmallThreads >= A) continue;  // uniform
+    for (int i = tid; i < kSmallWaves * E; i += kSmallThreads) s_wave[i] = 0;
+    __syncthreads();
+    const int a = r * kSmallThreads + tid;
+    const bool valid = a < A;
+    const int e = valid ? ids[a] : -1;
+    uint64_t remaining = __ballot(valid);
+    uint64_t peers = 0;
+    while (remaining) {
+      const int leader = __ffsll(static_cast<unsigned long long>(remaining)) - 1;
+      const int le = __shfl(e, leader, kWave);
+      const uint64_t m = __ballot(valid && e == le);
+      if (valid && e == le) peers = m;
+      remaining &= ~m;
+    }
+    const int rank = __popcll(peers & lt_mask), cnt = __popcll(peers);
+    if (valid && rank == cnt - 1) s_wave[wv * E + e] = cnt;
+    __syncthreads();
+    if (valid) {
+      int pos = s_run[e] + rank;
+      for (int w = 0; w < wv; ++w) pos += s_wave[w * E + e];
+      my_e[r] = e;
+      my_rank[r] = pos;
+    }
+    __syncthreads();
+    for (int e2 = tid; e2 < E; e2 += kSmallThreads) {
+      int sum = 0;
+      for (int w = 0; w < kSmallWaves; ++w) sum += s_wave[w * E + e2];
+      s_run[e2] += sum;
+    }
+    __syncthreads();
+  }
+  // expert offsets: exclusive scan of the counts (E <= kSmallThreads: one pass)
+  int total;
+  const int off = block_exclusive_scan(tid < E ? s_run[tid] : 0, s_tot, &total);
+  if (tid < E) {
+    offsets[tid] = off;
+    s_off[tid] = off;
+  }
+  if (tid == 0) {
+    offsets[E] = A;
+    s_off[E] = A;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kSmallRounds; ++r) {
+    if (my_e[r] >= 0) {
+      const int a = r * kSmallThreads + tid;
+      const int pos = s_off[my_e[r]] + my_rank[r];
+      perm_token[pos] = a / k;
+      inv_perm[a] = pos;
+    }
+  }
+  if (tiles) build_tile_list(s_off, E, bm, extra_rows, tiles, tiles_count);
+}
+
 __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -200,6 +287,20 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offs
   hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(1024), 0, s, counts, E, A, offsets);
   hipLaunchKernelGGL(scatter_kernel, dim3(chunks), dim3(kChunk), sizeof(int) * 5 * E, s, ids, A,
                      k, E, chunks, offsets, hist, perm_token, inv_perm);
+  return hipGetLastError();
+}
+
+bool permute_small_ok(int64_t A, int E) { return A >= 1 && A <= kSmallA && E <= kSmallE; }
+
+hipError_t launch_permute_small(const int32_t* ids, int T, int k, int E, int32_t* offsets,
+                                int32_t* perm_token, int32_t* inv_perm, int bm, int extra_rows,
+                                int4* tiles, int32_t* tiles_count, hipStream_t s) {
+  const int64_t A = static_cast<int64_t>(T) * k;
+  if (!permute_small_ok(A, E)) return hipErrorInvalidValue;
+  const size_t lds = sizeof(int) * (2 * E + 1 + kSmallWaves * E);
+  hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kSmallThreads), lds, s, ids,
+                     static_cast<int>(A), k, E, offsets, perm_token, inv_perm, bm, extra_rows,
+                     tiles, tiles_count);
   return hipGetLastError();
 }
 
