@@ -226,9 +226,15 @@ def test_route_from_logits_with_ties_bit_exact():
         assert np.max(np.abs(w.cpu().double().numpy() - w_ref)) <= 1e-6 * max(gamma, 1)
 
 
+# Batches of at most 4096 assignments over at most 768 experts are permuted by one workgroup
+# (rounds of 1024 assignments), larger ones by the multi-kernel counting sort: both sides of
+# each limit are here, with one expert taking every assignment across all four rounds.
 @pytest.mark.parametrize("T,k,E,mode", [(4096, 10, 512, "uniform"), (1000, 3, 64, "skewed"),
                                         (3, 2, 1000, "uniform"), (1, 1, 1, "uniform"),
-                                        (16384, 22, 896, "uniform"), (513, 4, 300, "one_hot")])
+                                        (16384, 22, 896, "uniform"), (513, 4, 300, "one_hot"),
+                                        (1024, 4, 768, "uniform"), (1365, 3, 768, "uniform"),
+                                        (1024, 4, 769, "uniform"), (683, 6, 300, "uniform"),
+                                        (4096, 1, 700, "one_hot"), (64, 8, 256, "uniform")])
 def test_permute_external_ids_bit_exact(T, k, E, mode):
     rng = np.random.default_rng(T + k + E)
     if mode == "uniform":
