@@ -184,6 +184,9 @@ __device__ void quant_row_fp8(const RouteArgs& a, int t) {
   const int l = lane_id(), sub = l & 15, groups = a.d / 128;
   const uint16_t* xr = a.x + static_cast<size_t>(t) * a.d;
   uint8_t* qr = a.xq + static_cast<size_t>(t) * a.d;
+  // (unrolled so that several iterations' loads are in flight: a decode batch has only a few
+  // dozen such waves on the whole GPU)
+#pragma unroll 4
   for (int g0 = 0; g0 < groups; g0 += 4) {
     const int grp = g0 + (l >> 4);
     const bool valid = grp < groups;  // whole 16-lane groups
