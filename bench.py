@@ -282,31 +282,53 @@ def cpu_info():
 
 
 class SclkSampler:
-    """Samples the GPU's current shader clock (rocm-smi) from a thread while a loop of forwards
-    runs; null where rocm-smi is unavailable."""
+    """Samples the GPU's shader clocks (amd-smi: one per XCD; else rocm-smi) from a thread while
+    a loop of forwards runs; None where neither tool reports them."""
 
     def __init__(self):
         import threading
-        self.samples, self.stop, self.err = [], threading.Event(), None
+        self.samples, self.stop, self.err, self.tool = [], threading.Event(), None, None
         self.t = threading.Thread(target=self._run, daemon=True)
 
-    def _run(self):
+    @staticmethod
+    def _amd_smi():
+        import subprocess
+        r = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True, text=True,
+                           timeout=10)
+        data = json.loads(r.stdout)
+        gpus = data.get("gpu_data", data) if isinstance(data, dict) else data
+        clocks = gpus[0]["clock"]
+        return [float(v["clk"]["value"]) for k, v in clocks.items() if k.startswith("gfx_")]
+
+    @staticmethod
+    def _rocm_smi():
         import re
         import subprocess
+        r = subprocess.run(["rocm-smi", "--showgpuclocks", "--json"], capture_output=True,
+                           text=True, timeout=10)
+        out = []
+        for card in json.loads(r.stdout[r.stdout.index("{"):]).values():
+            for key, val in card.items():
+                m = re.search(r"(\d+)\s*mhz", str(val).lower())
+                if "sclk" in key.lower() and m:
+                    out.append(float(m.group(1)))
+        return out
+
+    def _run(self):
         while not self.stop.is_set():
-            try:
-                r = subprocess.run(["rocm-smi", "--showgpuclocks", "--json"], capture_output=True,
-                                   text=True, timeout=5)
-                for card in json.loads(r.stdout).values():
-                    for key, val in card.items():
-                        if "sclk" in key.lower() and "speed" in key.lower():
-                            m = re.search(r"(\d+)\s*mhz", str(val).lower())
-                            if m:
-                                self.samples.append(int(m.group(1)))
-            except Exception as e:  # noqa: BLE001 -- a missing tool only loses the figure
-                self.err = repr(e)
-                return
-            self.stop.wait(0.2)
+            got = None
+            for name, fn in (("amd-smi", self._amd_smi), ("rocm-smi", self._rocm_smi)):
+                try:
+                    got = fn()
+                except Exception as e:  # noqa: BLE001 -- a missing tool only loses the figure
+                    self.err = f"{name}: {e!r}"[:200]
+                    continue
+                if got:
+                    self.tool = name
+                    break
+            if got:
+                self.samples.append(sum(got) / len(got))
+            self.stop.wait(0.1)
 
     def __enter__(self):
         self.t.start()
@@ -314,14 +336,16 @@ class SclkSampler:
 
     def __exit__(self, *a):
         self.stop.set()
-        self.t.join(timeout=10)
+        self.t.join(timeout=30)
 
     def result(self):
-        busy = sorted(self.samples)
-        if not busy:
-            return None
-        return {"median_mhz": busy[len(busy) // 2], "max_mhz": busy[-1], "samples": len(busy),
-                "how": "rocm-smi --showgpuclocks every 0.2 s during untimed forwards"}
+        if not self.samples:
+            return {"error": self.err}
+        v = sorted(self.samples)
+        return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1],
+                "samples": len(v),
+                "how": f"{self.tool}, mean over the XCDs' shader clocks, sampled during about "
+                       f"3 s of untimed forwards"}
 
 
 def run_workload(cfg, steps, warmup, dev, keep=False):
@@ -494,14 +518,14 @@ def main():
 
     sclk = None
     if not args.only:
-        # the shader clock under this workload: sampled during about 2 s of untimed forwards
+        # the shader clock under this workload: sampled during about 3 s of untimed forwards
         with SclkSampler() as smp:
-            t_end = time.perf_counter() + 2.0
+            t_end = time.perf_counter() + 3.0
             while time.perf_counter() < t_end:
                 for _ in range(20):
                     api.moe_forward(cfg, x, w, out, ws)
                 torch.cuda.synchronize()
-        sclk = smp.result() if smp.samples else {"error": smp.err}
+        sclk = smp.result()
 
     cpu = parity = None
     if not args.no_cpu_baseline:
