@@ -348,10 +348,10 @@ class SclkSampler:
                        f"3 s of untimed forwards"}
 
 
-def run_workload(cfg, steps, warmup, dev, keep=False):
+def run_workload(cfg, steps, warmup, dev, keep=False, sample_clock=True):
     """Pack one workload, run `warmup` untimed and `steps` timed forwards with a HIP event at
-    every stage boundary, and return its record (and, with keep, the objects a parity check
-    needs)."""
+    every stage boundary, sample the shader clock during about 3 s of further untimed forwards
+    (sample_clock), and return its record (and, with keep, the objects a parity check needs)."""
     import torch
 
     from mixture_experts_ffn_softplus_amd import api, profiling, synth
@@ -444,6 +444,15 @@ def run_workload(cfg, steps, warmup, dev, keep=False):
            "step_ms_min": round(step_times[0], 5), "dtype": DTYPE_NAME[cfg.expert_dtype],
            "config": config_record(cfg), "roofline": roofline, "step_roofline": step,
            "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()}}
+    if sample_clock:
+        # the shader clock under this workload (untimed; the clock follows the MFMA load)
+        with SclkSampler() as smp:
+            t_end = time.perf_counter() + 3.0
+            while time.perf_counter() < t_end:
+                for _ in range(max(1, int(50.0 / ms))):  # about 50 ms per batch
+                    api.moe_forward(cfg, x, w, out, ws)
+                torch.cuda.synchronize()
+        rec["sclk_under_load"] = smp.result()
     ctx = None
     if keep:
         ctx = {"inp": inp, "out": out, "logits": logits, "w": w, "ws": ws, "pw": pw}
@@ -507,7 +516,8 @@ def main():
     cfg = PRESETS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    rec, ctx = run_workload(cfg, args.steps, args.warmup, dev, keep=True)
+    rec, ctx = run_workload(cfg, args.steps, args.warmup, dev, keep=True,
+                            sample_clock=not args.only)
     x, w, ws, out = ctx["inp"]["x"], ctx["w"], ctx["ws"], ctx["out"]
 
     extra = {}
@@ -515,17 +525,6 @@ def main():
         extra["hash_routing"] = time_hash_routing(cfg, x, w, ws, args.steps, args.warmup)
     if args.bias_update:
         extra["bias_update"] = time_bias_update(cfg, x, w, out, ws, args.steps, args.warmup)
-
-    sclk = None
-    if not args.only:
-        # the shader clock under this workload: sampled during about 3 s of untimed forwards
-        with SclkSampler() as smp:
-            t_end = time.perf_counter() + 3.0
-            while time.perf_counter() < t_end:
-                for _ in range(20):
-                    api.moe_forward(cfg, x, w, out, ws)
-                torch.cuda.synchronize()
-        sclk = smp.result()
 
     cpu = parity = None
     if not args.no_cpu_baseline:
@@ -553,7 +552,8 @@ def main():
         "stage_ms": rec["stage_ms"], "cpu_baseline": cpu, "parity": parity,
         "workloads": {cfg.name: {k: rec[k] for k in ("ms_per_step", "tokens_per_s", "dtype")}
                       | {"step_roofline": rec["step_roofline"]}} | others,
-        "gpu": gpu_info(dev) | {"sclk_under_load": sclk}, "host_cpu": cpu_info(),
+        "gpu": gpu_info(dev) | {"sclk_under_load": rec.get("sclk_under_load")},
+        "host_cpu": cpu_info(),
     }
     result.update(extra)
     print(json.dumps(result), flush=True)
