@@ -231,7 +231,7 @@ MOE_API moe_status_t moe_route(const moe_config_t* cfg, const void* x, const moe
                        float* logits, int32_t* topk_ids, float* topk_w, void* xq,
                        float* xq_scales, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* moe_route for the layers that choose their experts by a fixed token-id hash
+/* moe_route for the layers whose experts a hash of the token id fixes
  * (router row, DeepSeek-V4-Pro cell: the first three MoE layers).  The hash is
  * a caller-owned table [vocab, k] of expert ids: topk_ids[t] =
  * hash_table[token_ids[t]] in the table's slot order, and topk_w[t] are the

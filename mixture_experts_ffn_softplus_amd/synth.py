@@ -26,7 +26,7 @@ Recipe (all logical layouts row-major):
   when the workload gates its shared experts.
 * Load skew: logit bias z_e = ln p_e - mean(ln p), p_e proportional to
   (e + 1)^-s, expert 0 hottest (fp32).
-* Routing by a fixed token-id hash: a table [vocab, k] of k distinct expert ids
+* Hash routing (experts fixed by the token id): a table [vocab, k] of k distinct expert ids
   per token id (the first k of a seeded random permutation of the experts for
   each row), vocab 131072 (the low end of the pages' 128K-262K tokenizers), and
   token ids drawn with Zipf frequencies p(rank r) proportional to 1/r, as word
@@ -218,7 +218,7 @@ HASH_VOCAB = 131072
 
 
 def hash_routing(cfg: MoEConfig, device="cpu", vocab: int = HASH_VOCAB, zipf_s: float = 1.0):
-    """(token_ids int32 [T], table int32 [vocab, k]) for routing by a fixed token-id hash."""
+    """(token_ids int32 [T], table int32 [vocab, k]) for hash routing (experts fixed by the token id)."""
     g = _gen(device, cfg.seed, TAG_HASH_TABLE)
     keys = torch.rand((vocab, cfg.num_experts), generator=g, device=device)
     table = keys.argsort(dim=1)[:, :cfg.top_k].to(torch.int32).contiguous()

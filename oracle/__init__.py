@@ -9,15 +9,16 @@ arrays into it.
 What it computes, and the passages it follows (archdiff.com comparison pages):
 
 * ``router_logits`` -- "Qwen3.5-397B-A17B vs DeepSeek-V4-Pro", component
-  table, router row, Qwen3.5 cell: a linear router scores the experts.
+  table, router row, Qwen3.5 cell: each expert's logit is a linear function
+  of the token vector, x . W_r.
 * ``route`` -- same row: softmax, top-k, renormalise, no selection bias
   (Qwen3.5 cell); sqrt-softplus affinities with a selection-only per-expert
   bias, selected scores normalised and scaled by 2.5 (DeepSeek-V4-Pro cell);
   the blueprint router box (sigma or sqrt-softplus, balanced by a bias) for the
   sigmoid score.  Ties at the top-k boundary go to the lower expert index
   (the pages are silent; this is the reading taken).
-* ``route_hashed`` -- same row, DeepSeek-V4-Pro cell: the first three MoE
-  layers choose experts by a fixed token-id hash.  Read as a fixed table of k
+* ``route_hashed`` -- same row, DeepSeek-V4-Pro cell: in its first three
+  MoE layers a fixed hash of the token id, not the router, picks the experts.  Read as a fixed table of k
   expert ids per token id; the combine weights stay the router's (the same
   formulas as ``route``, on the table's experts).
 * ``bias_update`` -- same cell: auxiliary-loss-free balancing with bias speed

@@ -1,7 +1,7 @@
 """Pins of the oracle's hash routing and bias-balancing step.
 
 Passage: "Qwen3.5-397B-A17B vs DeepSeek-V4-Pro", component table, router row, DeepSeek-V4-Pro
-cell.  The first three MoE layers choose experts by a fixed token-id hash; the other layers
+cell.  In the first three MoE layers a hash of the token id fixes the experts; the other layers
 balance the experts without an auxiliary loss, with a bias speed of 0.001.
 
 Readings (the pages give no more than that):
