@@ -20,7 +20,6 @@
 
 namespace moe {
 
-
 // Score of the sigma family, evaluated in fp64 and rounded once to fp32, so the
 // selection key is one fixed fp32 number.
 __device__ __forceinline__ float sigma_family_score(int score, float l) {
@@ -44,31 +43,25 @@ __device__ __forceinline__ uint64_t select_key(float key, int e) {
   return (static_cast<uint64_t>(u) << 32) | static_cast<uint32_t>(~e);
 }
 
-// max(v, v moved by one DPP lane pattern) over the 64-bit key; lanes outside ROW_MASK, or
-// whose source lane is out of range, see 0.
+// max(v, v moved by one DPP lane pattern) over 32-bit unsigned values; lanes outside ROW_MASK,
+// or whose source lane is out of range, see 0.  The wave's maximum, wave-uniform: within each
+// row of 16 lanes by quad swaps and the half-row and row mirrors, across rows by the row
+// broadcasts into lane 63; the minimum as the maximum of complements.
 template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ uint64_t dpp_max(uint64_t v) {
-  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(v), CTRL, ROW_MASK,
-                                                  0xF, false);
-  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(v >> 32), CTRL,
-                                                  ROW_MASK, 0xF, false);
-  const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+__device__ __forceinline__ uint32_t dpp_max32(uint32_t v) {
+  const uint32_t o = __builtin_amdgcn_update_dpp(0u, v, CTRL, ROW_MASK, 0xF, false);
   return o > v ? o : v;
 }
-
-// The wave's largest key, wave-uniform: within each row of 16 lanes by quad swaps and the
-// half-row and row mirrors, across rows by the row broadcasts into lane 63.
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
-  v = dpp_max<0xB1>(v);         // quad_perm [1,0,3,2]
-  v = dpp_max<0x4E>(v);         // quad_perm [2,3,0,1]
-  v = dpp_max<0x141>(v);        // row_half_mirror
-  v = dpp_max<0x140>(v);        // row_mirror
-  v = dpp_max<0x142, 0xA>(v);   // row_bcast15 into rows 1 and 3
-  v = dpp_max<0x143, 0xC>(v);   // row_bcast31 into rows 2 and 3
-  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), 63);
-  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), 63);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max32<0xB1>(v);        // quad_perm [1,0,3,2]
+  v = dpp_max32<0x4E>(v);        // quad_perm [2,3,0,1]
+  v = dpp_max32<0x141>(v);       // row_half_mirror
+  v = dpp_max32<0x140>(v);       // row_mirror
+  v = dpp_max32<0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
+  v = dpp_max32<0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3
+  return __builtin_amdgcn_readlane(v, 63);
 }
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
 
 // The lane's N keys sorted into descending order in registers (a bitonic network: the indices
 // are compile-time constants once unrolled, so nothing leaves the registers).
@@ -134,14 +127,35 @@ __device__ void topk_row(const float* row, int t, const RouteArgs& a) {
     }
   } else {
     sort_desc<SLOTS>(key);
-    // k rounds: the largest head wins, its lane drops it; lane j keeps the winner of round j
+    // The sorted keys split into their upper halves (the ordered fp32 keys; 0: no candidate)
+    // and, 4 bits a position, the slots i of the experts l + 64 i they belong to.  Within a
+    // lane equal keys are already in ascending expert order.
+    uint32_t hi[SLOTS];
+    uint64_t order = 0;
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      hi[i] = static_cast<uint32_t>(key[i] >> 32);
+      order |= static_cast<uint64_t>((~static_cast<uint32_t>(key[i]) >> 6) & 15u) << (4 * i);
+    }
+    // k rounds: the largest head wins (among equal heads the lowest expert id), its lane drops
+    // it; lane j keeps the winner of round j
     for (int j = 0; j < a.k; ++j) {
-      const uint64_t win = wave_max_key(key[0]);
-      const int we = static_cast<int>(~static_cast<uint32_t>(win));
+      const uint32_t m = wave_max_u32(hi[0]);
+      const uint64_t tied = __ballot(hi[0] == m);
+      int we;
+      if (__popcll(tied) == 1) {
+        const int wl = __ffsll(static_cast<unsigned long long>(tied)) - 1;
+        we = wl + kWave * static_cast<int>(
+                          __builtin_amdgcn_readlane(static_cast<uint32_t>(order), wl) & 15u);
+      } else {
+        const uint32_t id = static_cast<uint32_t>(l + kWave * static_cast<int>(order & 15u));
+        we = static_cast<int>(wave_min_u32(hi[0] == m ? id : 0xFFFFFFFFu));
+      }
       const bool mine = l == (we & (kWave - 1));
 #pragma unroll
-      for (int i = 0; i + 1 < SLOTS; ++i) key[i] = mine ? key[i + 1] : key[i];
-      key[SLOTS - 1] = mine ? 0 : key[SLOTS - 1];
+      for (int i = 0; i + 1 < SLOTS; ++i) hi[i] = mine ? hi[i + 1] : hi[i];
+      hi[SLOTS - 1] = mine ? 0u : hi[SLOTS - 1];
+      order = mine ? order >> 4 : order;
       if (l == j) my_id = we;
     }
   }
@@ -204,8 +218,13 @@ __device__ void quant_row_fp8(const RouteArgs& a, int t) {
 #pragma unroll
     for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
     const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
-    const uint32_t lo = e4m3x4(v[0] / sc, v[1] / sc, v[2] / sc, v[3] / sc);
-    const uint32_t hi = e4m3x4(v[4] / sc, v[5] / sc, v[6] / sc, v[7] / sc);
+    // v / sc correctly rounded to fp32 as RN32(v * RN64(1/sc)): the fp64 product is within
+    // 2^-52 (relative) of the quotient, and a quotient of two fp32 numbers is never within
+    // about 2^-49 of an fp32 rounding midpoint, so both round alike
+    const double rs = 1.0 / static_cast<double>(sc);
+    auto quo = [rs](float x) { return static_cast<float>(static_cast<double>(x) * rs); };
+    const uint32_t lo = e4m3x4(quo(v[0]), quo(v[1]), quo(v[2]), quo(v[3]));
+    const uint32_t hi = e4m3x4(quo(v[4]), quo(v[5]), quo(v[6]), quo(v[7]));
     if (valid) {
       *reinterpret_cast<uint2*>(qr + at) = uint2{lo, hi};
       if (sub == 0) a.xq_scales[static_cast<size_t>(t) * groups + grp] = sc;
@@ -264,6 +283,5 @@ hipError_t launch_bias_update(const int32_t* offsets, int E, float speed, float*
                      speed, bias);
   return hipGetLastError();
 }
-
 
 }  // namespace moe
