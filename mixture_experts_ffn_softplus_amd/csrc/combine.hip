@@ -92,7 +92,7 @@ __device__ float shared_gate(const CombineGate& g, int t, int d) {
 template <bool Y_F32, bool OUT_F32>
 __global__ __launch_bounds__(kCombineMaxThreads) void combine_kernel(
     const uint8_t* __restrict__ y, const int32_t* __restrict__ inv, const float* __restrict__ w,
-    int k, const float* __restrict__ base, CombineGate gate, uint8_t* __restrict__ out, int d) {
+    int k, const uint8_t* __restrict__ base, CombineGate gate, uint8_t* __restrict__ out, int d) {
   constexpr int ysz = Y_F32 ? 4 : 2, osz = OUT_F32 ? 4 : 2;
   __shared__ int32_t s_row[kCombineMaxK];
   __shared__ float s_w[kCombineMaxK];
@@ -110,15 +110,11 @@ __global__ __launch_bounds__(kCombineMaxThreads) void combine_kernel(
   for (int c = threadIdx.x; c < d / 8; c += blockDim.x) {
     float v[8];
     if (base) {
-      const f32x4* b = reinterpret_cast<const f32x4*>(base + static_cast<int64_t>(t) * d + c * 8);
-      // read once as well: non-temporal with the bf16 rows (FP8 experts), as measured above
-      const f32x4 b0 = Y_F32 ? b[0] : __builtin_nontemporal_load(b);
-      const f32x4 b1 = Y_F32 ? b[1] : __builtin_nontemporal_load(b + 1);
+      // the shared output, in y's element type; read once as well: non-temporal with the bf16
+      // rows (FP8 experts), as measured above
+      load8<Y_F32, !Y_F32>(base + (static_cast<int64_t>(t) * d + c * 8) * ysz, v);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[q] = G * b0[q];
-        v[4 + q] = G * b1[q];
-      }
+      for (int q = 0; q < 8; ++q) v[q] *= G;
     } else {
 #pragma unroll
       for (int q = 0; q < 8; ++q) v[q] = 0.0f;
@@ -155,6 +151,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const uint8_t* yb = static_cast<const uint8_t*>(a.y);
   uint8_t* ob = static_cast<uint8_t*>(a.out);
+  const uint8_t* bb = static_cast<const uint8_t*>(a.base);
   CombineGate g{};
   if (a.gate_vec && a.base) {
     if (!a.x || a.x_kind < 0 || a.x_kind > 2 || (a.x_kind == 2 && !a.x_scales))
@@ -171,16 +168,16 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   const dim3 grid(a.T), block(chunks < kCombineMaxThreads ? chunks : kCombineMaxThreads);
   if (a.y_f32 && a.out_f32)
     hipLaunchKernelGGL((combine_kernel<true, true>), grid, block, 0, s, yb, a.inv, a.w, a.k,
-                       a.base, g, ob, a.d);
+                       bb, g, ob, a.d);
   else if (a.y_f32)
     hipLaunchKernelGGL((combine_kernel<true, false>), grid, block, 0, s, yb, a.inv, a.w, a.k,
-                       a.base, g, ob, a.d);
+                       bb, g, ob, a.d);
   else if (a.out_f32)
     hipLaunchKernelGGL((combine_kernel<false, true>), grid, block, 0, s, yb, a.inv, a.w, a.k,
-                       a.base, g, ob, a.d);
+                       bb, g, ob, a.d);
   else
     hipLaunchKernelGGL((combine_kernel<false, false>), grid, block, 0, s, yb, a.inv, a.w, a.k,
-                       a.base, g, ob, a.d);
+                       bb, g, ob, a.d);
   return hipGetLastError();
 }
 

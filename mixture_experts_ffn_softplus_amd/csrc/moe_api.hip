@@ -66,6 +66,10 @@ int out_bytes(const moe_config_t* c) { return c->out_f32 ? 4 : act_bytes(c); }
 // y_perm: fp32 unless the activations are E4M3.  A bf16 y_perm would add a third bf16 rounding
 // (after h and the output) to a budget the output rounding alone half fills.
 int y_bytes(const moe_config_t* c) { return is_fp8(c) ? 2 : 4; }
+// The shared experts' output [T, d], which the combine adds once per token, in y_perm's
+// element type: bf16 for E4M3 activations, whose block output is bf16 (at fp8_block, 2 T d B =
+// 268 MB less written and read than an fp32 copy).
+int so_bytes(const moe_config_t* c) { return y_bytes(c); }
 
 // Router columns padded to the GEMM's N tiles: 128 for small E, else 256 (the wide 8-wave tile).
 int e_pad(const moe_config_t* c) {
@@ -219,7 +223,7 @@ WsLayout ws_layout(const moe_config_t* c) {
   L.h_scales = take(is_fp8(c) ? A * (f / 128) * 4 : 0);
   L.hs = take(T * fs * hb);
   L.hs_scales = take(is_fp8(c) ? T * (fs / 128) * 4 : 0);
-  L.so = take(c->num_shared > 0 ? T * d * 4 : 0);  // shared experts' output, fp32
+  L.so = take(c->num_shared > 0 ? T * d * so_bytes(c) : 0);  // shared experts' output
   L.y = take(A * d * y_bytes(c));
   L.total = o;
   return L;
@@ -423,9 +427,9 @@ hipError_t do_expert_ffn(const moe_config_t* c, const void* xa, const float* xs,
     h.a2_bytes = T * f * hb;
     h.a2_scales = is_fp8(c) ? at<float>(ws, L.hs_scales) : nullptr;
     set_group2_weights(c, h, w->ws_down, w->ws_down_scales);
-    h.out2 = at<float>(ws, L.so);
-    h.ldo2 = d * 4;
-    h.out2_f32 = 1;
+    h.out2 = at<uint8_t>(ws, L.so);
+    h.ldo2 = d * so_bytes(c);
+    h.out2_f32 = so_bytes(c) == 4;
   }
   e = launch_grouped_gemm(c->expert_dtype, kEpiStore, bm, h, max_tiles, s);
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_DOWN, s);
@@ -469,7 +473,7 @@ hipError_t pack_mx(const moe_config_t* c, const moe_logical_weights_t* lw, void*
   return e;
 }
 
-// shared_done: the shared experts' fp32 output is already in the workspace (they ran as the
+// shared_done: the shared experts' output is already in the workspace (they ran as the
 // extra group of the routed GEMMs), so only the combine runs.
 hipError_t do_combine(const moe_config_t* c, const void* xa, const float* xs, const void* y,
                       const int32_t* inv, const float* tw, const moe_weights_t* w, void* out,
@@ -481,9 +485,9 @@ hipError_t do_combine(const moe_config_t* c, const void* xa, const float* xs, co
   const int bm = shared_bm(c);
   const int max_tiles = static_cast<int>((T + bm - 1) / bm);
   hipError_t e = hipSuccess;
-  float* shared_out = nullptr;
+  uint8_t* shared_out = nullptr;
   if (c->num_shared > 0 && shared_done) {
-    shared_out = at<float>(ws, L.so);
+    shared_out = at<uint8_t>(ws, L.so);
     e = mark(ev, MOE_STAGE_SHARED_GATE_UP, s);
   } else if (c->num_shared > 0) {
     GemmArgs g{};
@@ -503,7 +507,7 @@ hipError_t do_combine(const moe_config_t* c, const void* xa, const float* xs, co
     e = launch_grouped_gemm(c->expert_dtype, kEpiSwiglu, bm, g, max_tiles, s);
     if (e == hipSuccess) e = mark(ev, MOE_STAGE_SHARED_GATE_UP, s);
     if (e != hipSuccess) return e;
-    shared_out = at<float>(ws, L.so);
+    shared_out = at<uint8_t>(ws, L.so);
     GemmArgs h{};
     h.A = at<uint8_t>(ws, L.hs);
     h.lda = F * hb;
@@ -516,8 +520,8 @@ hipError_t do_combine(const moe_config_t* c, const void* xa, const float* xs, co
     h.N = static_cast<int>(d);
     h.M = static_cast<int>(T);
     h.out = shared_out;
-    h.ldo = d * 4;
-    h.out_f32 = 1;
+    h.ldo = d * so_bytes(c);
+    h.out_f32 = so_bytes(c) == 4;
     e = launch_grouped_gemm(c->expert_dtype, kEpiStore, bm, h, max_tiles, s);
   } else {
     e = mark(ev, MOE_STAGE_SHARED_GATE_UP, s);

@@ -117,7 +117,7 @@ hipError_t launch_grouped_gemm(int dtype, int epi, int bm, const GemmArgs& a, in
 
 // ---- un-permute and weighted combine (combine.hip)
 // out[t] = G[t] * base[t] + sum_j w[t*k+j] * y[inv[t*k+j]] over d columns; y rows fp32 (y_f32)
-// or bf16, base fp32 [T, d] or null, out fp32 (out_f32) or bf16.  G = 1, or with gate_vec
+// or bf16, base [T, d] in y's element type or null, out fp32 (out_f32) or bf16.  G = 1, or with gate_vec
 // G[t] = sigmoid(x~[t] . gate_vec): x~ fp32 / bf16 (x_kind 0 / 1) or E4M3 codes times their
 // per-128 scales (x_kind 2); gate_vec fp32 or bf16 (gate_f32).
 struct CombineArgs {
@@ -126,7 +126,7 @@ struct CombineArgs {
   const int32_t* inv;
   const float* w;
   int k;
-  const float* base;
+  const void* base;
   const void* gate_vec;
   bool gate_f32;
   const void* x;

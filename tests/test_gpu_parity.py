@@ -277,7 +277,7 @@ def test_degenerate_layers(case):
 def test_shared_gate_factor(name):
     """The gate alone: with the routed experts' down projections zeroed, the gated output over
     the ungated one is G[t] = sigmoid(x~[t] . w_sg) on every column of token t.  No FP8 h
-    rounding enters (both runs share the shared experts' fp32 output S), so G is checked far
+    rounding enters (both runs share the shared experts' output S), so G is checked far
     below the block tolerance: out = round(G S) and round(S) in the output dtype, and the
     least-squares ratio over the d columns is off by at most the two roundings (2^-8 relative
     for bf16 worst case; 1e-3 allowed) -- or 1e-5 for fp32 outputs."""
