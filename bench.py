@@ -348,10 +348,41 @@ class SclkSampler:
                        f"3 s of untimed forwards"}
 
 
+def graph_ms_per_step(cfg, x, w, out, ws, steps):
+    """The same forward captured once in a HIP graph and replayed `steps` times (no launch
+    gaps between the kernels): ms per replay, timed with events on the replaying stream."""
+    import torch
+
+    from mixture_experts_ffn_softplus_amd import api
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        api.moe_forward(cfg, x, w, out, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.moe_forward(cfg, x, w, out, ws)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    del g
+    return ms
+
+
 def run_workload(cfg, steps, warmup, dev, keep=False, sample_clock=True):
     """Pack one workload, run `warmup` untimed and `steps` timed forwards with a HIP event at
-    every stage boundary, sample the shader clock during about 3 s of further untimed forwards
-    (sample_clock), and return its record (and, with keep, the objects a parity check needs)."""
+    every stage boundary; with sample_clock also time `steps` replays of a captured HIP graph of
+    the forward and sample the shader clock during about 3 s of further untimed forwards; return
+    its record (and, with keep, the objects a parity check needs)."""
     import torch
 
     from mixture_experts_ffn_softplus_amd import api, profiling, synth
@@ -445,6 +476,8 @@ def run_workload(cfg, steps, warmup, dev, keep=False, sample_clock=True):
            "config": config_record(cfg), "roofline": roofline, "step_roofline": step,
            "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()}}
     if sample_clock:
+        rec["graph_ms_per_step"] = round(graph_ms_per_step(cfg, x, w, out, ws, steps), 5)
+        log(f"{cfg.name}: graph replay {rec['graph_ms_per_step']:.4f} ms/step")
         # the shader clock under this workload (untimed; the clock follows the MFMA load)
         with SclkSampler() as smp:
             t_end = time.perf_counter() + 3.0
@@ -549,7 +582,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": rec["dtype"], "data": "synthetic", "config": rec["config"],
         "roofline": rec["roofline"], "step_roofline": rec["step_roofline"],
-        "stage_ms": rec["stage_ms"], "cpu_baseline": cpu, "parity": parity,
+        "stage_ms": rec["stage_ms"], "graph_ms_per_step": rec.get("graph_ms_per_step"),
+        "cpu_baseline": cpu, "parity": parity,
         "workloads": {cfg.name: {k: rec[k] for k in ("ms_per_step", "tokens_per_s", "dtype")}
                       | {"step_roofline": rec["step_roofline"]}} | others,
         "gpu": gpu_info(dev) | {"sclk_under_load": rec.get("sclk_under_load")},
