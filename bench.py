@@ -166,7 +166,10 @@ def cpu_baseline(cfg, inp, out, logits_gpu, n_tokens, seed=0):
            "sample": (f"{len(tok)} seeded tokens of {cfg.name}: fp64 router logits, top-k, "
                       f"permutation and routed+shared SwiGLU experts for those tokens; "
                       f"{t_cpu:.1f} s of CPU time"),
-           "seconds": t_cpu}
+           "seconds": t_cpu, "ms_per_token": round(t_cpu / len(tok) * 1e3, 3),
+           "extrapolated_s_for_all_tokens": round(t_cpu / len(tok) * cfg.num_tokens, 1),
+           "extrapolated": (f"ms_per_token x {cfg.num_tokens} tokens: an extrapolation, the "
+                            f"oracle ran on {len(tok)} tokens only")}
     return cpu, parity
 
 
