@@ -698,26 +698,53 @@ void grouped_gemm_kernel(GemmArgs a) {
       // stores made the fp8_block down GEMM 35% slower), and so do the E4M3-activation kernels,
       // whose registers the extra store path costs (fp8_block down +4%).
       const bool nt_out = !S::kFp8 && GROUPED && g.count == 1;
+      // One copy of the store loop per (element type, cache policy), chosen once per tile: with
+      // the choice inside the loop every block's permutes had to complete before its own store
+      // (one LDS round trip per block); in one straight run they overlap the other blocks'.
+      auto store_tile = [&](auto f32_tag, auto nt_tag) __attribute__((always_inline)) {
+        constexpr bool F32 = decltype(f32_tag)::value, NT = decltype(nt_tag)::value;
+        // a row block's permutes first, then its stores
 #pragma unroll
-      for (int i = 0; i < S::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < S::FN; ++j) {
+        for (int i = 0; i < S::FM; ++i) {
           const int row = srow + i * 16;
-          const int col = g.n0 + wn * S::TN + j * 16 + scol;
-          if (f32o) {
-            const uint32_t off = static_cast<uint32_t>(row * ldo + col * 4);
-            if (nt_out)
-              buffer_store16_nt(orsrc, off, xpose4(acc[i][j]));
-            else
-              buffer_store16(orsrc, off, xpose4(acc[i][j]));
+          if constexpr (F32) {
+            f32x4 v[S::FN];
+#pragma unroll
+            for (int j = 0; j < S::FN; ++j) v[j] = xpose4(acc[i][j]);
+#pragma unroll
+            for (int j = 0; j < S::FN; ++j) {
+              const int col = g.n0 + wn * S::TN + j * 16 + scol;
+              const uint32_t off = static_cast<uint32_t>(row * ldo + col * 4);
+              if constexpr (NT)
+                buffer_store16_nt(orsrc, off, v[j]);
+              else
+                buffer_store16(orsrc, off, v[j]);
+            }
           } else {
-            const uint32_t off = static_cast<uint32_t>(row * ldo + col * 2);
-            if (nt_out)
-              buffer_store8_nt(orsrc, off, xpose2(pack_bf16x4(acc[i][j])));
-            else
-              buffer_store8(orsrc, off, xpose2(pack_bf16x4(acc[i][j])));
+            uint2 v[S::FN];
+#pragma unroll
+            for (int j = 0; j < S::FN; ++j) v[j] = xpose2(pack_bf16x4(acc[i][j]));
+#pragma unroll
+            for (int j = 0; j < S::FN; ++j) {
+              const int col = g.n0 + wn * S::TN + j * 16 + scol;
+              const uint32_t off = static_cast<uint32_t>(row * ldo + col * 2);
+              if constexpr (NT)
+                buffer_store8_nt(orsrc, off, v[j]);
+              else
+                buffer_store8(orsrc, off, v[j]);
+            }
           }
         }
+      };
+      constexpr std::true_type kYes{};
+      constexpr std::false_type kNo{};
+      if constexpr (S::kFp8) {
+        if (f32o) store_tile(kYes, kNo); else store_tile(kNo, kNo);
+      } else if (f32o) {
+        if (nt_out) store_tile(kYes, kYes); else store_tile(kYes, kNo);
+      } else {
+        if (nt_out) store_tile(kNo, kYes); else store_tile(kNo, kNo);
+      }
     } else {
       // h = SiLU(gate) * up: pair p of this wave's fragments is (gate, up) = (2p, 2p+1)
       constexpr int HP = S::FN / 2;

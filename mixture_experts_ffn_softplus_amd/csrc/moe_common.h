@@ -115,9 +115,15 @@ __device__ __forceinline__ void buffer_store8_nt(__amdgpu_buffer_rsrc_t r, uint3
 __device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t v) {
   __builtin_amdgcn_raw_buffer_store_b32(static_cast<int>(v), r, static_cast<int>(voff), 0, 0);
 }
+// Two fp32 values as bf16 (round to nearest even, the first in the low half): one packed
+// conversion instruction for the pair.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
 __device__ __forceinline__ uint2 pack_bf16x4(f32x4 v) {
-  return uint2{f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16),
-               f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16)};
+  return uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 
 // ----------------------------------------------------------------------------- LDS DMA
