@@ -113,12 +113,13 @@ def test_binding_rejects_an_output_of_another_dtype(out_f32, dtype):
 def test_large_and_fp8_constraints():
     c = api.config_struct(PRESETS["fp8_block"], quant_block=64)
     assert api.lib().moe_workspace_size(ctypes.byref(c)) == 0
-    c = api.config_struct(PRESETS["softmax_bf16"], num_experts=2048)
-    assert api.lib().moe_route_from_logits(ctypes.byref(c), 1, None, 1, 1, None) == \
-        api.MOE_ERR_UNSUPPORTED
-    c = api.config_struct(PRESETS["softmax_bf16"], top_k=65, num_experts=512)
-    assert api.lib().moe_route_from_logits(ctypes.byref(c), 1, None, 1, 1, None) == \
-        api.MOE_ERR_UNSUPPORTED
+    # the limits themselves are accepted, one past either is not
+    for over, E, k in [(False, 1024, 64), (True, 1025, 64), (True, 1024, 65), (True, 2048, 8)]:
+        c = api.config_struct(PRESETS["softmax_bf16"], num_experts=E, top_k=k)
+        assert (api.lib().moe_workspace_size(ctypes.byref(c)) == 0) == over, (E, k)
+        if over:
+            assert api.lib().moe_route_from_logits(ctypes.byref(c), 1, None, 1, 1, None) == \
+                api.MOE_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("name,over,ok", [

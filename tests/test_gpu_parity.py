@@ -226,6 +226,49 @@ def test_route_from_logits_with_ties_bit_exact():
         assert np.max(np.abs(w.cpu().double().numpy() - w_ref)) <= 1e-6 * max(gamma, 1)
 
 
+@pytest.mark.parametrize("k", [64, 22, 1])
+def test_route_from_logits_with_ties_at_1024_experts(k):
+    # the library's largest expert count (16 experts a lane) and top-k: integer-valued logits
+    # make most heads tie in every round, across lanes and within a lane
+    T, E = 193, 1024
+    cfg = BF.with_(num_tokens=T, num_experts=E, top_k=k)
+    g = torch.Generator().manual_seed(6 + k)
+    logits = torch.randint(-2, 3, (T, E), generator=g).float().cuda()
+    for score, gamma, sb in [(SOFTMAX, 1.0, None),
+                             (SQRT_SOFTPLUS, 2.5, (torch.arange(E) % 3 - 1).float().cuda() * 0.25)]:
+        c = cfg.with_(score=score, routed_scale=gamma)
+        ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
+        w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+        api.moe_route_from_logits(c, logits, sb, ids, w)
+        torch.cuda.synchronize()
+        ids_ref, w_ref, _ = oracle_route_on(c, logits, sb)
+        assert np.array_equal(ids.cpu().numpy(), ids_ref)
+        assert np.max(np.abs(w.cpu().double().numpy() - w_ref)) <= 1e-6 * max(gamma, 1)
+
+
+# The library's limits: 1024 experts, top-64 (every routing lane and combine slot in use).
+LIMITS = {
+    "max_E_max_k_softmax": BF.with_(name="max_E_max_k_softmax", num_tokens=40, d_model=256,
+                                    num_experts=1024, top_k=64, d_ff=128, num_shared=1,
+                                    d_ff_shared=128, seed=51),
+    "max_E_max_k_sqrt_softplus": PRESETS["softplus_bf16"].with_(
+        name="max_E_max_k_sqrt_softplus", num_tokens=33, d_model=256, num_experts=1024,
+        top_k=64, d_ff=128, num_shared=1, d_ff_shared=128, seed=52),
+    "max_E_max_k_fp8": PRESETS["fp8_block"].with_(name="max_E_max_k_fp8", num_tokens=24,
+                                                  d_model=256, num_experts=1024, top_k=64,
+                                                  d_ff=512, num_shared=1, d_ff_shared=512,
+                                                  seed=53),
+    "max_E_top1_many_tokens": BF.with_(name="max_E_top1_many_tokens", num_tokens=3000,
+                                       d_model=256, num_experts=1024, top_k=1, d_ff=128,
+                                       num_shared=1, d_ff_shared=128, seed=54),
+}
+
+
+@pytest.mark.parametrize("name", list(LIMITS))
+def test_layers_at_the_limits(name):
+    check_layer(Layer(LIMITS[name]))
+
+
 # Batches of at most 4096 assignments over at most 768 experts are permuted by one workgroup
 # (rounds of 1024 assignments), larger ones by the multi-kernel counting sort: both sides of
 # each limit are here, with one expert taking every assignment across all four rounds.
