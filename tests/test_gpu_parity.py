@@ -143,6 +143,54 @@ def test_fp8_activation_codes_bit_exact(name):
     assert np.array_equal(xq.cpu().numpy(), codes)
 
 
+def _crafted_fp8_rows(T: int, d: int, seed: int) -> torch.Tensor:
+    """bf16 activation rows whose 128-value groups probe the quantiser's edges: all-zero groups,
+    -0, one spike over values in (and below) E4M3's subnormal range, values exactly on code
+    rounding midpoints (scale 1: amax = 448), a group whose maximum is the smallest bf16
+    normal, and ordinary Gaussian groups."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(T, d, generator=g)
+    groups = d // 128
+    mids = torch.tensor([1.0625, 1.1875, 2.125, 2.375, 0.0068359375, 0.013671875, 208.0, 432.0,
+                         -1.0625, -2.125, -0.0068359375, -208.0])
+    for t in range(T):
+        for gi in range(groups):
+            kind = (t * groups + gi) % 6
+            sl = slice(gi * 128, gi * 128 + 128)
+            if kind == 0:
+                x[t, sl] = 0.0
+                x[t, gi * 128] = -0.0
+            elif kind == 1:
+                x[t, sl] = torch.randn(128, generator=g) * 1e-4
+                x[t, gi * 128 + (t % 128)] = 3.0e3
+            elif kind == 2:
+                x[t, sl] = mids[torch.randint(0, len(mids), (128,), generator=g)]
+                x[t, gi * 128 + 5] = 448.0
+            elif kind == 3:
+                x[t, sl] = torch.randn(128, generator=g).abs() * 2.0 ** -126
+                x[t, gi * 128 + 3] = 2.0 ** -126
+    return x.to(torch.bfloat16)
+
+
+def test_fp8_activation_codes_bit_exact_on_crafted_rows():
+    cfg = SMALL["fp8_bf16_router"].with_(num_tokens=97)
+    layer = Layer(cfg)
+    T, d, k = cfg.num_tokens, cfg.d_model, cfg.top_k
+    dev = layer.ws.device
+    x = _crafted_fp8_rows(T, d, 31).to(dev)
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    xq = torch.empty(T, d, dtype=torch.uint8, device=dev)
+    xs = torch.empty(T, d // 128, dtype=torch.float32, device=dev)
+    api.moe_route(cfg, x, layer.w, None, ids, w, xq, xs, layer.ws)
+    torch.cuda.synchronize()
+    codes, scales, _ = oracle.quant_rows(exact64(x), 128)
+    assert np.array_equal(xs.cpu().numpy(), scales)
+    assert np.array_equal(xq.cpu().numpy(), codes)
+    # the crafted groups did reach the edges: zero groups, subnormal codes, rounding ties
+    assert (scales == 1.0).any() and ((codes & 0x78) == 0).any()
+
+
 # The split calls run the shared experts in launches of their own; moe_forward of the
 # decode-sized layers here runs them as an extra group of the routed GEMMs: the same bits.
 @pytest.mark.parametrize("name", ["bf16_sqrt_softplus_zipf", "bf16_gated_shared",
