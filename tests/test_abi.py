@@ -275,3 +275,22 @@ def test_noalloc_forward_refuses_configs_beyond_its_scratch():
     bad = api.config_struct(PRESETS["decode_bf16"], top_k=0)
     assert L.moe_forward_noalloc(ctypes.byref(bad), 1, ctypes.byref(w), 1, None, None) == \
         api.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_c_example_program_runs_on_the_host(tmp_path):
+    # the plain C++ driver of the ABI (no GPU call before these checks): usage without a
+    # directory, and a refused config reported before any device memory is touched
+    from mixture_experts_ffn_softplus_amd import build as hip_build
+    if not os.path.exists(hip_build.EXAMPLE):
+        pytest.skip("forward_c is not built")
+    r = subprocess.run([hip_build.EXAMPLE], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "usage" in r.stderr
+    bad = api.config_struct(PRESETS["fp8_block"], quant_block=64)
+    (tmp_path / "config.bin").write_bytes(bytes(bad))
+    r = subprocess.run([hip_build.EXAMPLE, str(tmp_path)], capture_output=True, text=True,
+                       timeout=60)
+    assert r.returncode == 1 and "not supported" in r.stderr
+    (tmp_path / "config.bin").write_bytes(bytes(bad)[:-4])
+    r = subprocess.run([hip_build.EXAMPLE, str(tmp_path)], capture_output=True, text=True,
+                       timeout=60)
+    assert r.returncode == 1 and "moe_config_t is" in r.stderr
