@@ -180,7 +180,10 @@ void grouped_gemm_kernel(GemmArgs a) {
   // per XCD; the XCD's workgroups take its tiles round-robin, so at any time they work on
   // consecutive tiles.
   const int NT = a.N / BN;
-  const int ntiles = GROUPED ? a.tiles_count[0] : (a.M + BM - 1) / BM;
+  // one-group launches may split K: tile index = split * (row tiles) + row tile
+  const int splits = GROUPED || a.k_splits < 2 ? 1 : a.k_splits;
+  const int mtiles = GROUPED ? 0 : (a.M + BM - 1) / BM;
+  const int ntiles = GROUPED ? a.tiles_count[0] : mtiles * splits;
   const int nblocks = ntiles * NT;
   const int xcd = blockIdx.x % kNumXcd, wg = blockIdx.x / kNumXcd;
   const int per_xcd = gridDim.x / kNumXcd;
@@ -213,8 +216,10 @@ void grouped_gemm_kernel(GemmArgs a) {
       const i32x4 ti = scalar_load16(a.tiles + first + m);
       g = TileGeo{ti[0], ti[1], ti[2] & 0xFF, nt * BN, count};
     } else {
+      // (the group field holds the K range of a split launch)
       const int tile = L / NT, nt = L - tile * NT;
-      g = TileGeo{0, tile * BM, min(BM, a.M - tile * BM), nt * BN, 1};
+      const int split = tile / mtiles, mt = tile - split * mtiles;
+      g = TileGeo{split, mt * BM, min(BM, a.M - mt * BM), nt * BN, 1};
     }
     return g;
   };
@@ -222,12 +227,12 @@ void grouped_gemm_kernel(GemmArgs a) {
   const int tid = threadIdx.x, l = lane_id(), wv = uniform(tid / kWave);
   const int wm = wv / S::WN, wn = wv % S::WN;
   const int lr = l & 15, kq = l >> 4;
-  const int KB = a.K * esize / kBlockK;  // pipeline steps per tile (K >= 128 elements)
+  const int KB = a.K * esize / kBlockK / splits;  // pipeline steps per tile (K >= 128 elements)
   const int64_t ldb = a.ldb;
   constexpr uint32_t kOob = 0x80000000u;  // beyond every buffer: reads zeros
   // A rows repeat every a_steps steps when a_steps > 0 (the router's hi + lo weight planes
   // are one [E, 2d] matrix multiplied by [x, x])
-  const int a_steps = a.a_steps > 0 ? a.a_steps : KB;
+  const int a_steps = a.a_steps > 0 ? a.a_steps : KB * splits;
 
   // ---------------------------------------------------------------- direct-to-LDS loads
   // Every load writes 16 bytes per lane straight into LDS at (wave base + 16 * lane): the
@@ -268,11 +273,13 @@ void grouped_gemm_kernel(GemmArgs a) {
   // epilogues: with at least NSLOT - 1 steps per tile the consuming side is on one of the two.
   TileGeo g_iss{}, g_prev{};
   int g_iss_t = -1;
+  int iss_k0 = 0;  // first K-step of the issuing side's tile (a split launch's K range)
   auto setup = [&](int t) {
     const TileGeo g = geo(t);
     g_prev = g_iss;
     g_iss = g;
     g_iss_t = t;
+    if constexpr (!GROUPED) iss_k0 = g.group * KB;
     const bool second = has2 && g.group == a.group2;  // (uniform)
     const int row0 = second ? g.m0 - a.m2 : g.m0;     // first A row of an unmapped tile
     a_rs = second ? a_rs2 : a_rs1;
@@ -315,7 +322,7 @@ void grouped_gemm_kernel(GemmArgs a) {
     // E4M3 activations: wave w < ASW loads the row scales of rows [64w, 64w+64), the next BSW
     // waves the weight scales, any other wave a dummy word
     if constexpr (S::kFp8) {
-      const int kb_bytes = KB * 4;
+      const int kb_bytes = KB * splits * 4;
       s_off = kOob;
       if (wv < S::ASW) {
         const uint32_t a_rows = static_cast<uint32_t>((second ? a.a2_bytes : a.a_bytes) / a.lda);
@@ -369,7 +376,7 @@ void grouped_gemm_kernel(GemmArgs a) {
       iss_s = 0;
       if (++iss_t < n_my) setup(iss_t);
     }
-    const int step = iss_s;
+    const int step = iss_k0 + iss_s;
     q_slot = iss_slot;
     iss_slot = iss_slot + 1 == S::NSLOT ? 0 : iss_slot + 1;
     ++iss_s;
@@ -687,8 +694,11 @@ void grouped_gemm_kernel(GemmArgs a) {
     const bool second = has2 && g.group == a.group2;
     const int64_t ldo = second ? a.ldo2 : a.ldo;
     const int orow0 = second ? g.m0 - a.m2 : g.m0;
+    // (a split launch stores K range g.group as its own partial plane)
+    const int64_t plane = GROUPED ? 0 : static_cast<int64_t>(g.group) * a.split_plane;
     const __amdgpu_buffer_rsrc_t orsrc =
-        buffer_rsrc(static_cast<uint8_t*>(second ? a.out2 : a.out) + static_cast<int64_t>(orow0) * ldo,
+        buffer_rsrc(static_cast<uint8_t*>(second ? a.out2 : a.out) + plane +
+                        static_cast<int64_t>(orow0) * ldo,
                     static_cast<uint32_t>(g.rows * ldo));
     if constexpr (EPI == kEpiStore) {
       const bool f32o = (second ? a.out2_f32 : a.out_f32) != 0;
@@ -924,8 +934,8 @@ static int persistent_grid(Kern kernel, int threads, int64_t max_blocks) {
 
 template <int DT, int BM, int BN, int EPI, bool G, bool G2 = false>
 static hipError_t launch_kernel(const GemmArgs& a, int max_tiles, hipStream_t s) {
-  // grouped: worst-case tile count from the caller; one group: exact, for this BM
-  if (!G) max_tiles = (a.M + BM - 1) / BM;
+  // grouped: worst-case tile count from the caller; one group: exact, for this BM and K split
+  if (!G) max_tiles = (a.M + BM - 1) / BM * (a.k_splits > 1 ? a.k_splits : 1);
   const int64_t nb = static_cast<int64_t>(max_tiles) * (a.N / BN);
   if (nb <= 0) return hipSuccess;
   auto kernel = grouped_gemm_kernel<DT, BM, BN, EPI, G, G2>;

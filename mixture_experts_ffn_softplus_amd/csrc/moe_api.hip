@@ -99,6 +99,23 @@ int router_bm(const moe_config_t* c) {
   return 16;
 }
 
+// K split of the router GEMM.  When its tiles leave most CUs idle (decode-sized batches) each
+// tile walks K alone, one latency-bound step after another; split into up to 8 ranges of at
+// least 8 K-steps, the ranges run side by side, each into its own fp32 plane of partial logits,
+// which the top-k waves add in a fixed order (so the logits stay run-to-run identical).
+int router_splits(const moe_config_t* c) {
+  const int kind = router_kind(c);
+  const int64_t T = c->num_tokens, Ep = e_pad(c);
+  const int bm = kind == kRouterF32 ? 32 : router_bm(c);  // the fp32 GEMM's tile is 32 x 128
+  const int bn = kind != kRouterF32 && bm == 128 && Ep % 256 == 0 ? 256 : 128;
+  const int64_t tiles = (T + bm - 1) / bm * (Ep / bn);
+  const int64_t K = kind == kRouterBF16HiLo ? 2 * c->d_model : c->d_model;
+  const int64_t steps = K * (kind == kRouterF32 ? 4 : 2) / kBlockK;
+  int s = 1;
+  while (s < 8 && tiles * 2 * s <= 256 && steps % (2 * s) == 0 && steps / (2 * s) >= 8) s *= 2;
+  return s;
+}
+
 int routed_bm(const moe_config_t* c) {
   int64_t avg = c->num_experts > 0 ? assignments(c) / c->num_experts : 0;
   return gemm_bm(c->expert_dtype, kEpiSwiglu, static_cast<int>(avg < 1 << 20 ? avg : 1 << 20));
@@ -207,7 +224,7 @@ WsLayout ws_layout(const moe_config_t* c) {
     o += align_up(bytes);
     return at;
   };
-  L.logits = take(T * e_pad(c) * 4);
+  L.logits = take(router_splits(c) * T * e_pad(c) * 4);  // one fp32 plane per K range
   L.ids = take(A * 4);
   L.w = take(A * 4);
   L.offsets = take((c->num_experts + 1) * 4);
@@ -298,12 +315,17 @@ hipError_t do_route(const moe_config_t* c, const void* x, const moe_weights_t* w
   g.out = lg;
   g.ldo = Ep * 4;
   g.out_f32 = 1;
+  const int splits = router_splits(c);
+  g.k_splits = splits;
+  g.split_plane = c->num_tokens * Ep * 4;
   const int bm = router_bm(c);
   hipError_t e = launch_grouped_gemm(kind == kRouterF32 ? MOE_F32 : MOE_BF16, kEpiStore, bm, g,
                                      (c->num_tokens + bm - 1) / bm, s);
   if (e != hipSuccess) return e;
   RouteArgs ra = route_args(c, w->select_bias, ids, tw);
   ra.logit_bias = w->logit_bias;
+  ra.splits = splits;
+  ra.plane = c->num_tokens * Ep;
   ra.token_ids = token_ids;
   ra.table = table;
   ra.vocab = vocab;
@@ -738,8 +760,9 @@ moe_status_t moe_route_from_logits(const moe_config_t* c, const float* logits,
   if (st != MOE_OK) return st;
   if (!logits || !ids || !tw) return MOE_ERR_INVALID_ARGUMENT;
   if (c->num_tokens == 0) return MOE_OK;
-  return hip_status(launch_topk(route_args(c, select_bias, ids, tw), logits, c->num_experts,
-                                nullptr, s));
+  // one plane (splits 0): the caller's logits are only read
+  return hip_status(launch_topk(route_args(c, select_bias, ids, tw), const_cast<float*>(logits),
+                                c->num_experts, nullptr, s));
 }
 
 moe_status_t moe_permute(const moe_config_t* c, const int32_t* ids, int32_t* offsets,

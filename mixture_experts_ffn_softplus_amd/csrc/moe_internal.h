@@ -27,12 +27,16 @@ struct RouteArgs {
   uint8_t* xq;
   float* xq_scales;
   int d;
+  // logits given as `splits` partial planes `plane` floats apart (a K-split router GEMM), added
+  // in plane order into the first before the choice (0 or 1: one plane)
+  int splits;
+  int64_t plane;
 };
 enum RouterKind { kRouterF32 = 0, kRouterBF16 = 1, kRouterBF16HiLo = 2 };
 // Scoring + top-k of fp32 logits rows `ld` apart (plus logit_bias), and the FP8 activations
-// when a.xq is set; copy: optional [T, E] copy of the biased logits.
-hipError_t launch_topk(const RouteArgs& a, const float* logits, int ld, float* copy,
-                       hipStream_t s);
+// when a.xq is set; copy: optional [T, E] copy of the biased logits.  With a.splits > 1 the
+// first plane is overwritten by the sum of the planes.
+hipError_t launch_topk(const RouteArgs& a, float* logits, int ld, float* copy, hipStream_t s);
 // Balancing step of the fp32 selection bias from the permutation's expert offsets [E+1]:
 // bias[e] += speed * sign(A - E * load_e), A = offsets[E].
 hipError_t launch_bias_update(const int32_t* offsets, int E, float speed, float* bias,
@@ -85,6 +89,10 @@ struct GemmArgs {
   int out_f32;                // store epilogue: fp32 rows (else bf16)
   // A rows repeat every a_steps K-steps when > 0 (0: no repeat)
   int a_steps;
+  // One group only (tiles null): K split into k_splits equal ranges of whole K-steps (0 or 1:
+  // no split), range s stored as its own partial product at out + s * split_plane bytes.
+  int k_splits;
+  int64_t split_plane;
   // One extra group after the routed experts when has_group2 (group index group2): the shared
   // experts, whose rows are the tokens in order.  Its rows [m2, m2 + rows) of the M space take
   // A row (r - m2) of A2 (no a_map), the weights B2 (+ scales), and store to out2 (+ scales)

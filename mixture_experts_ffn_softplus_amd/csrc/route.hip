@@ -236,11 +236,21 @@ __device__ void quant_row_fp8(const RouteArgs& a, int t) {
 // each (one fp32 add, the last step of the logits); when `copy` is non-null the E finished
 // logits of each row are also written there as [T, E].
 template <int SLOTS>
-__global__ __launch_bounds__(256) void topk_kernel(RouteArgs a, const float* __restrict__ logits,
-                                                   int ld, float* __restrict__ copy) {
+__global__ __launch_bounds__(256) void topk_kernel(RouteArgs a, float* logits, int ld,
+                                                   float* __restrict__ copy) {
   int t = blockIdx.x * 4 + threadIdx.x / kWave;
   if (t >= a.T) return;  // whole waves leave together
-  const float* row = logits + static_cast<size_t>(t) * ld;
+  float* row = logits + static_cast<size_t>(t) * ld;
+  if (a.splits > 1) {
+    // partial logits of a K-split router GEMM: their sum, in plane order, replaces the first
+    // plane's row; the wave's stores complete before any lane reads the row back
+    for (int e = lane_id(); e < a.E; e += kWave) {
+      float v = row[e];
+      for (int p = 1; p < a.splits; ++p) v += row[p * a.plane + e];
+      row[e] = v;
+    }
+    __threadfence();
+  }
   if (copy)
     for (int e = lane_id(); e < a.E; e += kWave)
       copy[static_cast<size_t>(t) * a.E + e] =
@@ -249,8 +259,7 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a, const float* __r
   if (a.xq) quant_row_fp8(a, t);
 }
 
-hipError_t launch_topk(const RouteArgs& a, const float* logits, int ld, float* copy,
-                       hipStream_t s) {
+hipError_t launch_topk(const RouteArgs& a, float* logits, int ld, float* copy, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   // experts per lane: E <= 64 * SLOTS (E <= 1024, checked by the caller)
   const dim3 grid((a.T + 3) / 4), block(256);

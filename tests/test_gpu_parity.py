@@ -317,6 +317,33 @@ def test_layers_at_the_limits(name):
     check_layer(Layer(LIMITS[name]))
 
 
+# Decode-sized batches with a deep reduction split the router GEMM's K into ranges whose partial
+# logits the top-k waves add (2, 8 and 4 ranges here: bf16, the fp32 router's bf16 hi + lo
+# planes, fp32); the logits, ids and block output are checked as everywhere, and repeated
+# forwards must agree bit for bit.
+ROUTER_SPLIT = {
+    "router_split_bf16": BF.with_(name="router_split_bf16", num_tokens=8, d_model=1024,
+                                  num_experts=32, top_k=2, d_ff=128, num_shared=1,
+                                  d_ff_shared=128, seed=71),
+    "router_split_fp8_f32_router": PRESETS["fp8_block"].with_(
+        name="router_split_fp8_f32_router", num_tokens=16, d_model=2048, num_experts=64,
+        top_k=4, d_ff=512, num_shared=1, d_ff_shared=512, seed=72),
+    "router_split_f32": PRESETS["tiny_fp32"].with_(name="router_split_f32", num_tokens=8,
+                                                   d_model=1024, num_experts=16, top_k=2,
+                                                   d_ff=128, num_shared=1, d_ff_shared=256,
+                                                   seed=73),
+}
+
+
+@pytest.mark.parametrize("name", list(ROUTER_SPLIT))
+def test_split_router_layers(name):
+    layer = Layer(ROUTER_SPLIT[name])
+    check_layer(layer)
+    first = layer.forward()
+    for _ in range(5):
+        assert torch.equal(layer.forward(), first)
+
+
 # Batches of at most 4096 assignments over at most 768 experts are permuted by one workgroup
 # (rounds of 1024 assignments), larger ones by the multi-kernel counting sort: both sides of
 # each limit are here, with one expert taking every assignment across all four rounds.
