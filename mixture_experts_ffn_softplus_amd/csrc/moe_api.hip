@@ -99,10 +99,12 @@ int router_bm(const moe_config_t* c) {
   return 16;
 }
 
-// K split of the router GEMM.  When its tiles leave most CUs idle (decode-sized batches) each
-// tile walks K alone, one latency-bound step after another; split into up to 8 ranges of at
-// least 8 K-steps, the ranges run side by side, each into its own fp32 plane of partial logits,
-// which the top-k waves add in a fixed order (so the logits stay run-to-run identical).
+// K split of the router GEMM.  When its tiles fill the GPU at most once (up to two workgroups
+// a CU), each tile walks K alone, one latency-bound step after another; split into up to 8
+// ranges of at least 8 K-steps, the ranges run side by side, each into its own fp32 plane of
+// partial logits, which the top-k waves add in a fixed order (so the logits stay run-to-run
+// identical).  Measured on MI355X: decode_bf16 route 0.032 -> 0.022 ms, softmax_bf16 and
+// softplus_bf16 -3 to -4 us.
 int router_splits(const moe_config_t* c) {
   const int kind = router_kind(c);
   const int64_t T = c->num_tokens, Ep = e_pad(c);
@@ -112,7 +114,7 @@ int router_splits(const moe_config_t* c) {
   const int64_t K = kind == kRouterBF16HiLo ? 2 * c->d_model : c->d_model;
   const int64_t steps = K * (kind == kRouterF32 ? 4 : 2) / kBlockK;
   int s = 1;
-  while (s < 8 && tiles * 2 * s <= 256 && steps % (2 * s) == 0 && steps / (2 * s) >= 8) s *= 2;
+  while (s < 8 && tiles * 2 * s <= 512 && steps % (2 * s) == 0 && steps / (2 * s) >= 8) s *= 2;
   return s;
 }
 
@@ -760,9 +762,8 @@ moe_status_t moe_route_from_logits(const moe_config_t* c, const float* logits,
   if (st != MOE_OK) return st;
   if (!logits || !ids || !tw) return MOE_ERR_INVALID_ARGUMENT;
   if (c->num_tokens == 0) return MOE_OK;
-  // one plane (splits 0): the caller's logits are only read
-  return hip_status(launch_topk(route_args(c, select_bias, ids, tw), const_cast<float*>(logits),
-                                c->num_experts, nullptr, s));
+  return hip_status(launch_topk(route_args(c, select_bias, ids, tw), logits, c->num_experts,
+                                nullptr, s));
 }
 
 moe_status_t moe_permute(const moe_config_t* c, const int32_t* ids, int32_t* offsets,

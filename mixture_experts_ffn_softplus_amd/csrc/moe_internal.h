@@ -28,15 +28,16 @@ struct RouteArgs {
   float* xq_scales;
   int d;
   // logits given as `splits` partial planes `plane` floats apart (a K-split router GEMM), added
-  // in plane order into the first before the choice (0 or 1: one plane)
+  // in plane order before the choice (0 or 1: one plane)
   int splits;
   int64_t plane;
 };
 enum RouterKind { kRouterF32 = 0, kRouterBF16 = 1, kRouterBF16HiLo = 2 };
 // Scoring + top-k of fp32 logits rows `ld` apart (plus logit_bias), and the FP8 activations
-// when a.xq is set; copy: optional [T, E] copy of the biased logits.  With a.splits > 1 the
-// first plane is overwritten by the sum of the planes.
-hipError_t launch_topk(const RouteArgs& a, float* logits, int ld, float* copy, hipStream_t s);
+// when a.xq is set; copy: optional [T, E] copy of the biased logits (with a.splits > 1: of the
+// planes' sum).
+hipError_t launch_topk(const RouteArgs& a, const float* logits, int ld, float* copy,
+                       hipStream_t s);
 // Balancing step of the fp32 selection bias from the permutation's expert offsets [E+1]:
 // bias[e] += speed * sign(A - E * load_e), A = offsets[E].
 hipError_t launch_bias_update(const int32_t* offsets, int E, float speed, float* bias,

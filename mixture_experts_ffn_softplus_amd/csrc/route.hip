@@ -236,20 +236,22 @@ __device__ void quant_row_fp8(const RouteArgs& a, int t) {
 // each (one fp32 add, the last step of the logits); when `copy` is non-null the E finished
 // logits of each row are also written there as [T, E].
 template <int SLOTS>
-__global__ __launch_bounds__(256) void topk_kernel(RouteArgs a, float* logits, int ld,
+__global__ __launch_bounds__(256) void topk_kernel(RouteArgs a, const float* logits, int ld,
                                                    float* __restrict__ copy) {
+  // partial logits of a K-split router GEMM, added in plane order into a row of this wave's
+  // own in LDS (the row the choice then reads; a wave's LDS accesses complete in order)
+  __shared__ float s_sum[4][1024];
   int t = blockIdx.x * 4 + threadIdx.x / kWave;
   if (t >= a.T) return;  // whole waves leave together
-  float* row = logits + static_cast<size_t>(t) * ld;
+  const float* row = logits + static_cast<size_t>(t) * ld;
   if (a.splits > 1) {
-    // partial logits of a K-split router GEMM: their sum, in plane order, replaces the first
-    // plane's row; the wave's stores complete before any lane reads the row back
+    float* sum = s_sum[threadIdx.x / kWave];
     for (int e = lane_id(); e < a.E; e += kWave) {
       float v = row[e];
       for (int p = 1; p < a.splits; ++p) v += row[p * a.plane + e];
-      row[e] = v;
+      sum[e] = v;
     }
-    __threadfence();
+    row = sum;
   }
   if (copy)
     for (int e = lane_id(); e < a.E; e += kWave)
@@ -259,7 +261,8 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a, float* logits, i
   if (a.xq) quant_row_fp8(a, t);
 }
 
-hipError_t launch_topk(const RouteArgs& a, float* logits, int ld, float* copy, hipStream_t s) {
+hipError_t launch_topk(const RouteArgs& a, const float* logits, int ld, float* copy,
+                       hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   // experts per lane: E <= 64 * SLOTS (E <= 1024, checked by the caller)
   const dim3 grid((a.T + 3) / 4), block(256);
