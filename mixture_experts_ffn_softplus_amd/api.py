@@ -279,7 +279,11 @@ _TORCH_ACT = {F32: torch.float32, BF16: torch.bfloat16}
 
 
 def y_dtype(cfg: MoEConfig):
-    return torch.bfloat16 if cfg.expert_dtype in (FP8_E4M3, MXFP4) else torch.float32
+    """Element type of y_perm: fp32 for fp32 experts, fp16 for bf16 experts, bf16 for FP8 /
+    MXFP4 experts (E4M3 activations)."""
+    if cfg.expert_dtype in (FP8_E4M3, MXFP4):
+        return torch.bfloat16
+    return torch.float32 if cfg.expert_dtype == F32 else torch.float16
 
 
 def out_dtype(cfg: MoEConfig):

@@ -11,6 +11,8 @@
 // Gated shared expert (shared-expert row, Qwen3.5 cell): the shared output is first scaled by
 // the token's sigmoid(x~ . w_sg), one dot product of length d per token reduced across the
 // workgroup before the streaming loop; x~ is the activation row the shared experts read.
+#include <type_traits>
+
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -27,13 +29,13 @@ struct CombineGate {
   int vec_f32, x_kind;
 };
 
-// Eight consecutive values of a row of bf16 (16 B) or fp32 (32 B) elements; NT: non-temporal
-// loads.  The expert rows are read once; measured on MI355X, non-temporal loads speed up the
-// bf16 rows (FP8 experts: 2.95 GB, 668 -> 585 us) but slow down the fp32 rows of the bf16
-// experts (0.67 GB, 183 -> 216 us), so only the former use them.
-template <bool F32, bool NT = false>
+// Eight consecutive values of a row of bf16 or fp16 (16 B) or fp32 (32 B) elements (RowKind);
+// NT: non-temporal loads.  The expert rows are read once; measured on MI355X, non-temporal
+// loads speed up the bf16 rows (FP8 experts: 2.95 GB, 668 -> 585 us) but slow down the fp32
+// rows (0.67 GB, 183 -> 216 us), so only the former use them.
+template <int KIND, bool NT = false>
 __device__ __forceinline__ void load8(const uint8_t* p, float* v) {
-  if constexpr (F32) {
+  if constexpr (KIND == kRowF32) {
     const f32x4* q = reinterpret_cast<const f32x4*>(p);
     const f32x4 a = NT ? __builtin_nontemporal_load(q) : q[0];
     const f32x4 b = NT ? __builtin_nontemporal_load(q + 1) : q[1];
@@ -48,8 +50,13 @@ __device__ __forceinline__ void load8(const uint8_t* p, float* v) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t bits = static_cast<uint32_t>(r[q]);
-      v[2 * q] = __uint_as_float(bits << 16);
-      v[2 * q + 1] = __uint_as_float(bits & 0xFFFF0000u);
+      if constexpr (KIND == kRowBF16) {
+        v[2 * q] = __uint_as_float(bits << 16);
+        v[2 * q + 1] = __uint_as_float(bits & 0xFFFF0000u);
+      } else {
+        v[2 * q] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+        v[2 * q + 1] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits >> 16)));
+      }
     }
   }
 }
@@ -62,9 +69,9 @@ __device__ float shared_gate(const CombineGate& g, int t, int d) {
     float xv[8], gv[8];
     const int64_t i = static_cast<int64_t>(t) * d + c * 8;
     if (g.x_kind == 0) {
-      load8<true>(g.x + i * 4, xv);
+      load8<kRowF32>(g.x + i * 4, xv);
     } else if (g.x_kind == 1) {
-      load8<false>(g.x + i * 2, xv);
+      load8<kRowBF16>(g.x + i * 2, xv);
     } else {
       const uint2 codes = *reinterpret_cast<const uint2*>(g.x + i);
       const float sc = g.xs[static_cast<int64_t>(t) * (d / 128) + (c * 8) / 128];
@@ -75,9 +82,9 @@ __device__ float shared_gate(const CombineGate& g, int t, int d) {
       }
     }
     if (g.vec_f32)
-      load8<true>(g.vec + c * 32, gv);
+      load8<kRowF32>(g.vec + c * 32, gv);
     else
-      load8<false>(g.vec + c * 16, gv);
+      load8<kRowBF16>(g.vec + c * 16, gv);
 #pragma unroll
     for (int q = 0; q < 8; ++q) z = fmaf(xv[q], gv[q], z);
   }
@@ -89,11 +96,14 @@ __device__ float shared_gate(const CombineGate& g, int t, int d) {
   return 1.0f / (1.0f + expf(-z));
 }
 
-template <bool Y_F32, bool OUT_F32>
+// YK: y's RowKind; the shared output is fp32 under fp32 or fp16 rows, bf16 under bf16 rows.
+template <int YK, bool OUT_F32>
 __global__ __launch_bounds__(kCombineMaxThreads) void combine_kernel(
     const uint8_t* __restrict__ y, const int32_t* __restrict__ inv, const float* __restrict__ w,
     int k, const uint8_t* __restrict__ base, CombineGate gate, uint8_t* __restrict__ out, int d) {
-  constexpr int ysz = Y_F32 ? 4 : 2, osz = OUT_F32 ? 4 : 2;
+  constexpr int BK = YK == kRowBF16 ? kRowBF16 : kRowF32;
+  constexpr int ysz = YK == kRowF32 ? 4 : 2, bsz = BK == kRowF32 ? 4 : 2, osz = OUT_F32 ? 4 : 2;
+  constexpr bool kNtY = YK == kRowBF16;  // non-temporal y and shared loads (see load8)
   __shared__ int32_t s_row[kCombineMaxK];
   __shared__ float s_w[kCombineMaxK];
   const int t = blockIdx.x;
@@ -110,9 +120,9 @@ __global__ __launch_bounds__(kCombineMaxThreads) void combine_kernel(
   for (int c = threadIdx.x; c < d / 8; c += blockDim.x) {
     float v[8];
     if (base) {
-      // the shared output, in y's element type; read once as well: non-temporal with the bf16
-      // rows (FP8 experts), as measured above
-      load8<Y_F32, !Y_F32>(base + (static_cast<int64_t>(t) * d + c * 8) * ysz, v);
+      // the shared output, read once as well: non-temporal with the bf16 rows (FP8 experts),
+      // as measured above
+      load8<BK, kNtY>(base + (static_cast<int64_t>(t) * d + c * 8) * bsz, v);
 #pragma unroll
       for (int q = 0; q < 8; ++q) v[q] *= G;
     } else {
@@ -124,7 +134,7 @@ __global__ __launch_bounds__(kCombineMaxThreads) void combine_kernel(
       float yv[kCombineBatch][8];
 #pragma unroll
       for (int u = 0; u < kCombineBatch; ++u)
-        load8<Y_F32, !Y_F32>(yc + s_row[j0 + u] * ldy, yv[u]);
+        load8<YK, kNtY>(yc + s_row[j0 + u] * ldy, yv[u]);
 #pragma unroll
       for (int u = 0; u < kCombineBatch; ++u) {
         const float wj = s_w[j0 + u];
@@ -166,18 +176,24 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   // one thread per 8-column chunk (whole waves), at most kCombineMaxThreads
   const int chunks = (a.d / 8 + kWave - 1) / kWave * kWave;
   const dim3 grid(a.T), block(chunks < kCombineMaxThreads ? chunks : kCombineMaxThreads);
-  if (a.y_f32 && a.out_f32)
-    hipLaunchKernelGGL((combine_kernel<true, true>), grid, block, 0, s, yb, a.inv, a.w, a.k,
-                       bb, g, ob, a.d);
-  else if (a.y_f32)
-    hipLaunchKernelGGL((combine_kernel<true, false>), grid, block, 0, s, yb, a.inv, a.w, a.k,
-                       bb, g, ob, a.d);
-  else if (a.out_f32)
-    hipLaunchKernelGGL((combine_kernel<false, true>), grid, block, 0, s, yb, a.inv, a.w, a.k,
-                       bb, g, ob, a.d);
-  else
-    hipLaunchKernelGGL((combine_kernel<false, false>), grid, block, 0, s, yb, a.inv, a.w, a.k,
-                       bb, g, ob, a.d);
+  // the shared output's element type follows y's (see combine_kernel)
+  const int bk = a.y_kind == kRowBF16 ? kRowBF16 : kRowF32;
+  if (a.y_kind < kRowBF16 || a.y_kind > kRowF16 || (a.base && a.base_kind != bk))
+    return hipErrorInvalidValue;
+  auto go = [&](auto yk, auto of) {
+    hipLaunchKernelGGL((combine_kernel<decltype(yk)::value, decltype(of)::value>), grid, block,
+                       0, s, yb, a.inv, a.w, a.k, bb, g, ob, a.d);
+  };
+  using F32 = std::integral_constant<int, kRowF32>;
+  using F16 = std::integral_constant<int, kRowF16>;
+  using BF16 = std::integral_constant<int, kRowBF16>;
+  using Yes = std::true_type;
+  using No = std::false_type;
+  switch (a.y_kind) {
+    case kRowF32: a.out_f32 ? go(F32{}, Yes{}) : go(F32{}, No{}); break;
+    case kRowF16: a.out_f32 ? go(F16{}, Yes{}) : go(F16{}, No{}); break;
+    default: a.out_f32 ? go(BF16{}, Yes{}) : go(BF16{}, No{}); break;
+  }
   return hipGetLastError();
 }
 

@@ -701,7 +701,7 @@ void grouped_gemm_kernel(GemmArgs a) {
                         static_cast<int64_t>(orow0) * ldo,
                     static_cast<uint32_t>(g.rows * ldo));
     if constexpr (EPI == kEpiStore) {
-      const bool f32o = (second ? a.out2_f32 : a.out_f32) != 0;
+      const bool f32o = (second ? a.out2_kind : a.out_kind) == kRowF32;
       // Rows of an expert whose rows fit one tile (the y_perm of weight-streaming experts) are
       // stored non-temporally: measured on MI355X, softmax_bf16's combine, which reads them,
       // 0.236 -> 0.216 ms.  Multi-tile experts keep the default policy (all-non-temporal y_perm
@@ -711,6 +711,8 @@ void grouped_gemm_kernel(GemmArgs a) {
       // One copy of the store loop per (element type, cache policy), chosen once per tile: with
       // the choice inside the loop every block's permutes had to complete before its own store
       // (one LDS round trip per block); in one straight run they overlap the other blocks'.
+      // Rows that are not fp32 are bf16 from the E4M3-activation kernels and fp16 from the
+      // bf16 / fp32 kernels (RowKind).
       auto store_tile = [&](auto f32_tag, auto nt_tag) __attribute__((always_inline)) {
         constexpr bool F32 = decltype(f32_tag)::value, NT = decltype(nt_tag)::value;
         // a row block's permutes first, then its stores
@@ -733,7 +735,8 @@ void grouped_gemm_kernel(GemmArgs a) {
           } else {
             uint2 v[S::FN];
 #pragma unroll
-            for (int j = 0; j < S::FN; ++j) v[j] = xpose2(pack_bf16x4(acc[i][j]));
+            for (int j = 0; j < S::FN; ++j)
+              v[j] = xpose2(S::kFp8 ? pack_bf16x4(acc[i][j]) : pack_f16x4(acc[i][j]));
 #pragma unroll
             for (int j = 0; j < S::FN; ++j) {
               const int col = g.n0 + wn * S::TN + j * 16 + scol;
@@ -1004,6 +1007,13 @@ static hipError_t launch_epi(int epi, int bm, const GemmArgs& a, int max_tiles, 
 
 hipError_t launch_grouped_gemm(int dtype, int epi, int bm, const GemmArgs& a, int max_tiles,
                                hipStream_t s) {
+  if (epi == kEpiStore) {
+    // the element types each kernel's store epilogue has (see RowKind)
+    const int half = dtype == MOE_FP8_E4M3 || dtype == MOE_MXFP4 ? kRowBF16 : kRowF16;
+    if ((a.out_kind != kRowF32 && a.out_kind != half) ||
+        (a.has_group2 && a.out2_kind != kRowF32 && a.out2_kind != half))
+      return hipErrorInvalidValue;
+  }
   switch (dtype) {
     case MOE_F32: return launch_epi<MOE_F32>(epi, bm, a, max_tiles, s);
     case MOE_BF16: return launch_epi<MOE_BF16>(epi, bm, a, max_tiles, s);

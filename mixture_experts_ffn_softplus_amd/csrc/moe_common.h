@@ -125,6 +125,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ uint2 pack_bf16x4(f32x4 v) {
   return uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
+// The same as IEEE binary16 (round to nearest even; magnitudes from 65520 up become inf).
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
+}
+__device__ __forceinline__ uint2 pack_f16x4(f32x4 v) {
+  return uint2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+}
 
 // ----------------------------------------------------------------------------- LDS DMA
 // Buffer loads whose data goes straight to LDS: lane l's BYTES land at (lds + BYTES * l), the

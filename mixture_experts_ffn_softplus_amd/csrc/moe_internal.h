@@ -61,6 +61,10 @@ hipError_t launch_tile_list(const int32_t* offsets, int E, int bm, int extra_row
 
 // ---- grouped GEMMs (gemm.hip)
 enum Epilogue { kEpiSwiglu = 0, kEpiStore = 1 };
+// Element type of the rows the store epilogue writes and the combine reads back (y_perm, the
+// shared experts' output, router logits): the bf16 / fp32 GEMMs store fp32 or fp16 rows, the
+// E4M3-activation GEMMs fp32 or bf16 rows.
+enum RowKind { kRowBF16 = 0, kRowF32 = 1, kRowF16 = 2 };
 
 struct GemmArgs {
   // A: activations, K-contiguous rows
@@ -87,7 +91,7 @@ struct GemmArgs {
   void* out;
   int64_t ldo;                // bytes per output row
   float* out_scales;          // FP8 h: [rows, out_cols/128]
-  int out_f32;                // store epilogue: fp32 rows (else bf16)
+  int out_kind;               // store epilogue: RowKind of the stored rows
   // A rows repeat every a_steps K-steps when > 0 (0: no repeat)
   int a_steps;
   // One group only (tiles null): K split into k_splits equal ranges of whole K-steps (0 or 1:
@@ -97,7 +101,7 @@ struct GemmArgs {
   // One extra group after the routed experts when has_group2 (group index group2): the shared
   // experts, whose rows are the tokens in order.  Its rows [m2, m2 + rows) of the M space take
   // A row (r - m2) of A2 (no a_map), the weights B2 (+ scales), and store to out2 (+ scales)
-  // with row stride ldo2 (fp32 rows when out2_f32, store epilogue).
+  // with row stride ldo2 (rows of RowKind out2_kind, store epilogue).
   int has_group2;
   int group2;
   int m2;
@@ -110,7 +114,7 @@ struct GemmArgs {
   void* out2;
   int64_t ldo2;
   float* out2_scales;
-  int out2_f32;
+  int out2_kind;
 };
 
 // dtype: MOE_F32 / MOE_BF16 / MOE_FP8_E4M3 / MOE_MXFP4 (E4M3 activations, E2M1 weights).
@@ -125,13 +129,15 @@ hipError_t launch_grouped_gemm(int dtype, int epi, int bm, const GemmArgs& a, in
                                hipStream_t s);
 
 // ---- un-permute and weighted combine (combine.hip)
-// out[t] = G[t] * base[t] + sum_j w[t*k+j] * y[inv[t*k+j]] over d columns; y rows fp32 (y_f32)
-// or bf16, base [T, d] in y's element type or null, out fp32 (out_f32) or bf16.  G = 1, or with gate_vec
+// out[t] = G[t] * base[t] + sum_j w[t*k+j] * y[inv[t*k+j]] over d columns; y rows of RowKind
+// y_kind, base [T, d] of RowKind base_kind (fp32 under fp16 or fp32 rows, bf16 under bf16 rows) or
+// null, out fp32 (out_f32) or bf16.  G = 1, or with gate_vec
 // G[t] = sigmoid(x~[t] . gate_vec): x~ fp32 / bf16 (x_kind 0 / 1) or E4M3 codes times their
 // per-128 scales (x_kind 2); gate_vec fp32 or bf16 (gate_f32).
 struct CombineArgs {
   const void* y;
-  bool y_f32;
+  int y_kind;
+  int base_kind;
   const int32_t* inv;
   const float* w;
   int k;
