@@ -288,9 +288,10 @@ MOE_API moe_status_t moe_permute(const moe_config_t* cfg, const int32_t* topk_id
  * y_perm[r] = h W_down[e], with x~ = x[perm_token[r]] (FP8: the block-scaled
  * xq / xq_scales from moe_route, and h re-quantised per 128 values).
  * y_perm [T*k, d]: fp32 for MOE_F32 experts; IEEE fp16 for MOE_BF16 experts
- * (round to nearest even: 8x finer than bf16 at half the bytes of fp32; a
- * single expert output of magnitude 65520 or more overflows to +-inf, which
- * the block output then carries); bf16 for MOE_FP8_E4M3 and MOE_MXFP4 experts. */
+ * (round to nearest even: 8x finer than bf16 at half the bytes of fp32; an
+ * expert output value of magnitude 65520 or more overflows, and the block
+ * output of that token then holds a non-finite value in that column, never a
+ * wrong finite one); bf16 for MOE_FP8_E4M3 and MOE_MXFP4 experts. */
 MOE_API moe_status_t moe_expert_ffn(const moe_config_t* cfg, const void* x_or_xq, const float* xq_scales,
                             const int32_t* expert_offsets, const int32_t* perm_token,
                             const moe_weights_t* weights, void* y_perm, void* ws,

@@ -31,8 +31,9 @@ struct CombineGate {
 
 // Eight consecutive values of a row of bf16 or fp16 (16 B) or fp32 (32 B) elements (RowKind);
 // NT: non-temporal loads.  The expert rows are read once; measured on MI355X, non-temporal
-// loads speed up the bf16 rows (FP8 experts: 2.95 GB, 668 -> 585 us) but slow down the fp32
-// rows (0.67 GB, 183 -> 216 us), so only the former use them.
+// loads speed up the 2-byte rows (bf16 rows of FP8 experts: 2.95 GB, 668 -> 585 us; fp16 rows
+// of softmax_bf16: 0.34 GB, 145 -> 139 us) but slow down the fp32 rows (0.67 GB, 183 -> 216
+// us), so only the former use them.
 template <int KIND, bool NT = false>
 __device__ __forceinline__ void load8(const uint8_t* p, float* v) {
   if constexpr (KIND == kRowF32) {
@@ -103,7 +104,8 @@ __global__ __launch_bounds__(kCombineMaxThreads) void combine_kernel(
     int k, const uint8_t* __restrict__ base, CombineGate gate, uint8_t* __restrict__ out, int d) {
   constexpr int BK = YK == kRowBF16 ? kRowBF16 : kRowF32;
   constexpr int ysz = YK == kRowF32 ? 4 : 2, bsz = BK == kRowF32 ? 4 : 2, osz = OUT_F32 ? 4 : 2;
-  constexpr bool kNtY = YK == kRowBF16;  // non-temporal y and shared loads (see load8)
+  constexpr bool kNtY = YK != kRowF32;       // non-temporal y loads (see load8)
+  constexpr bool kNtS = BK == kRowBF16;      // and shared-output loads
   __shared__ int32_t s_row[kCombineMaxK];
   __shared__ float s_w[kCombineMaxK];
   const int t = blockIdx.x;
@@ -120,9 +122,9 @@ __global__ __launch_bounds__(kCombineMaxThreads) void combine_kernel(
   for (int c = threadIdx.x; c < d / 8; c += blockDim.x) {
     float v[8];
     if (base) {
-      // the shared output, read once as well: non-temporal with the bf16 rows (FP8 experts),
-      // as measured above
-      load8<BK, kNtY>(base + (static_cast<int64_t>(t) * d + c * 8) * bsz, v);
+      // the shared output, read once as well: non-temporal when it is bf16 (FP8 experts), as
+      // measured above
+      load8<BK, kNtS>(base + (static_cast<int64_t>(t) * d + c * 8) * bsz, v);
 #pragma unroll
       for (int q = 0; q < 8; ++q) v[q] *= G;
     } else {

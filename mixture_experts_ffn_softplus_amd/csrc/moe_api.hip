@@ -68,7 +68,8 @@ int out_bytes(const moe_config_t* c) { return c->out_f32 ? 4 : act_bytes(c); }
 // budget the output rounding alone half fills (measured on 62 seeded random bf16 layers: worst
 // max-abs/RMS 0.0153 with fp32 rows, 0.0249 with bf16 rows); fp16 rows round 8x finer and halve
 // the fp32 rows' HBM traffic.  fp16 overflows where one expert's output reaches 65520 in
-// magnitude: such an output comes out of the block as +-inf, never as a wrong finite value.
+// magnitude: the token's block output is then non-finite in that column (inf, or NaN where the
+// combine's zero-weight padding rows meet it), never a wrong finite value.
 int y_kind(const moe_config_t* c) {
   return is_fp8(c) ? kRowBF16 : c->expert_dtype == MOE_F32 ? kRowF32 : kRowF16;
 }

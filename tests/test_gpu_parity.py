@@ -484,3 +484,35 @@ def test_full_size_workloads(name, sample):
     res, _, _ = check_layer(layer, sample=sample, seed=1, max_experts=48)
     del layer
     torch.cuda.empty_cache()
+
+
+def test_fp16_y_overflow_is_non_finite():
+    # bf16 experts keep y_perm as IEEE fp16: an expert output value of magnitude 65520 or more
+    # overflows.  Expert 3's down projection scaled by 2^20 (exact in bf16) puts nearly all of its
+    # output values past that; every token routed to it must come out non-finite (never a
+    # wrong finite row), and every other token must still match the oracle.
+    cfg = BF.with_(name="fp16_overflow", num_tokens=96, d_model=256, num_experts=8, top_k=2,
+                   d_ff=256, num_shared=1, d_ff_shared=256, seed=31)
+    inp = synth.inputs(cfg, "cuda")
+    inp["routed"]["down"][3].mul_(2.0 ** 20)
+    pw = api.pack(cfg, inp["w_router"], inp["routed"], inp["shared"], inp["logit_bias"],
+                  inp["select_bias"], shared_gate=inp["shared_gate"])
+    ws = api.workspace(cfg)
+    T, k, A = cfg.num_tokens, cfg.top_k, cfg.assignments
+    dbg = {"logits": torch.empty(T, cfg.num_experts, dtype=torch.float32, device="cuda"),
+           "topk_ids": torch.empty(T, k, dtype=torch.int32, device="cuda"),
+           "topk_w": torch.empty(T, k, dtype=torch.float32, device="cuda")}
+    out = torch.empty(T, cfg.d_model, dtype=api.out_dtype(cfg), device="cuda")
+    api.moe_forward(cfg, inp["x"], pw.struct(), out, ws, dbg)
+    torch.cuda.synchronize()
+    hit = (dbg["topk_ids"] == 3).any(dim=1).cpu().numpy()
+    assert 0 < hit.sum() < T
+    finite = torch.isfinite(out).cpu().numpy()
+    assert not finite[hit].all(axis=1).any()           # every hit token has non-finite values
+    assert (~finite[hit]).mean() > 0.9                  # and nearly all of its values are
+    ids, w, _ = oracle_route_on(cfg, dbg["logits"], inp["select_bias"])
+    tok = np.nonzero(~hit)[0]
+    ref = oracle_block(cfg, inp, tok, ids[tok], w[tok])
+    got = out[torch.as_tensor(tok, device="cuda")].double().cpu().numpy()
+    assert np.isfinite(got).all()
+    assert rel_err(got, ref) <= 2e-2
