@@ -110,6 +110,25 @@ def test_binding_rejects_an_output_of_another_dtype(out_f32, dtype):
         api.moe_expert_ffn(cfg, None, None, None, None, api.moe_weights_t(), y, ws)
 
 
+@pytest.mark.parametrize("preset, y_dtype", [("tiny_fp32", torch.float32),
+                                              ("softmax_bf16", torch.float16),
+                                              ("fp8_block", torch.bfloat16),
+                                              ("mxfp4_decode", torch.bfloat16)])
+def test_y_perm_element_type_per_expert_format(preset, y_dtype):
+    # y_perm rows: fp32 for fp32 experts, IEEE fp16 for bf16 experts, bf16 for E4M3
+    # activations; a buffer of any other element type is refused before a launch (the kernels
+    # would write 2-byte rows into a 4-byte buffer's first half, or overrun a 2-byte one)
+    cfg = PRESETS[preset].with_(num_tokens=4)
+    assert api.y_dtype(cfg) == y_dtype
+    ws = torch.empty(16, dtype=torch.uint8)
+    for other in (torch.float32, torch.float16, torch.bfloat16):
+        if other == y_dtype:
+            continue
+        y = torch.empty(cfg.assignments, cfg.d_model, dtype=other)
+        with pytest.raises(ValueError, match="y_perm must be"):
+            api.moe_expert_ffn(cfg, None, None, None, None, api.moe_weights_t(), y, ws)
+
+
 def test_large_and_fp8_constraints():
     c = api.config_struct(PRESETS["fp8_block"], quant_block=64)
     assert api.lib().moe_workspace_size(ctypes.byref(c)) == 0
